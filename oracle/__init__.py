@@ -1,0 +1,27 @@
+"""CPU oracle for the MoE layer forward: TEST INFRASTRUCTURE ONLY.
+
+A plain, slow, obviously-correct numpy (float64) statement of what the GPU path
+computes.  Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` may import it.  It shares no code with the HIP library or its
+Python binding, and imports neither.
+
+* :mod:`oracle.routing` -- top-k gating with softmax over the selected logits and
+  the routing metadata built from it (bitmatrix, per-expert histogram, ragged
+  offsets, stable expert-sorted gather/scatter indices, permuted gate weights).
+* :mod:`oracle.ffn` -- the expert FFN (SiLU-gated, SwiGLU-OAI, ReLU^2) run as the
+  masked per-expert loop, the weighted combine, and the sorted-dispatch variant.
+
+Every function is pinned by ``tests/test_oracle_*.py`` against brute force,
+library routines, closed forms, invariants and the hand-derived fixtures in
+``tests/golden/``; the one part with no such pin (the SwiGLU-OAI formula relative
+to the pages) is marked "parity unpinned" where it is defined.
+"""
+from .routing import (RoutingRef, bitmatrix, histogram, offsets_from_hist, route,
+                      round_to_dtype, sorted_indices, topk_select, topk_softmax)
+from .ffn import activation, moe_ffn, moe_ffn_sorted, split_gate_up
+
+__all__ = [
+    "RoutingRef", "route", "topk_select", "topk_softmax", "bitmatrix", "histogram",
+    "offsets_from_hist", "sorted_indices", "round_to_dtype",
+    "activation", "split_gate_up", "moe_ffn", "moe_ffn_sorted",
+]
