@@ -1,0 +1,179 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE-layer forward library, libmoe.so.
+ *
+ * Three entry points run the layer on one GPU, entirely on the device and with
+ * no device-to-host synchronisation:
+ *
+ *   moe_route    router logits -> top-k + softmax + all routing metadata
+ *   moe_experts  routing metadata + x -> grouped expert FFN -> weighted combine
+ *   moe_forward  moe_route followed by moe_experts, on one stream
+ *
+ * moe_experts is also exported as its two halves, moe_experts_w13 (grouped
+ * GEMM with w13 + activation) and moe_experts_w2 (grouped GEMM with w2 +
+ * routing weight + combine).
+ *
+ * Sources of the operations (the pages are cited by title and section):
+ *  - top-k over the router logits with softmax over the selected values, and the
+ *    metadata it yields -- expert bitmatrix, per-expert column sums (col_sum),
+ *    row- and column-sorted indices, gate weights permuted into sorted order --
+ *    follow the topk / routing_data_from_sparse_topk description in the vLLM PR
+ *    #45457 report ("implementation breakdown", "key source snippets").  The
+ *    gather index pair is (col_sorted, row_sorted) and the scatter pair is
+ *    (row_sorted, col_sorted); gate_scal has the dtype of the gating output.
+ *  - the stable sort by expert with contiguous per-expert row slices and
+ *    segment bounds [0] + group ends follows the minimind issue #835 page
+ *    ("It is removable in plain PyTorch"); here the bounds never leave the GPU.
+ *  - the expert FFN activations (SiLU-gated with optional clamp, SwiGLU-OAI with
+ *    alpha/beta/limit, non-gated ReLU^2), the rule that unset parameters keep
+ *    plain-SwiGLU defaults, and the packed [gate; up] vs interleaved
+ *    [g0, u0, g1, u1, ...] w13 layouts follow the vLLM PR #47106 report
+ *    ("implementation breakdown", the apply and w13-reorder snippets, "review
+ *    highlights").
+ *  - the caller owns the output and the workspaces, as in the experts apply()
+ *    signature of the PR #47106 report.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers, row-major, contiguous, 16-byte
+ *    aligned, allocated and owned by the caller.  The library never allocates,
+ *    frees, synchronises, logs, or keeps state between calls; it is re-entrant.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  All work is
+ *    enqueued on it; the call returns before the work finishes.
+ *  - Arguments are checked before anything is enqueued; on error a negative
+ *    moe_status_t is returned and nothing is written.  A launch failure returns
+ *    MOE_ERR_HIP.  Asynchronous device faults surface at the caller's next sync.
+ *  - n_tokens == 0 is valid: MOE_OK, nothing enqueued.
+ *  - Limits: 1 <= n_experts <= 256, 1 <= topk <= min(n_experts, 16),
+ *    n_tokens * topk < 2^31, hidden and inter positive multiples of 8.
+ *  - Logits must be finite.  Ties between equal logits go to the lower expert
+ *    index; -0.0 and +0.0 are equal.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,        /* a required pointer is NULL                     */
+  MOE_ERR_SHAPE = -2,       /* a size is out of range or inconsistent          */
+  MOE_ERR_DTYPE = -3,       /* unknown dtype, or dtypes that must match do not */
+  MOE_ERR_UNSUPPORTED = -4, /* unsupported (activation, layout) combination    */
+  MOE_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned                */
+  MOE_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required         */
+  MOE_ERR_HIP = -7          /* a HIP launch failed                             */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
+
+/* Expert activation.  g = gate row, u = up row of the GEMM1 output.
+ *   MOE_ACT_SILU:       a = g' * sigmoid(g') * u'            (uses limit only)
+ *   MOE_ACT_SWIGLU_OAI: a = g' * sigmoid(alpha*g') * (u' + beta)
+ *     with g' = min(g, limit) and u' = clamp(u, -limit, limit);
+ *   MOE_ACT_RELU2:      a = max(h, 0)^2, non-gated (w13 has inter rows), no params. */
+typedef enum { MOE_ACT_SILU = 0, MOE_ACT_SWIGLU_OAI = 1, MOE_ACT_RELU2 = 2 } moe_act_t;
+
+/* Row order of a gated w13 [E, 2*inter, hidden]:
+ *   PACKED:      rows [0, inter) are gate, rows [inter, 2*inter) are up;
+ *   INTERLEAVED: even rows are gate, odd rows are up.
+ * MOE_ACT_RELU2 requires MOE_W13_PACKED (its w13 is a single up matrix). */
+typedef enum { MOE_W13_PACKED = 0, MOE_W13_INTERLEAVED = 1 } moe_w13_layout_t;
+
+/* Activation parameters.  A field counts only if its bit is set in `set`; an
+ * unset field keeps the plain-SwiGLU default (alpha 1, beta 0, no clamp).  The
+ * library never substitutes other defaults.  SiLU reads only `limit`. */
+#define MOE_PARAM_ALPHA 1u
+#define MOE_PARAM_BETA 2u
+#define MOE_PARAM_LIMIT 4u
+typedef struct {
+  float alpha;
+  float beta;
+  float limit;
+  uint32_t set;
+} moe_act_params_t;
+
+/* Routing metadata buffers (device pointers, caller-allocated).  M = n_tokens*topk.
+ * Flat entry index f = t*topk + j names slot j of token t; slots are ordered by
+ * descending logit (ties: lower expert index first). */
+typedef struct {
+  int32_t *topk_idx;   /* [N, topk]  selected expert of each slot                 */
+  void *topk_w;        /* [N, topk]  softmax over the selected logits (w_dtype)   */
+  uint32_t *bitmatrix; /* [N, ceil(E/32)] bit e%32 of word e/32: token chose e    */
+  int32_t *col_sum;    /* [E]        entries routed to each expert                */
+  int32_t *offsets;    /* [E+1]      0, running sum of col_sum; offsets[E] = M    */
+  int32_t *col_sorted; /* [M]        f of the p-th entry in expert-major order,
+                                     token order kept inside an expert            */
+  int32_t *row_sorted; /* [M]        position p of entry f (inverse of col_sorted)*/
+  void *gate_scal;     /* [M]        topk_w flat [col_sorted[p]] (w_dtype)         */
+  int32_t w_dtype;     /* moe_dtype_t of topk_w and gate_scal                      */
+} moe_routing_t;
+
+/* Bytes of device workspace sufficient for moe_route (pass hidden = inter = 0),
+ * moe_experts and moe_forward with these sizes.  Returns 0 on invalid sizes. */
+size_t moe_workspace_bytes(int64_t n_tokens, int32_t n_experts, int32_t topk,
+                           int32_t hidden, int32_t inter, moe_dtype_t dtype);
+
+/* Top-k gating and routing metadata.
+ *   logits  [N, E] in logits_dtype.
+ *   out     every field of *out is written; out->w_dtype must equal logits_dtype
+ *           (the weights inherit the gating dtype).
+ *   The result is deterministic and bit-identical across runs. */
+moe_status_t moe_route(const void *logits, moe_dtype_t logits_dtype, int64_t n_tokens,
+                       int32_t n_experts, int32_t topk, const moe_routing_t *out,
+                       void *workspace, size_t ws_bytes, void *stream);
+
+/* Grouped expert FFN and weighted combine from existing routing metadata.
+ *   x    [N, hidden]; w13 [E, 2*inter, hidden] (gated) or [E, inter, hidden]
+ *   (ReLU^2); w2 [E, hidden, inter]; out [N, hidden].  x, w13, w2, out share
+ *   `dtype`.  Reads routing->offsets, col_sorted, row_sorted, gate_scal.
+ *   out[t] = sum over the token's slots j of gate * W2[e] act(W13[e] x[t]),
+ *   summed in slot order with fp32 accumulation (deterministic). */
+moe_status_t moe_experts(const void *x, moe_dtype_t dtype, int64_t n_tokens, int32_t hidden,
+                         const void *w13, const void *w2, int32_t n_experts, int32_t inter,
+                         int32_t topk, moe_act_t act, moe_w13_layout_t layout,
+                         const moe_act_params_t *params, const moe_routing_t *routing,
+                         void *out, void *workspace, size_t ws_bytes, void *stream);
+
+/* The two halves of moe_experts, for callers that keep the activation rows
+ * themselves (the experts apply() of the PR #47106 report likewise takes one
+ * workspace for the w13 stage and one for the w2 stage).
+ *
+ * moe_experts_w13: grouped GEMM with w13 and the activation.
+ *   act_out [N*topk, inter] in `dtype`; row p is the activation of sorted entry p
+ *   (the expert-major order of routing->col_sorted).  Reads routing->offsets and
+ *   col_sorted.  Needs no workspace. */
+moe_status_t moe_experts_w13(const void *x, moe_dtype_t dtype, int64_t n_tokens, int32_t hidden,
+                             const void *w13, int32_t n_experts, int32_t inter, int32_t topk,
+                             moe_act_t act, moe_w13_layout_t layout,
+                             const moe_act_params_t *params, const moe_routing_t *routing,
+                             void *act_out, void *stream);
+
+/* moe_experts_w2: grouped GEMM with w2, routing weight, and the combine.
+ *   act_in [N*topk, inter] from moe_experts_w13; w2 [E, hidden, inter];
+ *   out [N, hidden].  Reads routing->offsets, col_sorted, row_sorted, gate_scal.
+ *   workspace: at least moe_workspace_bytes(...) bytes (it holds the weighted
+ *   expert rows when topk > 1). */
+moe_status_t moe_experts_w2(const void *act_in, moe_dtype_t dtype, int64_t n_tokens,
+                            int32_t hidden, const void *w2, int32_t n_experts, int32_t inter,
+                            int32_t topk, const moe_routing_t *routing, void *out,
+                            void *workspace, size_t ws_bytes, void *stream);
+
+/* moe_route on `logits` (dtype `dtype`) into *routing_out, then moe_experts. */
+moe_status_t moe_forward(const void *x, const void *logits, moe_dtype_t dtype,
+                         int64_t n_tokens, int32_t hidden, const void *w13, const void *w2,
+                         int32_t n_experts, int32_t inter, int32_t topk, moe_act_t act,
+                         moe_w13_layout_t layout, const moe_act_params_t *params,
+                         const moe_routing_t *routing_out, void *out, void *workspace,
+                         size_t ws_bytes, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *moe_status_str(moe_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

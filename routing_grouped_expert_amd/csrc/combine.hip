@@ -1,0 +1,79 @@
+// Weighted scatter-combine: out[t] = sum over slots j of y_sorted[row_sorted[t*k + j]].
+//
+// The expert outputs were already scaled by their routing weights in GEMM2's
+// epilogue; this kernel adds each token's k rows back together, the step the
+// minimind issue #835 page does with index_add_ ("Summary").  That page notes
+// index_add_ uses atomics on the GPU when k > 1; here each thread owns one
+// 16-byte chunk of one output row and sums the k chunks in slot order in fp32,
+// so the result is deterministic.  The loads are 16-byte vectors; each token
+// row is read from k places and written once (HBM bound).
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+__device__ __forceinline__ void add_chunk(float (&acc)[8], u32x4_t v, bf16_t) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[2 * i] += __uint_as_float(v[i] << 16);
+    acc[2 * i + 1] += __uint_as_float(v[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void add_chunk(float (&acc)[4], u32x4_t v, float) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] += __uint_as_float(v[i]);
+}
+__device__ __forceinline__ u32x4_t pack_chunk(const float (&acc)[8], bf16_t) {
+  u32x4_t o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = (uint32_t)bf16_rne(acc[2 * i]) | ((uint32_t)bf16_rne(acc[2 * i + 1]) << 16);
+  return o;
+}
+__device__ __forceinline__ u32x4_t pack_chunk(const float (&acc)[4], float) {
+  u32x4_t o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = __float_as_uint(acc[i]);
+  return o;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y,
+                                                      const int32_t *__restrict__ row_sorted,
+                                                      T *__restrict__ out, int64_t N, int K,
+                                                      int H) {
+  constexpr int CH = 16 / sizeof(T);  // elements per 16-byte chunk
+  const int nch = H / CH;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= N * nch) return;
+  const int64_t t = idx / nch;
+  const int c = (int)(idx - t * nch);
+  float acc[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) acc[i] = 0.f;
+  for (int j = 0; j < K; ++j) {
+    const int64_t p = row_sorted[t * K + j];
+    add_chunk(acc, *reinterpret_cast<const u32x4_t *>(y + p * H + (int64_t)c * CH), T());
+  }
+  *reinterpret_cast<u32x4_t *>(out + t * H + (int64_t)c * CH) = pack_chunk(acc, T());
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void *y_sorted, const int32_t *row_sorted, void *out,
+                          moe_dtype_t dt, int64_t n_tokens, int topk, int hidden, hipStream_t s) {
+  const int ch = dt == MOE_BF16 ? 8 : 4;
+  const int64_t total = n_tokens * (hidden / ch);
+  const unsigned blocks = (unsigned)((total + 255) / 256);
+  if (dt == MOE_BF16)
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s,
+                       reinterpret_cast<const bf16_t *>(y_sorted), row_sorted,
+                       reinterpret_cast<bf16_t *>(out), n_tokens, topk, hidden);
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, s,
+                       reinterpret_cast<const float *>(y_sorted), row_sorted,
+                       reinterpret_cast<float *>(out), n_tokens, topk, hidden);
+  return hipGetLastError();
+}
+
+}  // namespace moe

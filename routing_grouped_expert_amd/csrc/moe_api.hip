@@ -1,0 +1,291 @@
+// C-ABI entry points of libmoe.so: argument checks, workspace layout, launch
+// order.  Every check runs before the first launch, so a rejected call writes
+// nothing.  No entry point allocates, frees, synchronises or keeps state.
+#include <math.h>
+
+#include <initializer_list>
+
+#include "moe_common.h"
+
+namespace {
+
+using moe::ActParams;
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool dtype_ok(int d) { return d == MOE_F32 || d == MOE_BF16; }
+inline size_t dsize(int d) { return d == MOE_BF16 ? 2 : 4; }
+
+// Sizes shared by all entry points.
+moe_status_t check_sizes(int64_t n, int32_t e, int32_t k) {
+  if (n < 0 || e < 1 || e > moe::kMaxExperts || k < 1 || k > moe::kMaxTopk || k > e)
+    return MOE_ERR_SHAPE;
+  if (n > (int64_t)0x7fffffff / k) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+moe_status_t check_ffn_sizes(int32_t hidden, int32_t inter) {
+  if (hidden < 8 || inter < 8 || hidden % 8 || inter % 8) return MOE_ERR_SHAPE;
+  if (hidden > (1 << 24) || inter > (1 << 24)) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
+size_t experts_ws_bytes(int64_t n, int32_t k, int32_t hidden, int32_t inter, int dt) {
+  const size_t m = (size_t)n * k;
+  size_t b = align256(m * inter * dsize(dt));  // activation rows a[M, inter]
+  if (k > 1) b += align256(m * hidden * dsize(dt));  // weighted expert outputs y[M, hidden]
+  return b;
+}
+
+moe_status_t check_routing_struct(const moe_routing_t *r, bool for_route, int64_t n) {
+  if (!r) return MOE_ERR_NULL;
+  if (!dtype_ok(r->w_dtype)) return MOE_ERR_DTYPE;
+  if (n == 0) return MOE_OK;
+  const void *need_exp[] = {r->offsets, r->col_sorted, r->row_sorted, r->gate_scal};
+  for (const void *p : need_exp) {
+    if (!p) return MOE_ERR_NULL;
+    if (!aligned16(p)) return MOE_ERR_ALIGN;
+  }
+  if (for_route) {
+    const void *need_rt[] = {r->topk_idx, r->topk_w, r->bitmatrix, r->col_sum};
+    for (const void *p : need_rt) {
+      if (!p) return MOE_ERR_NULL;
+      if (!aligned16(p)) return MOE_ERR_ALIGN;
+    }
+  }
+  return MOE_OK;
+}
+
+moe_status_t act_params(moe_act_t act, moe_w13_layout_t layout, const moe_act_params_t *p,
+                        ActParams *out) {
+  if (act != MOE_ACT_SILU && act != MOE_ACT_SWIGLU_OAI && act != MOE_ACT_RELU2)
+    return MOE_ERR_UNSUPPORTED;
+  if (layout != MOE_W13_PACKED && layout != MOE_W13_INTERLEAVED) return MOE_ERR_UNSUPPORTED;
+  if (act == MOE_ACT_RELU2 && layout != MOE_W13_PACKED) return MOE_ERR_UNSUPPORTED;
+  const uint32_t set = p ? p->set : 0u;
+  if (set & ~(MOE_PARAM_ALPHA | MOE_PARAM_BETA | MOE_PARAM_LIMIT)) return MOE_ERR_UNSUPPORTED;
+  // unset fields keep the plain-SwiGLU defaults; SiLU reads only the limit
+  out->alpha = 1.f;
+  out->beta = 0.f;
+  out->limit = INFINITY;
+  if (act == MOE_ACT_RELU2) return MOE_OK;
+  if (set & MOE_PARAM_LIMIT) {
+    if (!(p->limit >= 0.f)) return MOE_ERR_SHAPE;  // also rejects NaN
+    out->limit = p->limit;
+  }
+  if (act == MOE_ACT_SWIGLU_OAI) {
+    if (set & MOE_PARAM_ALPHA) out->alpha = p->alpha;
+    if (set & MOE_PARAM_BETA) out->beta = p->beta;
+    if (!isfinite(out->alpha) || !isfinite(out->beta)) return MOE_ERR_SHAPE;
+  }
+  return MOE_OK;
+}
+
+// Checks shared by the expert entry points: sizes, dtype, activation, routing.
+moe_status_t check_expert_args(moe_dtype_t dtype, int64_t n, int32_t hidden, int32_t e,
+                               int32_t inter, int32_t k, moe_act_t act, moe_w13_layout_t layout,
+                               const moe_act_params_t *params, const moe_routing_t *routing,
+                               ActParams *prm) {
+  moe_status_t st = check_sizes(n, e, k);
+  if (st != MOE_OK) return st;
+  if ((st = check_ffn_sizes(hidden, inter)) != MOE_OK) return st;
+  if (!dtype_ok(dtype)) return MOE_ERR_DTYPE;
+  // one expert's w13 / w2 block is addressed with 32-bit byte offsets
+  if ((int64_t)2 * inter * hidden * (int64_t)dsize(dtype) > (int64_t)0x7fffffff)
+    return MOE_ERR_SHAPE;
+  if ((st = act_params(act, layout, params, prm)) != MOE_OK) return st;
+  return check_routing_struct(routing, false, n);
+}
+
+moe_status_t check_ptrs(std::initializer_list<const void *> ptrs) {
+  for (const void *p : ptrs) {
+    if (!p) return MOE_ERR_NULL;
+    if (!aligned16(p)) return MOE_ERR_ALIGN;
+  }
+  return MOE_OK;
+}
+
+moe_status_t check_ws(const void *ws, size_t have, size_t need) {
+  if (need == 0) return MOE_OK;
+  if (!ws) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_ALIGN;
+  return have < need ? MOE_ERR_WORKSPACE : MOE_OK;
+}
+
+size_t y_bytes(int64_t n, int32_t k, int32_t hidden, int dt) {
+  return k > 1 ? align256((size_t)n * k * hidden * dsize(dt)) : 0;
+}
+
+moe_status_t check_experts(const void *x, moe_dtype_t dtype, int64_t n, int32_t hidden,
+                           const void *w13, const void *w2, int32_t e, int32_t inter, int32_t k,
+                           moe_act_t act, moe_w13_layout_t layout, const moe_act_params_t *params,
+                           const moe_routing_t *routing, void *out, void *ws, size_t ws_bytes,
+                           ActParams *prm) {
+  moe_status_t st = check_expert_args(dtype, n, hidden, e, inter, k, act, layout, params,
+                                      routing, prm);
+  if (st != MOE_OK || n == 0) return st;
+  if ((st = check_ptrs({x, w13, w2, out})) != MOE_OK) return st;
+  return check_ws(ws, ws_bytes, experts_ws_bytes(n, k, hidden, inter, dtype));
+}
+
+moe_status_t check_route(const void *logits, moe_dtype_t dt, int64_t n, int32_t e, int32_t k,
+                         const moe_routing_t *out, void *ws, size_t ws_bytes) {
+  moe_status_t st = check_sizes(n, e, k);
+  if (st != MOE_OK) return st;
+  if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
+  if ((st = check_routing_struct(out, true, n)) != MOE_OK) return st;
+  if (out->w_dtype != dt) return MOE_ERR_DTYPE;  // the weights inherit the gating dtype
+  if (n == 0) return MOE_OK;
+  if (!logits) return MOE_ERR_NULL;
+  if (!aligned16(logits)) return MOE_ERR_ALIGN;
+  if (!ws) return MOE_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOE_ERR_ALIGN;
+  if (ws_bytes < moe::route_scratch_bytes(n, e, k)) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+hipError_t run_w13(const void *x, moe_dtype_t dtype, int64_t n, int32_t hidden, const void *w13,
+                   int32_t e, int32_t inter, int32_t k, moe_act_t act, moe_w13_layout_t layout,
+                   const ActParams &prm, const moe_routing_t *r, void *a, hipStream_t s) {
+  return moe::launch_gemm1(x, w13, a, r->offsets, r->col_sorted, dtype, n, k, e, hidden, inter,
+                           act, layout, prm, s);
+}
+
+hipError_t run_w2(const void *a, moe_dtype_t dtype, int64_t n, int32_t hidden, const void *w2,
+                  int32_t e, int32_t inter, int32_t k, const moe_routing_t *r, void *out, void *y,
+                  hipStream_t s) {
+  const bool direct = k == 1;  // one row per token: GEMM2 writes the output rows itself
+  hipError_t err = moe::launch_gemm2(a, w2, direct ? out : y, r->offsets, r->col_sorted,
+                                     r->gate_scal, (moe_dtype_t)r->w_dtype, dtype, n, k, e,
+                                     hidden, inter, direct, s);
+  if (err != hipSuccess || direct) return err;
+  return moe::launch_combine(y, r->row_sorted, out, dtype, n, k, hidden, s);
+}
+
+moe_status_t run_experts(const void *x, moe_dtype_t dtype, int64_t n, int32_t hidden,
+                         const void *w13, const void *w2, int32_t e, int32_t inter, int32_t k,
+                         moe_act_t act, moe_w13_layout_t layout, const ActParams &prm,
+                         const moe_routing_t *r, void *out, void *ws, hipStream_t s) {
+  // workspace: activation rows a[M, inter], then (topk > 1) weighted rows y[M, hidden]
+  char *base = reinterpret_cast<char *>(ws);
+  void *a = base;
+  void *y = base + align256((size_t)n * k * inter * dsize(dtype));
+  if (run_w13(x, dtype, n, hidden, w13, e, inter, k, act, layout, prm, r, a, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (run_w2(a, dtype, n, hidden, w2, e, inter, k, r, out, y, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(int64_t n_tokens, int32_t n_experts, int32_t topk, int32_t hidden,
+                           int32_t inter, moe_dtype_t dtype) {
+  if (check_sizes(n_tokens, n_experts, topk) != MOE_OK || !dtype_ok(dtype)) return 0;
+  size_t route = moe::route_scratch_bytes(n_tokens, n_experts, topk);
+  size_t ffn = 0;
+  if (hidden != 0 || inter != 0) {
+    if (check_ffn_sizes(hidden, inter) != MOE_OK) return 0;
+    ffn = experts_ws_bytes(n_tokens, topk, hidden, inter, dtype);
+  }
+  const size_t b = route > ffn ? route : ffn;
+  return b ? b : 256;
+}
+
+moe_status_t moe_route(const void *logits, moe_dtype_t logits_dtype, int64_t n_tokens,
+                       int32_t n_experts, int32_t topk, const moe_routing_t *out,
+                       void *workspace, size_t ws_bytes, void *stream) {
+  moe_status_t st =
+      check_route(logits, logits_dtype, n_tokens, n_experts, topk, out, workspace, ws_bytes);
+  if (st != MOE_OK || n_tokens == 0) return st;
+  if (moe::launch_route(logits, logits_dtype, n_tokens, n_experts, topk, out, workspace,
+                        (hipStream_t)stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status_t moe_experts(const void *x, moe_dtype_t dtype, int64_t n_tokens, int32_t hidden,
+                         const void *w13, const void *w2, int32_t n_experts, int32_t inter,
+                         int32_t topk, moe_act_t act, moe_w13_layout_t layout,
+                         const moe_act_params_t *params, const moe_routing_t *routing, void *out,
+                         void *workspace, size_t ws_bytes, void *stream) {
+  ActParams prm;
+  moe_status_t st = check_experts(x, dtype, n_tokens, hidden, w13, w2, n_experts, inter, topk,
+                                  act, layout, params, routing, out, workspace, ws_bytes, &prm);
+  if (st != MOE_OK || n_tokens == 0) return st;
+  return run_experts(x, dtype, n_tokens, hidden, w13, w2, n_experts, inter, topk, act, layout,
+                     prm, routing, out, workspace, (hipStream_t)stream);
+}
+
+moe_status_t moe_experts_w13(const void *x, moe_dtype_t dtype, int64_t n_tokens, int32_t hidden,
+                             const void *w13, int32_t n_experts, int32_t inter, int32_t topk,
+                             moe_act_t act, moe_w13_layout_t layout,
+                             const moe_act_params_t *params, const moe_routing_t *routing,
+                             void *act_out, void *stream) {
+  ActParams prm;
+  moe_status_t st = check_expert_args(dtype, n_tokens, hidden, n_experts, inter, topk, act,
+                                      layout, params, routing, &prm);
+  if (st != MOE_OK || n_tokens == 0) return st;
+  if ((st = check_ptrs({x, w13, act_out})) != MOE_OK) return st;
+  return run_w13(x, dtype, n_tokens, hidden, w13, n_experts, inter, topk, act, layout, prm,
+                 routing, act_out, (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+moe_status_t moe_experts_w2(const void *act_in, moe_dtype_t dtype, int64_t n_tokens,
+                            int32_t hidden, const void *w2, int32_t n_experts, int32_t inter,
+                            int32_t topk, const moe_routing_t *routing, void *out,
+                            void *workspace, size_t ws_bytes, void *stream) {
+  ActParams prm;
+  moe_status_t st = check_expert_args(dtype, n_tokens, hidden, n_experts, inter, topk,
+                                      MOE_ACT_SILU, MOE_W13_PACKED, nullptr, routing, &prm);
+  if (st != MOE_OK || n_tokens == 0) return st;
+  if ((st = check_ptrs({act_in, w2, out})) != MOE_OK) return st;
+  if ((st = check_ws(workspace, ws_bytes, y_bytes(n_tokens, topk, hidden, dtype))) != MOE_OK)
+    return st;
+  return run_w2(act_in, dtype, n_tokens, hidden, w2, n_experts, inter, topk, routing, out,
+                workspace, (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+moe_status_t moe_forward(const void *x, const void *logits, moe_dtype_t dtype, int64_t n_tokens,
+                         int32_t hidden, const void *w13, const void *w2, int32_t n_experts,
+                         int32_t inter, int32_t topk, moe_act_t act, moe_w13_layout_t layout,
+                         const moe_act_params_t *params, const moe_routing_t *routing_out,
+                         void *out, void *workspace, size_t ws_bytes, void *stream) {
+  ActParams prm;
+  moe_status_t st = check_route(logits, dtype, n_tokens, n_experts, topk, routing_out, workspace,
+                                ws_bytes);
+  if (st != MOE_OK) return st;
+  st = check_experts(x, dtype, n_tokens, hidden, w13, w2, n_experts, inter, topk, act, layout,
+                     params, routing_out, out, workspace, ws_bytes, &prm);
+  if (st != MOE_OK || n_tokens == 0) return st;
+  hipStream_t s = (hipStream_t)stream;
+  // the routing scratch is dead once the routing kernels ran (stream order), so
+  // the expert intermediates reuse the same workspace bytes
+  if (moe::launch_route(logits, dtype, n_tokens, n_experts, topk, routing_out, workspace, s) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  return run_experts(x, dtype, n_tokens, hidden, w13, w2, n_experts, inter, topk, act, layout,
+                     prm, routing_out, out, workspace, s);
+}
+
+const char *moe_status_str(moe_status_t status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "required pointer is NULL";
+    case MOE_ERR_SHAPE: return "size out of range or inconsistent";
+    case MOE_ERR_DTYPE: return "unknown or mismatched dtype";
+    case MOE_ERR_UNSUPPORTED: return "unsupported activation/layout combination";
+    case MOE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Shared device helpers for the gfx950 MoE kernels (bf16 storage, vector types,
+// launch-size constants).  Internal to libmoe.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // bfloat16 storage
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));  // one 16-byte chunk
+
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopk = 16;
+
+__device__ __forceinline__ float to_f32(bf16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ float to_f32(float f) { return f; }
+
+// fp32 -> bf16, round to nearest, ties to even (NaN kept quiet).
+__device__ __forceinline__ bf16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ T from_f32(float f);
+template <> __device__ __forceinline__ float from_f32<float>(float f) { return f; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float f) { return bf16_rne(f); }
+
+__device__ __forceinline__ int popc64(unsigned long long x) { return __popcll(x); }
+
+}  // namespace moe
+
+// Host-side launchers (one per kernel family).  Each returns hipSuccess or the
+// launch error; argument checking happens in moe_api.hip before these run.
+namespace moe {
+constexpr int kRouteThreads = 256;
+constexpr int kRouteTokens = 256;  // tokens per routing block (one per thread in the rank phase)
+
+size_t route_scratch_bytes(int64_t n_tokens, int n_experts, int topk);
+hipError_t launch_route(const void *logits, moe_dtype_t dt, int64_t n_tokens, int n_experts,
+                        int topk, const moe_routing_t *r, void *scratch, hipStream_t s);
+
+struct ActParams {
+  float alpha, beta, limit;
+};
+
+// GEMM1: a[M, inter] = act(xs[M, hidden] . W13[e]^T) for every expert segment.
+hipError_t launch_gemm1(const void *x, const void *w13, void *act_out, const int32_t *offsets,
+                        const int32_t *col_sorted, moe_dtype_t dt, int64_t n_tokens, int topk,
+                        int n_experts, int hidden, int inter, moe_act_t act,
+                        moe_w13_layout_t layout, ActParams p, hipStream_t s);
+// GEMM2: y = gate_scal[p] * (a[p] . W2[e]^T); stored to y_sorted[M, hidden], or
+// (topk == 1) straight to out[token(p)].
+hipError_t launch_gemm2(const void *act_in, const void *w2, void *y, const int32_t *offsets,
+                        const int32_t *col_sorted, const void *gate_scal, moe_dtype_t gate_dt,
+                        moe_dtype_t dt, int64_t n_tokens, int topk, int n_experts, int hidden,
+                        int inter, bool direct_out, hipStream_t s);
+// out[t] = sum_j y_sorted[row_sorted[t*topk + j]] (fp32, slot order).
+hipError_t launch_combine(const void *y_sorted, const int32_t *row_sorted, void *out,
+                          moe_dtype_t dt, int64_t n_tokens, int topk, int hidden, hipStream_t s);
+}  // namespace moe

@@ -88,14 +88,15 @@ def _cfg_skewed(act: str = "silu") -> LayerSpec:
                      topk=8, dtype="bf16", act=act, layout="packed", zipf_s=1.1)
 
 
-def layer_spec(name: str, **overrides) -> LayerSpec:
-    """Named workloads: tiny_f32, minimind, gptoss, skewed."""
+def layer_spec(family: str, **overrides) -> LayerSpec:
+    """Named workloads: tiny_f32, minimind, gptoss, skewed; ``overrides`` replace
+    fields of the family's default spec (n_tokens, n_experts, act, name, ...)."""
     base = {
         "tiny_f32": _cfg_tiny,
         "minimind": _cfg_minimind,
         "gptoss": _cfg_gptoss,
         "skewed": _cfg_skewed,
-    }[name]()
+    }[family]()
     return base.with_(**overrides) if overrides else base
 
 

@@ -1,0 +1,77 @@
+"""GPU routing (moe_route) against the CPU oracle: integer metadata bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from routing_grouped_expert_amd import moe_route, Routing
+from routing_grouped_expert_amd.synth import ROUTING_SWEEP, routing_logits
+from tests.gpu_util import assert_routing_equal
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _run(logits_cpu: torch.Tensor, k: int, where: str):
+    print(f"[route] {where} N={logits_cpu.shape[0]} E={logits_cpu.shape[1]} k={k} "
+          f"dtype={logits_cpu.dtype}", flush=True)
+    ref = oracle.route(logits_cpu, k, "bf16" if logits_cpu.dtype == torch.bfloat16 else "f32")
+    gpu = moe_route(logits_cpu.to(DEV), k)
+    torch.cuda.synchronize()
+    return assert_routing_equal(gpu, ref, where), gpu
+
+
+@pytest.mark.parametrize("n,e,k", ROUTING_SWEEP, ids=[f"n{n}-e{e}-k{k}" for n, e, k in ROUTING_SWEEP])
+def test_routing_sweep_bit_exact(n, e, k):
+    _run(routing_logits(n, e, "bf16", seed=n + e), k, "sweep")
+
+
+EDGE = [
+    (256, 32, 4, "bf16"),    # exactly one block (fused single launch)
+    (255, 32, 4, "bf16"),
+    (257, 32, 4, "bf16"),    # two blocks, ragged tail
+    (1000, 6, 2, "bf16"),    # E not a multiple of the 16-byte vector: scalar loads
+    (777, 33, 3, "bf16"),
+    (33, 8, 2, "f32"),       # fp32 logits (tiny layer)
+    (600, 5, 5, "f32"),      # k == E
+    (700, 64, 16, "bf16"),   # largest top-k
+    (1500, 256, 8, "bf16"),  # largest expert count
+    (300, 1, 1, "bf16"),     # single expert
+    (40, 64, 8, "bf16"),     # N*k < E-ish: many empty experts
+    (5000, 128, 1, "f32"),
+]
+
+
+@pytest.mark.parametrize("n,e,k,dt", EDGE, ids=[f"n{a}-e{b}-k{c}-{d}" for a, b, c, d in EDGE])
+def test_routing_edges(n, e, k, dt):
+    _run(routing_logits(n, e, dt, seed=7 * n + e), k, "edge")
+
+
+def test_routing_forced_ties_and_signed_zero():
+    g = torch.Generator().manual_seed(3)
+    lg = torch.randint(-2, 3, (3000, 48), generator=g).to(torch.float32)
+    lg[lg == 0] = torch.where(torch.rand(int((lg == 0).sum()), generator=g) < 0.5, -0.0, 0.0)
+    for dt in (torch.bfloat16, torch.float32):
+        _run(lg.to(dt), 4, f"ties-{dt}")
+    _run(torch.full((500, 16), 0.75).to(torch.bfloat16), 3, "all-equal")
+
+
+def test_routing_skewed_zipf():
+    _run(routing_logits(16384, 64, "bf16", seed=0, zipf_s=1.1), 8, "zipf")
+
+
+def test_routing_empty_is_noop():
+    lg = torch.empty(0, 32, dtype=torch.bfloat16, device=DEV)
+    r = moe_route(lg, 4)
+    torch.cuda.synchronize()
+    assert r.topk_idx.shape == (0, 4)
+
+
+def test_routing_deterministic():
+    lg = routing_logits(65536, 128, "bf16", seed=11).to(DEV)
+    a = moe_route(lg, 4)
+    b = moe_route(lg, 4)
+    torch.cuda.synchronize()
+    for f in ("topk_idx", "topk_w", "bitmatrix", "col_sum", "offsets", "col_sorted",
+              "row_sorted", "gate_scal"):
+        assert torch.equal(getattr(a, f), getattr(b, f)), f
