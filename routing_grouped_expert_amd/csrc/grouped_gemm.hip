@@ -7,35 +7,54 @@
 // vLLM PR #47106 report (activation kinds, parameters, w13 layouts).
 //
 // Design (this file's own):
-//  * One workgroup computes a BM x BN tile of one expert's output.  The m-tiles
-//    of all experts are numbered expert by expert; a workgroup finds its expert
-//    from the device-side offsets (a 64-lane scan of ceil(count / BM) per
-//    expert and a binary search), so the host never learns the counts.  The
-//    grid is an upper bound (floor(M/BM) + min(E, M) m-tiles); surplus
-//    workgroups return at once.
+//  * Persistent workgroups.  The m-tiles of all experts are numbered expert by
+//    expert; every workgroup derives the tile starts from the device-side
+//    offsets (a 64-lane scan of ceil(count / BM) per expert), so the host never
+//    learns the counts, and loops over (m-tile, n-tile) pairs with a stride of
+//    the grid size.  Only real tiles are visited; the grid is sized to the
+//    machine, not to a host-side upper bound.
+//  * Operands go from HBM straight into LDS with buffer_load ... lds (16 bytes
+//    per lane, no VGPR staging) through an S-stage ring: at step kt a workgroup
+//    waits for slice kt, passes one barrier, issues slice kt + S - 1 into the
+//    slot freed by step kt - 1, and runs the MFMAs of slice kt.  Lanes whose
+//    chunk lies past the expert's rows, past the output columns, or past K get
+//    an out-of-range buffer offset and the hardware writes zeros, so tails need
+//    no separate code.
 //  * GEMM1 gathers its A rows straight from x: sorted row p reads token
 //    col_sorted[p] / topk.  No gathered copy of x is ever written.
-//  * Both operands are K-contiguous.  Tiles of 128-byte K-slices are staged
-//    through LDS (double buffered, one barrier per K step) with the 16-byte
-//    chunk index XOR-swizzled by the row, so the 16-byte fragment reads of a
-//    32-row MFMA operand hit distinct banks.
+//  * Tiles are 128-byte K-slices per row with the 16-byte chunk index XOR-
+//    swizzled by the row; each lane of a load fetches the chunk that belongs in
+//    its fixed LDS slot, and the 16-byte fragment reads of a 32-row MFMA operand
+//    hit distinct banks.
 //  * Gated GEMM1 tiles hold BN gate rows and the BN matching up rows of w13,
-//    picked by layout (packed: rows n and inter+n; interleaved: 2n and 2n+1),
-//    so gate and up of one output land in the same lane and register of two
-//    accumulators and the activation runs in the epilogue from fp32.
+//    picked by layout (packed: rows n and inter + n; interleaved: 2n and
+//    2n + 1), so gate and up of one output land in the same lane and register
+//    of two accumulators and the activation runs in the epilogue from fp32.
 //  * bf16 uses v_mfma_f32_32x32x16_bf16, fp32 uses v_mfma_f32_32x32x2_f32.
+#include <type_traits>
+
 #include "moe_common.h"
 
 namespace moe {
 namespace {
 
-constexpr int BM = 128;         // rows per tile
-constexpr int BN = 128;         // output columns per tile
-constexpr int kThreads = 256;   // 4 waves, 2 (rows) x 2 (columns), 64 x 64 each
 constexpr int kRowBytes = 128;  // one K-slice row in LDS
-constexpr int kChunks = kRowBytes / 16;
+constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every num_records used here
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
 
 enum { EPI_ACT = 0, EPI_Y = 1, EPI_OUT = 2 };
+
+struct GemmArgs {
+  const void *A;                 // GEMM1: x [N, K]; GEMM2: a [M, K]
+  const void *W;                 // [E, NSETS * Nout, K]
+  void *C;                       // output rows
+  const int32_t *offsets;        // [E + 1]
+  const int32_t *col_sorted;     // [M]
+  const void *gate_scal;         // [M] (GEMM2)
+  uint32_t a_bytes;              // bytes of A (buffer range)
+  int gate_bf16, E, K, Nout, topk, gather, interleaved, act;
+  ActParams prm;
+};
 
 template <typename T> struct Mma;
 template <> struct Mma<bf16_t> {
@@ -59,8 +78,43 @@ template <> struct Mma<float> {
   }
 };
 
-// 16-byte LDS slot of (row, chunk) after the XOR swizzle.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kChunks + (chunk ^ (row & 7)); }
+// LDS byte offset of (row, logical 16-byte chunk) after the XOR swizzle.  A
+// ds_read_b128 is served 16 lanes at a time from 64 four-byte banks (256
+// bytes), i.e. two 128-byte rows per bank line: rows of equal parity share
+// banks, so the XOR key is (row / 2) % 8 -- the 8 same-parity rows among any 16
+// consecutive rows then hit 8 distinct 16-byte slots.
+__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ swz_key(row)) << 4);
+}
+
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4 left at 7, lgkmcnt 11:8 = 0).
+template <int N> __device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// 16 bytes per lane from buffer `r` at byte offset `voff` into LDS at
+// lds + 16 * lane (lds must be the same for the whole wave).  Issued as inline
+// asm so the compiler does not track the LDS write: left to itself it waits for
+// every outstanding load before any LDS read, which would serialise the ring.
+// The waits for these loads are the explicit wait_vm<> calls.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char *lds, uint32_t voff) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(void __attribute__((address_space(3))) *)lds;
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(m0))
+      : "memory", "m0");
+}
 
 __device__ __forceinline__ float act_fn(int act, float g, float u, const ActParams &p) {
   if (act == MOE_ACT_RELU2) {
@@ -72,32 +126,85 @@ __device__ __forceinline__ float act_fn(int act, float g, float u, const ActPara
   return gc * (1.f / (1.f + expf(-p.alpha * gc))) * (uc + p.beta);
 }
 
-template <typename T, int NSETS, int EPI>
-__global__ __launch_bounds__(kThreads) void grouped_gemm(
-    const T *__restrict__ A, const T *__restrict__ W, T *__restrict__ C,
-    const int32_t *__restrict__ offsets, const int32_t *__restrict__ col_sorted,
-    const void *__restrict__ gate_scal, int gate_bf16, int E, int K, int Nout, int topk,
-    int gather, int interleaved, int act, ActParams prm) {
+// Where tile L of the expert-major tile order lives: expert e, output-column
+// tile nt, and the rows [row0, row0 + rows) of the expert's sorted segment.
+// Inside an expert, tiles are walked in blocks of GM m-tiles x GN n-tiles
+// (n-block outer, m-block inner, m-tile fastest inside a block), so the 32
+// workgroups one XCD runs at a time share each row tile GN ways and each weight
+// tile GM ways.
+constexpr int GM = 8, GN = 4;
+
+struct TileInfo {
+  int e, row0, rows, n0;
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ TileInfo tile_info(int L, const int *s_ts, const int32_t *offsets,
+                                              int E, int n_nt) {
+  const int q = L / n_nt;  // s_ts[e] <= q < s_ts[e + 1] exactly when L is in expert e
+  int lo = 0, hi = E - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s_ts[mid] <= q) lo = mid; else hi = mid - 1;
+  }
+  const int me = s_ts[lo + 1] - s_ts[lo];  // m-tiles of this expert
+  const int l = L - s_ts[lo] * n_nt;
+  const int nb = l / (GN * me);
+  const int gn = min(GN, n_nt - nb * GN);
+  const int r = l - nb * GN * me;
+  const int mb = r / (GM * gn);
+  const int gm = min(GM, me - mb * GM);
+  const int r2 = r - mb * GM * gn;
+  const int mt = mb * GM + r2 % gm;
+  const int nt = nb * GN + r2 / gm;
+  TileInfo ti;
+  ti.e = lo;
+  ti.row0 = offsets[lo] + mt * BM;
+  ti.rows = min(BM, offsets[lo + 1] - ti.row0);
+  ti.n0 = nt * BN;
+  return ti;
+}
+
+// Tile of BM rows x BN output columns; WM x WN waves; S-stage LDS ring.
+//
+// Work split: tiles are ordered expert by expert (within an expert n-tile-
+// major, m-tile fastest) and cut into 8 contiguous chunks, one per XCD; the
+// dispatcher places workgroup b on XCD b % 8, so the workgroups of one XCD --
+// which share that XCD's L2 -- walk one chunk together: concurrently they hold
+// neighbouring m-tiles of the same weight tile, or neighbouring n-tiles of the
+// same rows.  A workgroup's tiles form one stream of K-slices: the ring keeps
+// loading S - 1 slices ahead across tile boundaries, so a tile's epilogue runs
+// while the next tile's first slices are in flight.
+template <typename T, int NSETS, int EPI, int BM, int BN, int WM, int WN, int S>
+__global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
   using Mm = Mma<T>;
   using Frag = typename Mm::Frag;
   constexpr int BK = Mm::BK;
-  constexpr int NB = NSETS * BN;  // B rows per tile
-  constexpr int A_CH = BM * kChunks / kThreads;
-  constexpr int B_CH = NB * kChunks / kThreads;
+  constexpr int NW = WM * WN;
+  constexpr int NB = NSETS * BN;          // B rows per tile
+  constexpr int JA = BM / 8 / NW;         // 1 KB A loads per wave per slice
+  constexpr int JB = NB / 8 / NW;
+  constexpr int TM = BM / WM / 32;        // 32x32 sub-tiles per wave
+  constexpr int TN = BN / WN / 32;
+  constexpr int STAGE = (BM + NB) * kRowBytes;
+  static_assert(JA * 8 * NW == BM && JB * 8 * NW == NB, "tile rows vs waves");
+  static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "wave tiles");
+  static_assert(S >= 2 && S <= 4 && (S - 2) * (JA + JB) < 64, "stages / vmcnt range");
 
-  __shared__ u32x4_t sA[2][BM * kChunks];
-  __shared__ u32x4_t sB[2][NB * kChunks];
+  __shared__ __attribute__((aligned(16))) char smem[S * STAGE];
   __shared__ int s_ts[kMaxExperts + 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
+  const int E = g.E, K = g.K, Nout = g.Nout;
 
-  // ---- which expert and rows this workgroup owns ---------------------------
+  // ---- tile starts per expert (same in every workgroup) ---------------------
   if (wave == 0) {
     int v[4], s = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
-      v[q] = (e < E) ? (offsets[e + 1] - offsets[e] + BM - 1) / BM : 0;
+      v[q] = (e < E) ? (g.offsets[e + 1] - g.offsets[e] + BM - 1) / BM : 0;
       s += v[q];
     }
     int incl = s;
@@ -116,170 +223,232 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm(
     if (lane == 63) s_ts[E] = incl;
   }
   __syncthreads();
-  const int n_ntiles = (Nout + BN - 1) / BN;
-  const int mt = blockIdx.x / n_ntiles;  // n-tiles of one m-tile are adjacent
-  const int nt = blockIdx.x - mt * n_ntiles;
-  if (mt >= s_ts[E]) return;  // uniform: surplus tile slot
-  int lo = 0, hi = E - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (s_ts[mid] <= mt) lo = mid; else hi = mid - 1;
-  }
-  const int e = lo;
-  const int row0 = offsets[e] + (mt - s_ts[e]) * BM;
-  const int rows = min(BM, offsets[e + 1] - row0);
-  const int n0 = nt * BN;
-  const T *We = W + (int64_t)e * NSETS * Nout * K;
 
-  // ---- per-thread global sources of its 16-byte chunks ---------------------
-  // A: byte offsets from A (gathered rows for GEMM1), -1 for rows past the
-  // segment; B: byte offsets inside this expert's weight block, -1 past Nout.
-  int64_t a_off[A_CH];
-  int b_off[B_CH];
-#pragma unroll
-  for (int i = 0; i < A_CH; ++i) {
-    const int c = tid + i * kThreads, r = c / kChunks, ch = c % kChunks;
-    a_off[i] = -1;
-    if (r < rows) {
-      const int p = row0 + r;
-      const int64_t arow = gather ? (int64_t)(col_sorted[p] / topk) : (int64_t)p;
-      a_off[i] = arow * K * (int64_t)sizeof(T) + ch * 16;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < B_CH; ++i) {
-    const int c = tid + i * kThreads, r = c / kChunks, ch = c % kChunks;
-    const int set = r / BN, n = n0 + r % BN;
-    b_off[i] = -1;
-    if (n < Nout) {
-      const int grow = NSETS == 1 ? n : (interleaved ? 2 * n + set : set * Nout + n);
-      b_off[i] = grow * K * (int)sizeof(T) + ch * 16;
-    }
-  }
-  const char *Ab = reinterpret_cast<const char *>(A);
-  const char *Bb = reinterpret_cast<const char *>(We);
+  const int n_nt = (Nout + BN - 1) / BN;
+  const int total = s_ts[E] * n_nt;
+  // this workgroup's tiles: L = first + i * stride, i < my_tiles
+  const int gx = (int)gridDim.x / 8;  // workgroups per XCD (grid is a multiple of 8)
+  const int xcd = (int)blockIdx.x % 8, qx = (int)blockIdx.x / 8;
+  const int chunk = (total + 7) / 8;
+  const int cbeg = min(total, xcd * chunk), cend = min(total, cbeg + chunk);
+  const int first = cbeg + qx;
+  const int my_tiles = first < cend ? (cend - first + gx - 1) / gx : 0;
 
   const int kbytes = K * (int)sizeof(T);
   const int nk = (K + BK - 1) / BK;
-  u32x4_t ra[A_CH], rb[B_CH];
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  const int nz = my_tiles * nk;  // K-slices in this workgroup's stream
+  const int lrow = lane >> 3;  // row within a 1 KB load; the lane fills physical chunk lane % 8
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void *>(g.A), (short)0, (int)g.a_bytes, kRsrcWord3);
+  const uint32_t w_bytes = (uint32_t)NSETS * Nout * kbytes;
+  const int wm = wave % WM, wn = wave / WM;
 
-#define MOE_GLOAD(kt_)                                                                        \
-  do {                                                                                        \
-    const int kb_ = (kt_) * kRowBytes;                                                        \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) {                                        \
-      const int ch_ = (tid + i * kThreads) % kChunks;                                         \
-      ra[i] = (a_off[i] >= 0 && kb_ + ch_ * 16 < kbytes)                                      \
-                  ? *reinterpret_cast<const u32x4_t *>(Ab + a_off[i] + kb_) : zero;             \
-    }                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                        \
-      const int ch_ = (tid + i * kThreads) % kChunks;                                         \
-      rb[i] = (b_off[i] >= 0 && kb_ + ch_ * 16 < kbytes)                                      \
-                  ? *reinterpret_cast<const u32x4_t *>(Bb + b_off[i] + kb_) : zero;             \
-    }                                                                                         \
-  } while (0)
-#define MOE_SSTORE(st_)                                                                       \
-  do {                                                                                        \
-    _Pragma("unroll") for (int i = 0; i < A_CH; ++i) {                                        \
-      const int c_ = tid + i * kThreads;                                                      \
-      sA[(st_)][swz(c_ / kChunks, c_ % kChunks)] = ra[i];                                     \
-    }                                                                                         \
-    _Pragma("unroll") for (int i = 0; i < B_CH; ++i) {                                        \
-      const int c_ = tid + i * kThreads;                                                      \
-      sB[(st_)][swz(c_ / kChunks, c_ % kChunks)] = rb[i];                                     \
-    }                                                                                         \
-  } while (0)
+  // issue side: the tile whose slices are being loaded
+  uint32_t va[JA], vb[JB];
+  __amdgpu_buffer_rsrc_t rb = ra;
+  auto setup_issue = [&](int i) {
+    const TileInfo ti = tile_info<BM, BN>(first + i * gx, s_ts, g.offsets, E, n_nt);
+    rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(reinterpret_cast<const char *>(g.W)) + (size_t)ti.e * w_bytes,
+        (short)0, (int)w_bytes, kRsrcWord3);
+#pragma unroll
+    for (int j = 0; j < JA; ++j) {
+      const int r = (wave * JA + j) * 8 + lrow;
+      va[j] = kOOB;
+      if (r < ti.rows) {
+        const int p = ti.row0 + r;
+        const uint32_t arow = g.gather ? (uint32_t)(g.col_sorted[p] / g.topk) : (uint32_t)p;
+        va[j] = arow * (uint32_t)kbytes + (((lane & 7) ^ swz_key(r)) << 4);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < JB; ++j) {
+      const int r = (wave * JB + j) * 8 + lrow;
+      const int set = r / BN, n = ti.n0 + r % BN;
+      vb[j] = kOOB;
+      if (n < Nout) {
+        const int grow = NSETS == 1 ? n : (g.interleaved ? 2 * n + set : set * Nout + n);
+        vb[j] = (uint32_t)grow * (uint32_t)kbytes + (((lane & 7) ^ swz_key(r)) << 4);
+      }
+    }
+  };
+  auto issue = [&](int z) {  // load slice z of the stream into ring slot z % S
+    const int i = z / nk, kt = z - i * nk;
+    if (kt == 0) setup_issue(i);
+    const uint32_t kb = (uint32_t)kt * kRowBytes;
+    char *base = smem + (z % S) * STAGE;
+    // kOOB + kb stays out of range, so invalid rows / columns need no test;
+    // only a K-tail slice (kb + 128 > row bytes) masks chunks past K.  Rows
+    // are K * sizeof(T) bytes, a multiple of 16, so the tail is chunk-aligned.
+    if ((int)kb + kRowBytes <= kbytes) {
+#pragma unroll
+      for (int j = 0; j < JA; ++j) dma16(ra, base + (wave * JA + j) * 1024, va[j] + kb);
+#pragma unroll
+      for (int j = 0; j < JB; ++j)
+        dma16(rb, base + BM * kRowBytes + (wave * JB + j) * 1024, vb[j] + kb);
+    } else {
+#pragma unroll
+      for (int j = 0; j < JA; ++j) {
+        const int coff = ((lane & 7) ^ swz_key((wave * JA + j) * 8 + lrow)) << 4;
+        dma16(ra, base + (wave * JA + j) * 1024, (int)kb + coff < kbytes ? va[j] + kb : kOOB);
+      }
+#pragma unroll
+      for (int j = 0; j < JB; ++j) {
+        const int coff = ((lane & 7) ^ swz_key((wave * JB + j) * 8 + lrow)) << 4;
+        dma16(rb, base + BM * kRowBytes + (wave * JB + j) * 1024,
+              (int)kb + coff < kbytes ? vb[j] + kb : kOOB);
+      }
+    }
+  };
 
-  const int wm = wave & 1, wn = wave >> 1;
-  f32x16_t acc[2][2][NSETS];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int s = 0; s < NSETS; ++s)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][s][r] = 0.f;
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nz) issue(s);
 
-  MOE_GLOAD(0);
-  MOE_SSTORE(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    __syncthreads();
-    const int st = kt & 1;
-    if (kt + 1 < nk) MOE_GLOAD(kt + 1);
-    const char *la = reinterpret_cast<const char *>(sA[st]);
-    const char *lb = reinterpret_cast<const char *>(sB[st]);
+  f32x16_t acc[TM][TN][NSETS];
+  T *C = reinterpret_cast<T *>(g.C);
+  for (int z = 0; z < nz; ++z) {
+    // slices issued after z that may still be in flight: min(S - 2, nz - 1 - z)
+    const int pend = min(S - 2, nz - 1 - z);
+    if (pend >= 2) wait_vm<(S >= 4 ? 2 * (JA + JB) : 0)>();
+    else if (pend == 1) wait_vm<(S >= 3 ? JA + JB : 0)>();
+    else wait_vm<0>();
+    barrier();
+    if (z + S - 1 < nz) issue(z + S - 1);
+    const int kt = z % nk;
+    if (kt == 0) {
 #pragma unroll
-    for (int ks = 0; ks < BK / Mm::KS; ++ks) {
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][s][r] = 0.f;
+    }
+    const char *la = smem + (z % S) * STAGE;
+    const char *lb = la + BM * kRowBytes;
+    // fragments of k-step ks + 1 are read while the MFMAs of k-step ks run
+    constexpr int NKS = BK / Mm::KS;
+    Frag fa[2][TM], fb[2][TN][NSETS];
+    auto load_frags = [&](int buf, int ks) {
       const int byte = (ks * Mm::KS + (lane >> 5) * Mm::EPL) * (int)sizeof(T);
       const int ch = byte >> 4, inner = byte & 15;
-      Frag fa[2], fb[2][NSETS];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = wm * 64 + i * 32 + (lane & 31);
-        fa[i] = Mm::ld(la + swz(row, ch) * 16 + inner);
+      for (int i = 0; i < TM; ++i) {
+        const int row = wm * (BM / WM) + i * 32 + (lane & 31);
+        fa[buf][i] = Mm::ld(la + swz(row, ch) + inner);
       }
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int s = 0; s < NSETS; ++s) {
-          const int row = s * BN + wn * 64 + j * 32 + (lane & 31);
-          fb[j][s] = Mm::ld(lb + swz(row, ch) * 16 + inner);
+          const int row = s * BN + wn * (BN / WN) + j * 32 + (lane & 31);
+          fb[buf][j][s] = Mm::ld(lb + swz(row, ch) + inner);
+        }
+    };
+    load_frags(0, 0);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ks + 1 < NKS) load_frags((ks + 1) & 1, ks + 1);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int s = 0; s < NSETS; ++s)
+            acc[i][j][s] = Mm::mma(fa[ks & 1][i], fb[ks & 1][j][s], acc[i][j][s]);
+    }
+    if (kt != nk - 1) continue;
+
+    // ---- epilogue: lane holds column (lane % 32), 16 rows of each 32x32 ------
+    const TileInfo ti = tile_info<BM, BN>(first + (z / nk) * gx, s_ts, g.offsets, E, n_nt);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * (BM / WM) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row >= ti.rows) continue;
+        const int p = ti.row0 + row;
+        float gs = 1.f;
+        int64_t orow = p;
+        if (EPI != EPI_ACT) {
+          gs = g.gate_bf16 ? to_f32(reinterpret_cast<const bf16_t *>(g.gate_scal)[p])
+                           : reinterpret_cast<const float *>(g.gate_scal)[p];
+          if (EPI == EPI_OUT) orow = g.col_sorted[p];  // topk == 1: entry index == token
         }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int s = 0; s < NSETS; ++s) acc[i][j][s] = Mm::mma(fa[i], fb[j][s], acc[i][j][s]);
-    }
-    if (kt + 1 < nk) MOE_SSTORE((kt + 1) & 1);
-  }
-#undef MOE_GLOAD
-#undef MOE_SSTORE
-
-  // ---- epilogue: lane holds column (lane % 32) and 16 rows of each 32x32 ----
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (row >= rows) continue;
-      const int p = row0 + row;
-      float g = 1.f;
-      int64_t orow = p;
-      if (EPI != EPI_ACT) {
-        g = gate_bf16 ? to_f32(reinterpret_cast<const bf16_t *>(gate_scal)[p])
-                      : reinterpret_cast<const float *>(gate_scal)[p];
-        if (EPI == EPI_OUT) orow = col_sorted[p];  // topk == 1: entry index == token
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = n0 + wn * 64 + j * 32 + (lane & 31);
-        if (col >= Nout) continue;
-        float v;
-        if (EPI == EPI_ACT)
-          v = act_fn(act, acc[i][j][0][r], NSETS == 2 ? acc[i][j][NSETS - 1][r] : 0.f, prm);
-        else
-          v = acc[i][j][0][r] * g;
-        C[orow * Nout + col] = from_f32<T>(v);
+        for (int j = 0; j < TN; ++j) {
+          const int col = ti.n0 + wn * (BN / WN) + j * 32 + (lane & 31);
+          if (col >= Nout) continue;
+          float v;
+          if (EPI == EPI_ACT)
+            v = act_fn(g.act, acc[i][j][0][r], NSETS == 2 ? acc[i][j][NSETS - 1][r] : 0.f, g.prm);
+          else
+            v = acc[i][j][0][r] * gs;
+          C[orow * Nout + col] = from_f32<T>(v);
+        }
       }
     }
   }
 }
 
-template <typename T, int NSETS, int EPI>
-hipError_t launch_t(const void *A, const void *W, void *C, const int32_t *offsets,
-                    const int32_t *col_sorted, const void *gate_scal, int gate_bf16, int64_t M,
-                    int E, int K, int Nout, int topk, int gather, int interleaved, int act,
-                    ActParams prm, hipStream_t s) {
-  const int64_t mtiles = M / BM + (M < E ? M : E);
-  const dim3 grid((unsigned)(mtiles * ((Nout + BN - 1) / BN)));
-  hipLaunchKernelGGL((grouped_gemm<T, NSETS, EPI>), grid, dim3(kThreads), 0, s,
-                     reinterpret_cast<const T *>(A), reinterpret_cast<const T *>(W),
-                     reinterpret_cast<T *>(C), offsets, col_sorted, gate_scal, gate_bf16, E, K,
-                     Nout, topk, gather, interleaved, act, prm);
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  return cus;
+}
+
+template <int BM_, int BN_, int WM_, int WN_, int S_> struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_;
+};
+// Tile configurations, largest first (rows x output columns, waves rows x
+// columns, ring stages).  Gated tiles carry 2 * BN weight rows.
+using GatedL = Cfg<256, 128, 4, 2, 2>;  // 8 waves, 64 x (64 + 64) each
+using GatedM = Cfg<128, 128, 2, 4, 3>;  // 8 waves, 64 x (32 + 32) each
+using GatedS = Cfg<32, 128, 1, 4, 4>;   // 4 waves, 32 x (32 + 32) each
+using PlainL = Cfg<256, 256, 4, 2, 2>;  // 8 waves, 64 x 128 each
+using PlainM = Cfg<128, 128, 2, 2, 3>;  // 4 waves, 64 x 64 each
+using PlainS = Cfg<32, 128, 1, 4, 4>;   // 4 waves, 32 x 32 each
+
+template <typename C, int NSETS> constexpr int lds_bytes() {
+  return C::S * (C::BM + NSETS * C::BN) * kRowBytes + (kMaxExperts + 1) * 4;
+}
+
+// Upper bound on the tiles of one launch: floor(M / BM) + min(E, M) m-tiles.
+inline int64_t est_tiles(int64_t M, int E, int Nout, int BM, int BN) {
+  return (M / BM + (M < E ? M : E)) * ((Nout + BN - 1) / BN);
+}
+
+template <typename T, int NSETS, int EPI, typename C>
+hipError_t launch_cfg(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
+  constexpr int LDS = lds_bytes<C, NSETS>();
+  constexpr int per_cu = (160 * 1024) / LDS > 0 ? (160 * 1024) / LDS : 1;
+  const int64_t tiles = est_tiles(M, E, a.Nout, C::BM, C::BN);
+  int64_t grid = (int64_t)device_cus() * (per_cu < 2 ? per_cu : 2);
+  if (grid > tiles) grid = tiles;
+  grid = (grid + 7) / 8 * 8;  // whole XCD rounds; surplus workgroups get no tiles
+  hipLaunchKernelGGL((grouped_gemm<T, NSETS, EPI, C::BM, C::BN, C::WM, C::WN, C::S>),
+                     dim3((unsigned)grid), dim3(64 * C::WM * C::WN), 0, s, a);
   return hipGetLastError();
+}
+
+// The largest tile whose tile count still covers the machine; rows per expert
+// below 48 take the 32-row tile (weight streaming, little MFMA waste).
+template <typename T, int NSETS, int EPI>
+hipError_t launch_t(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
+  using L = typename std::conditional<NSETS == 2, GatedL, PlainL>::type;
+  using Md = typename std::conditional<NSETS == 2, GatedM, PlainM>::type;
+  using Sm = typename std::conditional<NSETS == 2, GatedS, PlainS>::type;
+  const int64_t cus = device_cus();
+  if (M < 48 * (int64_t)E) return launch_cfg<T, NSETS, EPI, Sm>(a, M, E, s);
+  if (est_tiles(M, E, a.Nout, L::BM, L::BN) >= cus) return launch_cfg<T, NSETS, EPI, L>(a, M, E, s);
+  if (est_tiles(M, E, a.Nout, Md::BM, Md::BN) >= cus / 2)
+    return launch_cfg<T, NSETS, EPI, Md>(a, M, E, s);
+  return launch_cfg<T, NSETS, EPI, Sm>(a, M, E, s);
 }
 
 }  // namespace
@@ -289,18 +458,15 @@ hipError_t launch_gemm1(const void *x, const void *w13, void *act_out, const int
                         int n_experts, int hidden, int inter, moe_act_t act,
                         moe_w13_layout_t layout, ActParams p, hipStream_t s) {
   const int64_t M = n_tokens * topk;
-  const int il = layout == MOE_W13_INTERLEAVED;
+  const size_t es = dt == MOE_BF16 ? 2 : 4;
+  GemmArgs a{x, w13, act_out, offsets, col_sorted, nullptr, (uint32_t)(n_tokens * hidden * es),
+             0, n_experts, hidden, inter, topk, 1, layout == MOE_W13_INTERLEAVED, act, p};
   const bool gated = act != MOE_ACT_RELU2;
-  if (dt == MOE_BF16) {
-    return gated ? launch_t<bf16_t, 2, EPI_ACT>(x, w13, act_out, offsets, col_sorted, nullptr, 0, M,
-                                               n_experts, hidden, inter, topk, 1, il, act, p, s)
-                 : launch_t<bf16_t, 1, EPI_ACT>(x, w13, act_out, offsets, col_sorted, nullptr, 0, M,
-                                               n_experts, hidden, inter, topk, 1, il, act, p, s);
-  }
-  return gated ? launch_t<float, 2, EPI_ACT>(x, w13, act_out, offsets, col_sorted, nullptr, 0, M,
-                                            n_experts, hidden, inter, topk, 1, il, act, p, s)
-               : launch_t<float, 1, EPI_ACT>(x, w13, act_out, offsets, col_sorted, nullptr, 0, M,
-                                            n_experts, hidden, inter, topk, 1, il, act, p, s);
+  if (dt == MOE_BF16)
+    return gated ? launch_t<bf16_t, 2, EPI_ACT>(a, M, n_experts, s)
+                 : launch_t<bf16_t, 1, EPI_ACT>(a, M, n_experts, s);
+  return gated ? launch_t<float, 2, EPI_ACT>(a, M, n_experts, s)
+               : launch_t<float, 1, EPI_ACT>(a, M, n_experts, s);
 }
 
 hipError_t launch_gemm2(const void *act_in, const void *w2, void *y, const int32_t *offsets,
@@ -308,20 +474,15 @@ hipError_t launch_gemm2(const void *act_in, const void *w2, void *y, const int32
                         moe_dtype_t dt, int64_t n_tokens, int topk, int n_experts, int hidden,
                         int inter, bool direct_out, hipStream_t s) {
   const int64_t M = n_tokens * topk;
-  const int gb = gate_dt == MOE_BF16;
-  const ActParams none{1.f, 0.f, 0.f};
-  if (dt == MOE_BF16) {
-    return direct_out
-               ? launch_t<bf16_t, 1, EPI_OUT>(act_in, w2, y, offsets, col_sorted, gate_scal, gb, M,
-                                              n_experts, inter, hidden, topk, 0, 0, 0, none, s)
-               : launch_t<bf16_t, 1, EPI_Y>(act_in, w2, y, offsets, col_sorted, gate_scal, gb, M,
-                                            n_experts, inter, hidden, topk, 0, 0, 0, none, s);
-  }
-  return direct_out
-             ? launch_t<float, 1, EPI_OUT>(act_in, w2, y, offsets, col_sorted, gate_scal, gb, M,
-                                           n_experts, inter, hidden, topk, 0, 0, 0, none, s)
-             : launch_t<float, 1, EPI_Y>(act_in, w2, y, offsets, col_sorted, gate_scal, gb, M,
-                                         n_experts, inter, hidden, topk, 0, 0, 0, none, s);
+  const size_t es = dt == MOE_BF16 ? 2 : 4;
+  GemmArgs a{act_in, w2, y, offsets, col_sorted, gate_scal, (uint32_t)(M * inter * es),
+             gate_dt == MOE_BF16, n_experts, inter, hidden, topk, 0, 0, 0,
+             ActParams{1.f, 0.f, 0.f}};
+  if (dt == MOE_BF16)
+    return direct_out ? launch_t<bf16_t, 1, EPI_OUT>(a, M, n_experts, s)
+                      : launch_t<bf16_t, 1, EPI_Y>(a, M, n_experts, s);
+  return direct_out ? launch_t<float, 1, EPI_OUT>(a, M, n_experts, s)
+                    : launch_t<float, 1, EPI_Y>(a, M, n_experts, s);
 }
 
 }  // namespace moe

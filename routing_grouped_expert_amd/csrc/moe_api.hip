@@ -90,8 +90,11 @@ moe_status_t check_expert_args(moe_dtype_t dtype, int64_t n, int32_t hidden, int
   if (st != MOE_OK) return st;
   if ((st = check_ffn_sizes(hidden, inter)) != MOE_OK) return st;
   if (!dtype_ok(dtype)) return MOE_ERR_DTYPE;
-  // one expert's w13 / w2 block is addressed with 32-bit byte offsets
-  if ((int64_t)2 * inter * hidden * (int64_t)dsize(dtype) > (int64_t)0x7fffffff)
+  // the GEMMs address one expert's w13 / w2 block, x and the activation rows
+  // with 32-bit byte offsets
+  const int64_t lim = 0x7fffffff, es = (int64_t)dsize(dtype);
+  if ((int64_t)2 * inter * hidden * es > lim || n * hidden * es > lim ||
+      n * k * (int64_t)inter * es > lim)
     return MOE_ERR_SHAPE;
   if ((st = act_params(act, layout, params, prm)) != MOE_OK) return st;
   return check_routing_struct(routing, false, n);
