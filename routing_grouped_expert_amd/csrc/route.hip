@@ -29,6 +29,21 @@ namespace {
 
 template <typename T> struct Logit;
 
+// 16 bytes of one token's logits row (values e0 .. e0 + kVec - 1), zero past E.
+__device__ __forceinline__ uint32_t bits_of(bf16_t v) { return v; }
+__device__ __forceinline__ uint32_t bits_of(float v) { return __float_as_uint(v); }
+
+template <typename T>
+__device__ __forceinline__ u32x4_t fetch16(const T *row, int e0, int E, bool vec) {
+  if (vec) return *reinterpret_cast<const u32x4_t *>(row + e0);
+  constexpr int V = 16 / sizeof(T), PW = 4 / sizeof(T);  // values per 32-bit word
+  u32x4_t r = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < V; ++i)
+    if (e0 + i < E) r[i / PW] |= bits_of(row[e0 + i]) << (32 / PW * (i % PW));
+  return r;
+}
+
 // bf16 logits: key = ordered 16 value bits << 16 | (0xffff - expert).
 template <> struct Logit<bf16_t> {
   typedef uint32_t Key;
@@ -44,18 +59,12 @@ template <> struct Logit<bf16_t> {
     const uint32_t bits = (ord & 0x8000u) ? (ord & 0x7fffu) : (~ord & 0xffffu);
     return __uint_as_float(bits << 16);
   }
-  __device__ static void load(const bf16_t *row, int e0, int E, bool vec, Key (&k)[kVec]) {
-    if (vec) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(row + e0);
-      const uint32_t w[4] = {v[0], v[1], v[2], v[3]};
+  // keys of values e0 .. e0 + 7; values past E (zero-filled) get key 0
+  __device__ static void decode(u32x4_t v, int e0, int E, Key (&k)[kVec]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        k[2 * i] = key(w[i] & 0xffffu, e0 + 2 * i);
-        k[2 * i + 1] = key(w[i] >> 16, e0 + 2 * i + 1);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kVec; ++i) k[i] = (e0 + i < E) ? key(row[e0 + i], e0 + i) : 0u;
+    for (int i = 0; i < 4; ++i) {
+      k[2 * i] = (e0 + 2 * i < E) ? key(v[i] & 0xffffu, e0 + 2 * i) : 0u;
+      k[2 * i + 1] = (e0 + 2 * i + 1 < E) ? key(v[i] >> 16, e0 + 2 * i + 1) : 0u;
     }
   }
 };
@@ -75,28 +84,38 @@ template <> struct Logit<float> {
     const uint32_t bits = (ord & 0x80000000u) ? (ord & 0x7fffffffu) : ~ord;
     return __uint_as_float(bits);
   }
-  __device__ static void load(const float *row, int e0, int E, bool vec, Key (&k)[kVec]) {
-    if (vec) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t *>(row + e0);
-      k[0] = key(v[0], e0);
-      k[1] = key(v[1], e0 + 1);
-      k[2] = key(v[2], e0 + 2);
-      k[3] = key(v[3], e0 + 3);
-    } else {
+  __device__ static void decode(u32x4_t v, int e0, int E, Key (&k)[kVec]) {
 #pragma unroll
-      for (int i = 0; i < kVec; ++i)
-        k[i] = (e0 + i < E) ? key(__float_as_uint(row[e0 + i]), e0 + i) : 0ull;
-    }
+    for (int i = 0; i < 4; ++i) k[i] = (e0 + i < E) ? key(v[i], e0 + i) : 0ull;
   }
 };
 
-__device__ __forceinline__ uint32_t shfl_xor_key(uint32_t v, int m) {
-  return (uint32_t)__shfl_xor((int)v, m);
+// ---- in-group maximum of order keys -----------------------------------------
+// Groups of G lanes (G a power of two, aligned).  Steps inside a 16-lane row
+// use DPP row permutes (register-only): swap neighbours, swap pairs, mirror
+// each half-row, mirror the row.  After each step every lane holds the max of
+// a block twice as large.  Wider groups finish with cross-row shuffles.
+template <int CTRL> __device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
 }
-__device__ __forceinline__ unsigned long long shfl_xor_key(unsigned long long v, int m) {
-  const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, m);
-  const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), m);
-  return ((unsigned long long)hi << 32) | lo;
+template <int CTRL> __device__ __forceinline__ uint32_t dpp(uint32_t v) { return dpp32<CTRL>(v); }
+template <int CTRL> __device__ __forceinline__ unsigned long long dpp(unsigned long long v) {
+  return ((unsigned long long)dpp32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp32<CTRL>((uint32_t)v);
+}
+__device__ __forceinline__ uint32_t xshfl(uint32_t v, int m) { return (uint32_t)__shfl_xor((int)v, m); }
+__device__ __forceinline__ unsigned long long xshfl(unsigned long long v, int m) {
+  return ((unsigned long long)xshfl((uint32_t)(v >> 32), m) << 32) | xshfl((uint32_t)v, m);
+}
+template <typename K> __device__ __forceinline__ K kmax(K a, K b) { return a > b ? a : b; }
+
+template <typename K> __device__ __forceinline__ K group_max(K m, int G) {
+  if (G >= 2) m = kmax(m, dpp<0xB1>(m));    // quad_perm [1,0,3,2]
+  if (G >= 4) m = kmax(m, dpp<0x4E>(m));    // quad_perm [2,3,0,1]
+  if (G >= 8) m = kmax(m, dpp<0x141>(m));   // row_half_mirror
+  if (G >= 16) m = kmax(m, dpp<0x140>(m));  // row_mirror
+  if (G >= 32) m = kmax(m, xshfl(m, 16));
+  if (G >= 64) m = kmax(m, xshfl(m, 32));
+  return m;
 }
 
 // Exclusive scan of in[0..E) into out[0..E], out[E] = total; E <= 256.  Wave 0
@@ -130,194 +149,210 @@ __device__ void block_exclusive_scan(const int *in, int *out, int E) {
   __syncthreads();
 }
 
-template <typename T>
-__global__ __launch_bounds__(kRouteThreads) void route_topk_rank(
-    const T *__restrict__ logits, int64_t N, int E, int K, int logG, int vec,
-    int32_t *__restrict__ topk_idx, T *__restrict__ topk_w, uint32_t *__restrict__ bitmatrix,
-    int32_t *__restrict__ blk_cnt, uint8_t *__restrict__ blk_rank, int fused,
-    int32_t *__restrict__ col_sum, int32_t *__restrict__ offsets,
-    int32_t *__restrict__ col_sorted, int32_t *__restrict__ row_sorted,
-    T *__restrict__ gate_scal) {
-  using L = Logit<T>;
-  using Key = typename L::Key;
-  constexpr int V = L::kVec;
-  constexpr int kWords = kMaxExperts / 32;
+constexpr int kWords = kMaxExperts / 32;
 
-  __shared__ uint32_t s_bits[kRouteTokens][kWords];
-  __shared__ uint8_t s_sel[kRouteTokens * kMaxTopk];
-  __shared__ uint8_t s_rank[kRouteTokens * kMaxTopk];
-  __shared__ T s_w[kRouteTokens * kMaxTopk];
-  __shared__ unsigned long long s_mask[kRouteThreads / 64][kMaxExperts];
-  __shared__ int s_cnt[kRouteThreads / 64][kMaxExperts];
-  __shared__ int s_tot[kMaxExperts];
-  __shared__ int s_off[kMaxExperts + 1];
+// LDS of one routing chunk (NT tokens, one per thread in the rank phase).
+template <typename T, int NT> struct ChunkLds {
+  uint32_t bits[NT][kWords];               // bitmatrix rows of the chunk
+  uint8_t sel[NT * kMaxTopk];              // selected experts, slot order
+  T w[NT * kMaxTopk];                      // their weights (layer dtype)
+  float val[NT * kMaxTopk];                // their logits
+  unsigned long long mask[NT / 64][kMaxExperts];  // per-wave ballot masks
+  int cnt[NT / 64][kMaxExperts];           // per-wave counts -> exclusive wave bases
+  int tot[kMaxExperts];                    // chunk counts per expert
+};
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+// Phase A for tokens [tok0, tok0 + NT): top-k, softmax, topk_idx / topk_w /
+// bitmatrix rows to HBM, selected experts and bitmatrix rows to LDS.
+template <typename T, int NT, int THREADS>
+__device__ __forceinline__ void topk_chunk(const T *__restrict__ logits, int64_t N, int E, int K,
+                                           int logG, int vec, int64_t tok0,
+                                           int32_t *__restrict__ topk_idx,
+                                           T *__restrict__ topk_w,
+                                           uint32_t *__restrict__ bitmatrix,
+                                           ChunkLds<T, NT> &L) {
+  using Lg = Logit<T>;
+  using Key = typename Lg::Key;
+  constexpr int V = Lg::kVec;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int G = 1 << logG;
   const int tpp = 64 >> logG;  // tokens per wave pass
   const int grp = lane >> logG, lg = lane & (G - 1);
   const int words = (E + 31) >> 5;
-  const int64_t tok0 = (int64_t)blockIdx.x * kRouteTokens;
-
-  // ---- phase A: top-k + softmax + bitmatrix, G lanes per token ------------
-  for (int pass = 0; pass < G; ++pass) {
-    const int tl = wave * 64 + pass * tpp + grp;  // token within the block
-    const int64_t t = tok0 + tl;
-    const bool live = t < N;
-    const int e0 = lg * V;
-    Key key[V];
-    if (live && e0 < E) {
-      L::load(logits + t * E, e0, E, vec != 0, key);
-    } else {
+  // each of the THREADS / 64 waves takes TPW consecutive tokens of the chunk;
+  // many waves per SIMD overlap the serial reduction chains of their passes
+  constexpr int TPW = NT / (THREADS / 64);
+  const int npass = (TPW + tpp - 1) / tpp;
+  // A lane's 16-byte logit chunks for kBatch passes are fetched before any is
+  // used, so their loads overlap.  The batch is kept small: these kernels run
+  // their code once per wave, so every extra unrolled copy is paid in cold
+  // instruction-cache misses.
+  constexpr int kBatch = 4;
+  for (int pass0 = 0; pass0 < npass; pass0 += kBatch) {
+    u32x4_t raw[kBatch];
 #pragma unroll
-      for (int i = 0; i < V; ++i) key[i] = 0;
+    for (int q = 0; q < kBatch; ++q) {
+      const int slot = (pass0 + q) * tpp + grp;  // token slot within the wave
+      const int64_t t = tok0 + wave * TPW + slot;
+      raw[q] = u32x4_t{0u, 0u, 0u, 0u};
+      if (slot < TPW && t < N && lg * V < E) raw[q] = fetch16(logits + t * E, lg * V, E, vec != 0);
     }
-    int sel_e[kMaxTopk];
-    float sel_v[kMaxTopk];
 #pragma unroll
-    for (int j = 0; j < kMaxTopk; ++j) {
-      sel_e[j] = 0;
-      sel_v[j] = 0.f;
-      if (j < K) {
-        Key m = key[0];
+    for (int q = 0; q < kBatch; ++q) {
+      const int slot = (pass0 + q) * tpp + grp;
+      if (pass0 + q < npass) {
+        const int tl = wave * TPW + slot;  // token within the chunk
+        const int64_t t = tok0 + tl;
+        const bool inwave = slot < TPW;
+        const bool live = inwave && t < N;
+        const int e0 = lg * V;
+        Key key[V];
+        Lg::decode(raw[q], e0, live ? E : 0, key);
+        // k rounds: the group's largest remaining key; its owner clears it.
+        // Slot j's expert and logit go to LDS (the group's lanes share them).
+        uint32_t word = 0;  // bitmatrix word lg of this token
+        for (int j = 0; j < K; ++j) {
+          Key m = key[0];
 #pragma unroll
-        for (int i = 1; i < V; ++i) m = key[i] > m ? key[i] : m;
-        for (int d = 1; d < G; d <<= 1) {
-          const Key o = shfl_xor_key(m, d);
-          m = o > m ? o : m;
+          for (int i = 1; i < V; ++i) m = kmax(m, key[i]);
+          m = group_max(m, G);
+          const int e = Lg::expert(m);
+#pragma unroll
+          for (int i = 0; i < V; ++i)
+            if (e0 + i == e) key[i] = 0;  // only the owning lane matches
+          if ((e >> 5) == lg) word |= 1u << (e & 31);
+          if (lg == 0 && inwave) {
+            L.sel[tl * K + j] = (uint8_t)e;
+            L.val[tl * K + j] = Lg::value(m);
+          }
         }
-        const int e = L::expert(m);
-        sel_e[j] = e;
-        sel_v[j] = L::value(m);
-#pragma unroll
-        for (int i = 0; i < V; ++i)
-          if (e0 + i == e) key[i] = 0;  // only the owning lane matches
-      }
-    }
-    // softmax over the selected logits (slot 0 holds the maximum)
-    float ex[kMaxTopk];
-    float ssum = 0.f;
-#pragma unroll
-    for (int j = 0; j < kMaxTopk; ++j) {
-      ex[j] = 0.f;
-      if (j < K) {
-        ex[j] = expf(sel_v[j] - sel_v[0]);
-        ssum += ex[j];
-      }
-    }
-    if (live) {
-#pragma unroll
-      for (int j = 0; j < kMaxTopk; ++j) {
-        if (j < K) {
-          const T w = from_f32<T>(ex[j] / ssum);
-          if ((j & (G - 1)) == lg) {
-            topk_idx[t * K + j] = sel_e[j];
+        if (live) {
+          // softmax over the selected logits, summed in slot order; slot 0 is the max
+          const float* vals = &L.val[tl * K];
+          const float vmax = vals[0];
+          float ssum = 0.f;
+          for (int j = 0; j < K; ++j) ssum += expf(vals[j] - vmax);
+          for (int j = lg; j < K; j += G) {
+            const T w = from_f32<T>(expf(vals[j] - vmax) / ssum);
+            topk_idx[t * K + j] = L.sel[tl * K + j];
             topk_w[t * K + j] = w;
+            L.w[tl * K + j] = w;
           }
-          if (lg == 0) {
-            s_sel[tl * K + j] = (uint8_t)sel_e[j];
-            s_w[tl * K + j] = w;
+          if (lg < words) {
+            bitmatrix[t * words + lg] = word;
+            L.bits[tl][lg] = word;
           }
-        }
-      }
-#pragma unroll
-      for (int wd = 0; wd < kWords; ++wd) {
-        if (wd < words && (wd & (G - 1)) == lg) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int j = 0; j < kMaxTopk; ++j)
-            if (j < K && (sel_e[j] >> 5) == wd) word |= 1u << (sel_e[j] & 31);
-          bitmatrix[t * words + wd] = word;
-          s_bits[tl][wd] = word;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int wd = 0; wd < kWords; ++wd)
-        if (wd < words && (wd & (G - 1)) == lg) s_bits[tl][wd] = 0u;
-    }
-  }
-  __syncthreads();
-
-  // ---- phase B: per-wave expert masks by ballot; thread tid owns token tid --
-  {
-    uint32_t myb[kWords];
-#pragma unroll
-    for (int wd = 0; wd < kWords; ++wd) myb[wd] = (wd < words) ? s_bits[tid][wd] : 0u;
-    unsigned long long mk[kMaxExperts / 64] = {0ull, 0ull, 0ull, 0ull};
-#pragma unroll
-    for (int wd = 0; wd < kWords; ++wd) {
-      if (wd < words) {
-#pragma unroll
-        for (int b = 0; b < 32; ++b) {
-          const int e = wd * 32 + b;
-          if (e < E) {
-            const unsigned long long m = __ballot((myb[wd] >> b) & 1u);
-            if (lane == (e & 63)) mk[wd >> 1] = m;
-          }
+        } else if (inwave && lg < words) {
+          L.bits[tl][lg] = 0u;
         }
       }
     }
-#pragma unroll
-    for (int q = 0; q < kMaxExperts / 64; ++q) {
-      const int e = q * 64 + lane;
-      if (e < E) {
-        s_mask[wave][e] = mk[q];
-        s_cnt[wave][e] = popc64(mk[q]);
-      }
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < E; e += kRouteThreads) {
-    int run = 0;
-#pragma unroll
-    for (int w = 0; w < kRouteThreads / 64; ++w) {
-      const int c = s_cnt[w][e];
-      s_cnt[w][e] = run;  // exclusive prefix over the block's waves
-      run += c;
-    }
-    s_tot[e] = run;
-  }
-  __syncthreads();
-  {
-    const int64_t t = tok0 + tid;
-    if (t < N) {
-      const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
-#pragma unroll
-      for (int j = 0; j < kMaxTopk; ++j) {
-        if (j < K) {
-          const int e = s_sel[tid * K + j];
-          const int r = s_cnt[wave][e] + popc64(s_mask[wave][e] & below);
-          if (fused)
-            s_rank[tid * K + j] = (uint8_t)r;
-          else
-            blk_rank[t * K + j] = (uint8_t)r;
-        }
-      }
-    }
-  }
-  if (!fused) {
-    for (int e = tid; e < E; e += kRouteThreads) blk_cnt[(int64_t)blockIdx.x * E + e] = s_tot[e];
-    return;
-  }
-
-  // ---- fused tail (a single block holds every token) -----------------------
-  __syncthreads();
-  block_exclusive_scan(s_tot, s_off, E);
-  for (int e = tid; e <= E; e += kRouteThreads) {
-    offsets[e] = s_off[e];
-    if (e < E) col_sum[e] = s_tot[e];
-  }
-  const int M = (int)N * K;
-  for (int f = tid; f < M; f += kRouteThreads) {
-    const int p = s_off[s_sel[f]] + s_rank[f];
-    col_sorted[p] = f;
-    row_sorted[f] = p;
-    gate_scal[p] = s_w[f];
   }
 }
 
+// Phase B: per-wave ballot masks per expert (thread tid owns chunk token tid),
+// exclusive wave bases in L.cnt, chunk totals in L.tot.  Ends synchronised.
+template <typename T, int NT>
+__device__ __forceinline__ void rank_chunk(int E, ChunkLds<T, NT> &L) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (tid < NT) {  // thread tid owns chunk token tid (wave-uniform condition)
+    uint32_t w = 0;
+    for (int e = 0; e < E; ++e) {  // a runtime loop keeps the code small
+      if ((e & 31) == 0) w = L.bits[tid][e >> 5];
+      const unsigned long long m = __ballot((w >> (e & 31)) & 1u);
+      if (lane == (e & 63)) {
+        L.mask[wave][e] = m;
+        L.cnt[wave][e] = popc64(m);
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) {
+    int run = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < NT / 64; ++w2) {
+      const int c = L.cnt[w2][e];
+      L.cnt[w2][e] = run;  // exclusive prefix over the chunk's waves
+      run += c;
+    }
+    L.tot[e] = run;
+  }
+  __syncthreads();
+}
+
+// Rank within the chunk of slot j of chunk token tid (expert e = L.sel[...]).
+template <typename T, int NT>
+__device__ __forceinline__ int chunk_rank(const ChunkLds<T, NT> &L, int e) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  return L.cnt[wave][e] + popc64(L.mask[wave][e] & below);
+}
+
+// Small batches (N <= NT tokens): one workgroup, one launch.  Every per-entry
+// value stays in LDS; the scan and the scatter follow the rank phase directly.
+template <typename T, int NT, int THREADS>
+__global__ __launch_bounds__(THREADS) void route_fused(
+    const T *__restrict__ logits, int64_t N, int E, int K, int logG, int vec,
+    int32_t *__restrict__ topk_idx, T *__restrict__ topk_w, uint32_t *__restrict__ bitmatrix,
+    int32_t *__restrict__ col_sum, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ col_sorted, int32_t *__restrict__ row_sorted,
+    T *__restrict__ gate_scal) {
+  __shared__ ChunkLds<T, NT> L;
+  __shared__ uint16_t s_rank[NT * kMaxTopk];
+  __shared__ int s_off[kMaxExperts + 1];
+  const int tid = threadIdx.x;
+  topk_chunk<T, NT, THREADS>(logits, N, E, K, logG, vec, 0, topk_idx, topk_w, bitmatrix, L);
+  __syncthreads();
+  rank_chunk<T, NT>(E, L);
+  if (tid < N) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j)
+      if (j < K) s_rank[tid * K + j] = (uint16_t)chunk_rank<T, NT>(L, L.sel[tid * K + j]);
+  }
+  block_exclusive_scan(L.tot, s_off, E);  // synchronises
+  for (int e = tid; e <= E; e += THREADS) {
+    offsets[e] = s_off[e];
+    if (e < E) col_sum[e] = L.tot[e];
+  }
+  const int M = (int)N * K;
+  for (int f = tid; f < M; f += THREADS) {
+    const int p = s_off[L.sel[f]] + s_rank[f];
+    col_sorted[p] = f;
+    row_sorted[f] = p;
+    gate_scal[p] = L.w[f];
+  }
+}
+
+// Multi-block path, kernel 1: one chunk of kRouteTokens tokens per workgroup;
+// per-block expert counts and per-entry in-block ranks to the workspace.
+constexpr int kTopkThreads = 1024;
+
+template <typename T>
+__global__ __launch_bounds__(kTopkThreads) void route_topk_rank(
+    const T *__restrict__ logits, int64_t N, int E, int K, int logG, int vec,
+    int32_t *__restrict__ topk_idx, T *__restrict__ topk_w, uint32_t *__restrict__ bitmatrix,
+    int32_t *__restrict__ blk_cnt, uint8_t *__restrict__ blk_rank) {
+  __shared__ ChunkLds<T, kRouteThreads> L;
+  const int tid = threadIdx.x;
+  const int64_t tok0 = (int64_t)blockIdx.x * kRouteTokens;
+  topk_chunk<T, kRouteThreads, kTopkThreads>(logits, N, E, K, logG, vec, tok0, topk_idx, topk_w,
+                                             bitmatrix, L);
+  __syncthreads();
+  rank_chunk<T, kRouteThreads>(E, L);
+  const int64_t t = tok0 + tid;
+  if (tid < kRouteTokens && t < N) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j)
+      if (j < K) blk_rank[t * K + j] = (uint8_t)chunk_rank<T, kRouteThreads>(L, L.sel[tid * K + j]);
+  }
+  for (int e = tid; e < E; e += kTopkThreads) blk_cnt[(int64_t)blockIdx.x * E + e] = L.tot[e];
+}
+
+// Multi-block path, kernel 2: workgroup b scatters routing block b.  It sums
+// the per-block counts (totals over all blocks, prefix over the blocks before
+// b) with the loads unrolled so they overlap, scans the totals into offsets
+// (workgroup 0 writes col_sum / offsets), and places every entry of its block
+// at offsets[e] + (entries of e in earlier blocks) + rank in the block.
 template <typename T>
 __global__ __launch_bounds__(kRouteThreads) void route_scatter(
     int64_t N, int E, int K, int nblocks, const int32_t *__restrict__ blk_cnt,
@@ -330,14 +365,40 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter(
   __shared__ int s_off[kMaxExperts + 1];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
-  for (int e = tid; e < E; e += kRouteThreads) {
-    int pre = 0, post = 0;
-    for (int bb = 0; bb < b; ++bb) pre += blk_cnt[(int64_t)bb * E + e];
-    for (int bb = b; bb < nblocks; ++bb) post += blk_cnt[(int64_t)bb * E + e];
-    s_tot[e] = pre + post;
-    s_base[e] = pre;
+  // each thread: one expert, a quarter of the blocks (E <= 256 threads x 4 parts)
+  {
+    const int parts = kRouteThreads / E >= 4 ? 4 : (kRouteThreads / E >= 2 ? 2 : 1);
+    const int e = tid % E, part = tid / E;
+    __shared__ int s_pre[4][kMaxExperts];
+    __shared__ int s_all[4][kMaxExperts];
+    if (part < parts) {
+      int pre = 0, all = 0;
+      constexpr int U = 8;
+      for (int bb0 = part * U; bb0 < nblocks; bb0 += parts * U) {
+        int c[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) c[u] = (bb0 + u < nblocks) ? blk_cnt[(int64_t)(bb0 + u) * E + e] : 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          all += c[u];
+          if (bb0 + u < b) pre += c[u];
+        }
+      }
+      s_pre[part][e] = pre;
+      s_all[part][e] = all;
+    }
+    __syncthreads();
+    for (int x = tid; x < E; x += kRouteThreads) {
+      int pre = 0, all = 0;
+      for (int q = 0; q < parts; ++q) {
+        pre += s_pre[q][x];
+        all += s_all[q][x];
+      }
+      s_base[x] = pre;
+      s_tot[x] = all;
+    }
+    __syncthreads();
   }
-  __syncthreads();
   block_exclusive_scan(s_tot, s_off, E);
   if (b == 0) {
     for (int e = tid; e <= E; e += kRouteThreads) {
@@ -347,18 +408,36 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter(
   }
   for (int e = tid; e < E; e += kRouteThreads) s_base[e] += s_off[e];
   __syncthreads();
-  const int64_t f0 = (int64_t)b * kRouteTokens * K;
-  const int64_t tend = ((int64_t)(b + 1) * kRouteTokens < N) ? (int64_t)(b + 1) * kRouteTokens : N;
-  const int64_t f1 = tend * K;
-  for (int64_t f = f0 + tid; f < f1; f += kRouteThreads) {
-    const int p = s_base[topk_idx[f]] + blk_rank[f];
-    col_sorted[p] = (int32_t)f;
-    row_sorted[f] = p;
-    gate_scal[p] = topk_w[f];
+  // the block's entries: token t = b * 256 + tid, slots 0..K-1 (all loads first)
+  const int64_t t = (int64_t)b * kRouteTokens + tid;
+  if (t < N) {
+    int ex[kMaxTopk], rk[kMaxTopk];
+    T w[kMaxTopk];
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j) {
+      if (j < K) {
+        ex[j] = topk_idx[t * K + j];
+        rk[j] = blk_rank[t * K + j];
+        w[j] = topk_w[t * K + j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j) {
+      if (j < K) {
+        const int p = s_base[ex[j]] + rk[j];
+        col_sorted[p] = (int32_t)(t * K + j);
+        row_sorted[t * K + j] = p;
+        gate_scal[p] = w[j];
+      }
+    }
   }
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+constexpr int kFusedTokens = 512;
+// One workgroup routes everything when the batch fits one chunk.
+inline bool use_fused(int64_t N, int E) { return N <= kFusedTokens; }
 
 template <typename T>
 hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, const moe_routing_t *r,
@@ -368,26 +447,29 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, const moe_ro
   int logG = 0;
   while ((1 << logG) < need) ++logG;
   const int vec = (E % V) == 0;
-  const int64_t nb = (N + kRouteTokens - 1) / kRouteTokens;
-  const int fused = nb == 1;
-  int32_t *blk_cnt = reinterpret_cast<int32_t *>(scratch);
-  uint8_t *blk_rank = reinterpret_cast<uint8_t *>(scratch) + align256((size_t)nb * E * 4);
   T *tw = reinterpret_cast<T *>(r->topk_w);
   T *gs = reinterpret_cast<T *>(r->gate_scal);
-  hipLaunchKernelGGL(route_topk_rank<T>, dim3((unsigned)nb), dim3(kRouteThreads), 0, s, logits,
-                     N, E, K, logG, vec, r->topk_idx, tw, r->bitmatrix, blk_cnt, blk_rank, fused,
-                     r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs);
-  if (!fused) {
-    hipLaunchKernelGGL(route_scatter<T>, dim3((unsigned)nb), dim3(kRouteThreads), 0, s, N, E, K,
-                       (int)nb, blk_cnt, blk_rank, r->topk_idx, tw, r->col_sum, r->offsets,
+  if (use_fused(N, E)) {
+    hipLaunchKernelGGL((route_fused<T, kFusedTokens, 1024>), dim3(1), dim3(1024), 0, s, logits,
+                       N, E, K, logG, vec, r->topk_idx, tw, r->bitmatrix, r->col_sum, r->offsets,
                        r->col_sorted, r->row_sorted, gs);
+    return hipGetLastError();
   }
+  const int64_t nb = (N + kRouteTokens - 1) / kRouteTokens;
+  int32_t *blk_cnt = reinterpret_cast<int32_t *>(scratch);
+  uint8_t *blk_rank = reinterpret_cast<uint8_t *>(scratch) + align256((size_t)nb * E * 4);
+  hipLaunchKernelGGL(route_topk_rank<T>, dim3((unsigned)nb), dim3(kTopkThreads), 0, s, logits, N,
+                     E, K, logG, vec, r->topk_idx, tw, r->bitmatrix, blk_cnt, blk_rank);
+  hipLaunchKernelGGL(route_scatter<T>, dim3((unsigned)nb), dim3(kRouteThreads), 0, s, N, E, K,
+                     (int)nb, blk_cnt, blk_rank, r->topk_idx, tw, r->col_sum, r->offsets,
+                     r->col_sorted, r->row_sorted, gs);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t route_scratch_bytes(int64_t n_tokens, int n_experts, int topk) {
+  if (use_fused(n_tokens, n_experts)) return 0;
   const int64_t nb = (n_tokens + kRouteTokens - 1) / kRouteTokens;
   return align256((size_t)nb * n_experts * 4) + align256((size_t)n_tokens * topk);
 }

@@ -85,8 +85,11 @@ def test_route_argument_checks(lib):
     assert route(lib, r=routing(w_dtype=N.MOE_F32)) == N.MOE_ERR_DTYPE  # weights inherit
     assert route(lib, logits=MISALIGNED) == N.MOE_ERR_ALIGN
     assert route(lib, r=routing({"gate_scal": MISALIGNED})) == N.MOE_ERR_ALIGN
-    assert route(lib, ws=None) == N.MOE_ERR_WORKSPACE
-    assert route(lib, wsb=16) == N.MOE_ERR_WORKSPACE
+    # small batches route inside one workgroup with no scratch, so the
+    # workspace checks use a batch that needs it
+    assert lib.moe_workspace_bytes(4096, 8, 2, 0, 0, N.MOE_BF16) > 16
+    assert route(lib, n=4096, ws=None) == N.MOE_ERR_WORKSPACE
+    assert route(lib, n=4096, wsb=16) == N.MOE_ERR_WORKSPACE
 
 
 def experts(lib, n=33, h=128, e=8, i=256, k=2, act=N.MOE_ACT_SILU, layout=N.MOE_W13_PACKED,
