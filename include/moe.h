@@ -44,6 +44,10 @@
  *  - n_tokens == 0 is valid: MOE_OK, nothing enqueued.
  *  - Limits: 1 <= n_experts <= 256, 1 <= topk <= min(n_experts, 16),
  *    n_tokens * topk < 2^31, hidden and inter positive multiples of 8.
+ *    moe_experts* and moe_forward also need each of these below 2^31 bytes:
+ *    one expert's w13 block (2 * inter * hidden elements), x (n_tokens *
+ *    hidden), the activation rows (n_tokens * topk * inter) and the sorted
+ *    expert outputs (n_tokens * topk * hidden).
  *  - Logits must be finite.  Ties between equal logits go to the lower expert
  *    index; -0.0 and +0.0 are equal.
  */

@@ -31,6 +31,7 @@
 //    2n + 1), so gate and up of one output land in the same lane and register
 //    of two accumulators and the activation runs in the epilogue from fp32.
 //  * bf16 uses v_mfma_f32_32x32x16_bf16, fp32 uses v_mfma_f32_32x32x2_f32.
+#include <cmath>
 #include <type_traits>
 
 #include "moe_common.h"
@@ -38,11 +39,13 @@
 namespace moe {
 namespace {
 
-constexpr int kRowBytes = 128;  // one K-slice row in LDS
 constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every num_records used here
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
 
-enum { EPI_ACT = 0, EPI_Y = 1, EPI_OUT = 2 };
+// Epilogue kinds: GEMM1 applies the activation (gated without or with the
+// clamp, or ReLU^2); GEMM2 scales by the routing weight and writes the sorted
+// row (EPI_Y) or, with one expert per token, the token's output row (EPI_OUT).
+enum { EPI_GATED = 0, EPI_Y = 1, EPI_OUT = 2, EPI_GATED_CLAMP = 3, EPI_RELU2 = 4 };
 
 struct GemmArgs {
   const void *A;                 // GEMM1: x [N, K]; GEMM2: a [M, K]
@@ -52,13 +55,13 @@ struct GemmArgs {
   const int32_t *col_sorted;     // [M]
   const void *gate_scal;         // [M] (GEMM2)
   uint32_t a_bytes;              // bytes of A (buffer range)
+  uint32_t c_bytes;              // bytes of C
   int gate_bf16, E, K, Nout, topk, gather, interleaved, act;
   ActParams prm;
 };
 
 template <typename T> struct Mma;
 template <> struct Mma<bf16_t> {
-  static constexpr int BK = 64;  // K elements per LDS slice
   static constexpr int KS = 16;  // K per instruction
   static constexpr int EPL = 8;  // K elements per lane fragment
   typedef bf16x8_t Frag;
@@ -68,7 +71,6 @@ template <> struct Mma<bf16_t> {
   }
 };
 template <> struct Mma<float> {
-  static constexpr int BK = 32;
   static constexpr int KS = 2;
   static constexpr int EPL = 1;
   typedef float Frag;
@@ -78,20 +80,28 @@ template <> struct Mma<float> {
   }
 };
 
-// LDS byte offset of (row, logical 16-byte chunk) after the XOR swizzle.  A
-// ds_read_b128 is served 16 lanes at a time from 64 four-byte banks (256
-// bytes), i.e. two 128-byte rows per bank line: rows of equal parity share
-// banks, so the XOR key is (row / 2) % 8 -- the 8 same-parity rows among any 16
-// consecutive rows then hit 8 distinct 16-byte slots.
-__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * kRowBytes + ((chunk ^ swz_key(row)) << 4);
+// LDS rows are RB bytes (one K-slice of one operand row).  A ds_read_b128 is
+// served 16 lanes at a time from 64 four-byte banks (256 bytes), i.e. from
+// 256 / RB rows at once, and the 16 lanes of a fragment read hit 16
+// consecutive rows at the same logical chunk.  XOR-ing the chunk index with
+// (row / (256 / RB)) % (RB / 16) spreads those 16 reads over all 16 bank
+// groups: row % (256 / RB) picks the group's row in the bank line and the key
+// the chunk.
+template <int RB> __device__ __forceinline__ int swz_key(int row) {
+  return (row / (256 / RB)) % (RB / 16);
+}
+template <int RB> __device__ __forceinline__ int swz(int row, int chunk) {
+  return row * RB + ((chunk ^ swz_key<RB>(row)) << 4);
 }
 
+// Workgroup barrier that also stops the scheduler from moving any instruction
+// (MFMAs included) across it, so phases stay where the code puts them.
 __device__ __forceinline__ void barrier() {
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and 15:14,
@@ -101,11 +111,28 @@ template <int N> __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
+// Wait until at most P * PER + (st ? NST : 0) vector-memory operations are
+// outstanding, for the largest P <= pend (pend <= PMAX).  PER is the number of
+// load instructions per slice and NST the number of stores one epilogue
+// issues; vmcnt counts loads and stores together and retires them in order.
+template <int PER, int NST, int P>
+__device__ __forceinline__ void wait_pending(int pend, bool st) {
+  if constexpr (P == 0) {
+    if (st) wait_vm<NST>(); else wait_vm<0>();
+  } else {
+    if (pend >= P) {
+      if (st) wait_vm<P * PER + NST>(); else wait_vm<P * PER>();
+    } else {
+      wait_pending<PER, NST, P - 1>(pend, st);
+    }
+  }
+}
+
 // 16 bytes per lane from buffer `r` at byte offset `voff` into LDS at
 // lds + 16 * lane (lds must be the same for the whole wave).  Issued as inline
 // asm so the compiler does not track the LDS write: left to itself it waits for
 // every outstanding load before any LDS read, which would serialise the ring.
-// The waits for these loads are the explicit wait_vm<> calls.
+// The waits for these loads are the explicit wait_pending<> calls.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char *lds, uint32_t voff) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(void __attribute__((address_space(3))) *)lds;
   asm volatile(
@@ -116,14 +143,41 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char *lds, uint3
       : "memory", "m0");
 }
 
-__device__ __forceinline__ float act_fn(int act, float g, float u, const ActParams &p) {
-  if (act == MOE_ACT_RELU2) {
+// Activation of one (gate, up) pair.  Gated kinds evaluate the logistic
+// function as 1 / (1 + 2^(nal * g)) with nal = -alpha * log2(e), using the
+// hardware exp2 and reciprocal (about 1 ulp each); the clamp variant first
+// limits the gate from above and the up value to [-limit, limit].
+template <int EPI>
+__device__ __forceinline__ float act_val(float g, float u, float nal, const ActParams &p) {
+  if constexpr (EPI == EPI_RELU2) {
     const float r = fmaxf(g, 0.f);
     return r * r;
+  } else {
+    if constexpr (EPI == EPI_GATED_CLAMP) {
+      g = fminf(g, p.limit);
+      u = fminf(fmaxf(u, -p.limit), p.limit);
+    }
+    const float e = __builtin_amdgcn_exp2f(nal * g);
+    return g * __builtin_amdgcn_rcpf(1.f + e) * (u + p.beta);
   }
-  const float gc = fminf(g, p.limit);
-  const float uc = fminf(fmaxf(u, -p.limit), p.limit);
-  return gc * (1.f / (1.f + expf(-p.alpha * gc))) * (uc + p.beta);
+}
+
+// Four consecutive output elements of one row.
+typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t off, const float (&v)[4],
+                                       bf16_t) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  // v_cvt_pk_bf16_f32: round to nearest even, as bf16_rne
+  const bf16x4_t b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2_t, b), r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, uint32_t off, const float (&v)[4],
+                                       float) {
+  i32x4_t d;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) d[t] = __float_as_int(v[t]);
+  __builtin_amdgcn_raw_buffer_store_b128(d, r, (int)off, 0, 0);
 }
 
 // Where tile L of the expert-major tile order lives: expert e, output-column
@@ -139,8 +193,8 @@ struct TileInfo {
 };
 
 template <int BM, int BN>
-__device__ __forceinline__ TileInfo tile_info(int L, const int *s_ts, const int32_t *offsets,
-                                              int E, int n_nt) {
+__device__ __forceinline__ TileInfo tile_info(int L, const int *s_ts, const int *s_off, int E,
+                                              int n_nt) {
   const int q = L / n_nt;  // s_ts[e] <= q < s_ts[e + 1] exactly when L is in expert e
   int lo = 0, hi = E - 1;
   while (lo < hi) {
@@ -159,13 +213,14 @@ __device__ __forceinline__ TileInfo tile_info(int L, const int *s_ts, const int3
   const int nt = nb * GN + r2 / gm;
   TileInfo ti;
   ti.e = lo;
-  ti.row0 = offsets[lo] + mt * BM;
-  ti.rows = min(BM, offsets[lo + 1] - ti.row0);
+  ti.row0 = s_off[lo] + mt * BM;
+  ti.rows = min(BM, s_off[lo + 1] - ti.row0);
   ti.n0 = nt * BN;
   return ti;
 }
 
-// Tile of BM rows x BN output columns; WM x WN waves; S-stage LDS ring.
+// Tile of BM rows x BN output columns; WM x WN waves; S-stage LDS ring of
+// RB-byte K-slices.
 //
 // Work split: tiles are ordered expert by expert (within an expert n-tile-
 // major, m-tile fastest) and cut into 8 contiguous chunks, one per XCD; the
@@ -175,24 +230,57 @@ __device__ __forceinline__ TileInfo tile_info(int L, const int *s_ts, const int3
 // same rows.  A workgroup's tiles form one stream of K-slices: the ring keeps
 // loading S - 1 slices ahead across tile boundaries, so a tile's epilogue runs
 // while the next tile's first slices are in flight.
-template <typename T, int NSETS, int EPI, int BM, int BN, int WM, int WN, int S>
+//
+// Eight-wave tiles run a ping-pong schedule: waves 0-3 and 4-7 (one of each
+// on every SIMD) alternate between a memory phase -- issue this wave's share
+// of a future slice, read all fragments of the current slice into registers
+// -- and an MFMA phase on those registers, one group a barrier behind the
+// other, so each SIMD's matrix core is fed by one wave while the other waits
+// on LDS and HBM.  Four-wave tiles keep one phase per slice and overlap the
+// fragment reads of k-step ks + 1 with the MFMAs of k-step ks.
+//
+// The MFMA takes the weight fragment as its first operand, so the 32 x 32
+// accumulator comes out transposed: lane l holds sorted row (l % 32) of the
+// sub-tile and each group of four registers four consecutive output columns.
+// The epilogue then writes 8-byte (bf16) or 16-byte (fp32) pieces of a row,
+// and needs one output-row index and one routing weight per lane.
+template <typename T, int NSETS, int EPI, int BM, int BN, int WM, int WN, int S, int RB>
 __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
   using Mm = Mma<T>;
   using Frag = typename Mm::Frag;
-  constexpr int BK = Mm::BK;
+  constexpr int BK = RB / (int)sizeof(T);  // K elements per slice
+  constexpr int NKS = BK / Mm::KS;         // MFMA k-steps per slice
+  constexpr int CPR = RB / 16;             // 16-byte chunks per LDS row
+  constexpr int RPI = 1024 / RB;           // rows per 1 KB load instruction
   constexpr int NW = WM * WN;
-  constexpr int NB = NSETS * BN;          // B rows per tile
-  constexpr int JA = BM / 8 / NW;         // 1 KB A loads per wave per slice
-  constexpr int JB = NB / 8 / NW;
-  constexpr int TM = BM / WM / 32;        // 32x32 sub-tiles per wave
+  constexpr int NB = NSETS * BN;           // B rows per tile
+  constexpr int JA = BM / RPI / NW;        // load instructions per wave per slice
+  constexpr int JB = NB / RPI / NW;
+  constexpr int TM = BM / WM / 32;         // 32x32 sub-tiles per wave
   constexpr int TN = BN / WN / 32;
-  constexpr int STAGE = (BM + NB) * kRowBytes;
-  static_assert(JA * 8 * NW == BM && JB * 8 * NW == NB, "tile rows vs waves");
+  constexpr int STAGE = (BM + NB) * RB;
+  constexpr int NST = TM * TN * 4;         // stores per wave per epilogue
+  constexpr bool META = EPI == EPI_Y || EPI == EPI_OUT;
+  constexpr bool PP = NW == 8;             // ping-pong schedule
+  // a tile's metadata is written when its first slice is issued (S - 1
+  // slices ahead) and read by its epilogue; NSL slots keep the epilogue of
+  // tile i clear of the set-up of tile i + NSL
+  constexpr int NSL = S + 1;
+  static_assert(RB == 64 || RB == 128, "row bytes");
+  static_assert(JA >= 1 && JB >= 1 && JA * RPI * NW == BM && JB * RPI * NW == NB,
+                "tile rows vs waves");
   static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "wave tiles");
-  static_assert(S >= 2 && S <= 4 && (S - 2) * (JA + JB) < 64, "stages / vmcnt range");
+  static_assert(BK % Mm::KS == 0, "slice vs instruction K");
+  static_assert(S >= 2 && (S - 2) * (JA + JB) + NST < 64, "stages / vmcnt range");
+  static_assert((EPI == EPI_RELU2 || EPI == EPI_Y || EPI == EPI_OUT) == (NSETS == 1),
+                "gated epilogues take two weight sets");
 
   __shared__ __attribute__((aligned(16))) char smem[S * STAGE];
-  __shared__ int s_ts[kMaxExperts + 1];
+  __shared__ int s_ts[kMaxExperts + 1];   // first m-tile of each expert
+  __shared__ int s_off[kMaxExperts + 1];  // the routing offsets
+  __shared__ TileInfo s_tile[NSL];        // per slot: the tile
+  // per slot: output row and routing weight of each tile row
+  __shared__ i32x2_t s_meta[META ? NSL : 1][META ? BM : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps LDS bases scalar
@@ -204,7 +292,10 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = lane * 4 + q;
-      v[q] = (e < E) ? (g.offsets[e + 1] - g.offsets[e] + BM - 1) / BM : 0;
+      const int o0 = e < E ? g.offsets[e] : 0;
+      const int o1 = e < E ? g.offsets[e + 1] : 0;
+      if (e < E) s_off[e] = o0;
+      v[q] = (e < E) ? (o1 - o0 + BM - 1) / BM : 0;
       s += v[q];
     }
     int incl = s;
@@ -220,7 +311,10 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
       if (e < E) s_ts[e] = run;
       run += v[q];
     }
-    if (lane == 63) s_ts[E] = incl;
+    if (lane == 63) {
+      s_ts[E] = incl;
+      s_off[E] = g.offsets[E];
+    }
   }
   __syncthreads();
 
@@ -236,159 +330,234 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
 
   const int kbytes = K * (int)sizeof(T);
   const int nk = (K + BK - 1) / BK;
-  const int nz = my_tiles * nk;  // K-slices in this workgroup's stream
-  const int lrow = lane >> 3;  // row within a 1 KB load; the lane fills physical chunk lane % 8
+  const int nz = my_tiles * nk;  // K-slices in this workgroup's stream (uniform)
+  if (nz == 0) return;
+  const int lrow = lane / CPR;   // row within a 1 KB load; the lane fills physical chunk lane % CPR
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void *>(g.A), (short)0, (int)g.a_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rc =
+      __builtin_amdgcn_make_buffer_rsrc(g.C, (short)0, (int)g.c_bytes, kRsrcWord3);
   const uint32_t w_bytes = (uint32_t)NSETS * Nout * kbytes;
   const int wm = wave % WM, wn = wave / WM;
+  const float nal = -g.prm.alpha * 1.44269504088896341f;
 
   // issue side: the tile whose slices are being loaded
   uint32_t va[JA], vb[JB];
   __amdgpu_buffer_rsrc_t rb = ra;
   auto setup_issue = [&](int i) {
-    const TileInfo ti = tile_info<BM, BN>(first + i * gx, s_ts, g.offsets, E, n_nt);
+    const TileInfo ti = tile_info<BM, BN>(first + i * gx, s_ts, s_off, E, n_nt);
+    if (tid == 0) s_tile[i % NSL] = ti;
     rb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char *>(reinterpret_cast<const char *>(g.W)) + (size_t)ti.e * w_bytes,
         (short)0, (int)w_bytes, kRsrcWord3);
 #pragma unroll
-    for (int j = 0; j < JA; ++j) {
-      const int r = (wave * JA + j) * 8 + lrow;
-      va[j] = kOOB;
-      if (r < ti.rows) {
-        const int p = ti.row0 + r;
-        const uint32_t arow = g.gather ? (uint32_t)(g.col_sorted[p] / g.topk) : (uint32_t)p;
-        va[j] = arow * (uint32_t)kbytes + (((lane & 7) ^ swz_key(r)) << 4);
-      }
-    }
-#pragma unroll
     for (int j = 0; j < JB; ++j) {
-      const int r = (wave * JB + j) * 8 + lrow;
+      const int r = (wave * JB + j) * RPI + lrow;
       const int set = r / BN, n = ti.n0 + r % BN;
       vb[j] = kOOB;
       if (n < Nout) {
         const int grow = NSETS == 1 ? n : (g.interleaved ? 2 * n + set : set * Nout + n);
-        vb[j] = (uint32_t)grow * (uint32_t)kbytes + (((lane & 7) ^ swz_key(r)) << 4);
+        vb[j] = (uint32_t)grow * (uint32_t)kbytes + (((lane % CPR) ^ swz_key<RB>(r)) << 4);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < JA; ++j) {
+      const int r = (wave * JA + j) * RPI + lrow;
+      va[j] = kOOB;
+      if (r < ti.rows) {
+        const int p = ti.row0 + r;
+        const uint32_t arow = g.gather ? (uint32_t)(g.col_sorted[p] / g.topk) : (uint32_t)p;
+        va[j] = arow * (uint32_t)kbytes + (((lane % CPR) ^ swz_key<RB>(r)) << 4);
+        if (META && lane % CPR == 0) {
+          const float gs = g.gate_bf16 ? to_f32(reinterpret_cast<const bf16_t *>(g.gate_scal)[p])
+                                       : reinterpret_cast<const float *>(g.gate_scal)[p];
+          i32x2_t m;
+          m[0] = EPI == EPI_OUT ? g.col_sorted[p] : p;  // topk == 1: entry index == token
+          m[1] = __float_as_int(gs);
+          s_meta[i % NSL][r] = m;
+        }
       }
     }
   };
   auto issue = [&](int z) {  // load slice z of the stream into ring slot z % S
     const int i = z / nk, kt = z - i * nk;
     if (kt == 0) setup_issue(i);
-    const uint32_t kb = (uint32_t)kt * kRowBytes;
+    const uint32_t kb = (uint32_t)kt * RB;
     char *base = smem + (z % S) * STAGE;
     // kOOB + kb stays out of range, so invalid rows / columns need no test;
-    // only a K-tail slice (kb + 128 > row bytes) masks chunks past K.  Rows
+    // only a K-tail slice (kb + RB > row bytes) masks chunks past K.  Rows
     // are K * sizeof(T) bytes, a multiple of 16, so the tail is chunk-aligned.
-    if ((int)kb + kRowBytes <= kbytes) {
-#pragma unroll
-      for (int j = 0; j < JA; ++j) dma16(ra, base + (wave * JA + j) * 1024, va[j] + kb);
+    if ((int)kb + RB <= kbytes) {
 #pragma unroll
       for (int j = 0; j < JB; ++j)
-        dma16(rb, base + BM * kRowBytes + (wave * JB + j) * 1024, vb[j] + kb);
+        dma16(rb, base + BM * RB + (wave * JB + j) * 1024, vb[j] + kb);
+#pragma unroll
+      for (int j = 0; j < JA; ++j) dma16(ra, base + (wave * JA + j) * 1024, va[j] + kb);
     } else {
 #pragma unroll
-      for (int j = 0; j < JA; ++j) {
-        const int coff = ((lane & 7) ^ swz_key((wave * JA + j) * 8 + lrow)) << 4;
-        dma16(ra, base + (wave * JA + j) * 1024, (int)kb + coff < kbytes ? va[j] + kb : kOOB);
-      }
-#pragma unroll
       for (int j = 0; j < JB; ++j) {
-        const int coff = ((lane & 7) ^ swz_key((wave * JB + j) * 8 + lrow)) << 4;
-        dma16(rb, base + BM * kRowBytes + (wave * JB + j) * 1024,
+        const int coff = ((lane % CPR) ^ swz_key<RB>((wave * JB + j) * RPI + lrow)) << 4;
+        dma16(rb, base + BM * RB + (wave * JB + j) * 1024,
               (int)kb + coff < kbytes ? vb[j] + kb : kOOB);
       }
+#pragma unroll
+      for (int j = 0; j < JA; ++j) {
+        const int coff = ((lane % CPR) ^ swz_key<RB>((wave * JA + j) * RPI + lrow)) << 4;
+        dma16(ra, base + (wave * JA + j) * 1024, (int)kb + coff < kbytes ? va[j] + kb : kOOB);
+      }
     }
+  };
+
+  f32x16_t acc[TM][TN][NSETS];
+  int st_until = -1;  // last slice whose wait must also cover the latest epilogue's stores
+
+  // Slice w is in LDS as far as this wave's loads go: at most the loads of
+  // the slices issued after w (this wave has issued up to min(w + S - 2,
+  // nz - 1)) may remain, plus an epilogue's stores if they were issued after
+  // slice w's loads (an epilogue at slice z0 follows the loads of slices up to
+  // z0 + S - 1).  Waits on ds operations too.
+  auto wait_slice = [&](int w) {
+    wait_pending<JA + JB, NST, S - 2>(min(S - 2, nz - 1 - w), w <= st_until);
+  };
+  auto frag_addr = [&](int ks, int row) {  // byte in a slice of k-step ks, operand row
+    const int byte = (ks * Mm::KS + (lane >> 5) * Mm::EPL) * (int)sizeof(T);
+    return swz<RB>(row, byte >> 4) + (byte & 15);
+  };
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int s = 0; s < NSETS; ++s)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][s][r] = 0.f;
+  };
+
+  // ---- epilogue: lane holds row (lane % 32) and, in register group q, the
+  // four columns 8q + 4 * (lane / 32) + [0, 4) of each 32 x 32 sub-tile ------
+  auto epilogue = [&](int z) {
+    const int ti_i = z / nk;
+    const TileInfo ti = s_tile[ti_i % NSL];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int row = wm * (BM / WM) + i * 32 + (lane & 31);
+      const bool ok = row < ti.rows;
+      uint32_t orow = (uint32_t)(ti.row0 + row);
+      float gs = 1.f;
+      if (META) {
+        const i32x2_t m = s_meta[ti_i % NSL][row];
+        orow = (uint32_t)m[0];
+        gs = __int_as_float(m[1]);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = ti.n0 + wn * (BN / WN) + j * 32 + 8 * q + 4 * (lane >> 5);
+          float v[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            if constexpr (META)
+              v[t] = acc[i][j][0][4 * q + t] * gs;
+            else
+              v[t] = act_val<EPI>(acc[i][j][0][4 * q + t], acc[i][j][NSETS - 1][4 * q + t], nal,
+                                  g.prm);
+          }
+          // Nout is a multiple of 8, so col < Nout covers all four columns
+          const uint32_t off = (ok && col < Nout)
+                                   ? (orow * (uint32_t)Nout + (uint32_t)col) * (uint32_t)sizeof(T)
+                                   : kOOB;
+          store4(rc, off, v, T());
+        }
+      }
+    }
+    st_until = z + S - 1;
   };
 
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
     if (s < nz) issue(s);
 
-  f32x16_t acc[TM][TN][NSETS];
-  T *C = reinterpret_cast<T *>(g.C);
-  for (int z = 0; z < nz; ++z) {
-    // slices issued after z that may still be in flight: min(S - 2, nz - 1 - z)
-    const int pend = min(S - 2, nz - 1 - z);
-    if (pend >= 2) wait_vm<(S >= 4 ? 2 * (JA + JB) : 0)>();
-    else if (pend == 1) wait_vm<(S >= 3 ? JA + JB : 0)>();
-    else wait_vm<0>();
+  if constexpr (PP) {
+    const int grp = wave >> 2;
+    Frag fa[NKS][TM], fb[NKS][TN][NSETS];
+    wait_slice(0);
     barrier();
-    if (z + S - 1 < nz) issue(z + S - 1);
-    const int kt = z % nk;
-    if (kt == 0) {
+    if (grp) barrier();  // group 1 runs one phase behind group 0
+    for (int z = 0; z < nz; ++z) {
+      // memory phase: next loads out, this slice's fragments in
+      if (z + S - 1 < nz) issue(z + S - 1);
+      const char *la = smem + (z % S) * STAGE;
+      const char *lb = la + BM * RB;
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int s = 0; s < NSETS; ++s)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][s][r] = 0.f;
-    }
-    const char *la = smem + (z % S) * STAGE;
-    const char *lb = la + BM * kRowBytes;
-    // fragments of k-step ks + 1 are read while the MFMAs of k-step ks run
-    constexpr int NKS = BK / Mm::KS;
-    Frag fa[2][TM], fb[2][TN][NSETS];
-    auto load_frags = [&](int buf, int ks) {
-      const int byte = (ks * Mm::KS + (lane >> 5) * Mm::EPL) * (int)sizeof(T);
-      const int ch = byte >> 4, inner = byte & 15;
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int row = wm * (BM / WM) + i * 32 + (lane & 31);
-        fa[buf][i] = Mm::ld(la + swz(row, ch) + inner);
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int s = 0; s < NSETS; ++s) {
-          const int row = s * BN + wn * (BN / WN) + j * 32 + (lane & 31);
-          fb[buf][j][s] = Mm::ld(lb + swz(row, ch) + inner);
-        }
-    };
-    load_frags(0, 0);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      if (ks + 1 < NKS) load_frags((ks + 1) & 1, ks + 1);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
+          fa[ks][i] = Mm::ld(la + frag_addr(ks, wm * (BM / WM) + i * 32 + (lane & 31)));
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
           for (int s = 0; s < NSETS; ++s)
-            acc[i][j][s] = Mm::mma(fa[ks & 1][i], fb[ks & 1][j][s], acc[i][j][s]);
-    }
-    if (kt != nk - 1) continue;
-
-    // ---- epilogue: lane holds column (lane % 32), 16 rows of each 32x32 ------
-    const TileInfo ti = tile_info<BM, BN>(first + (z / nk) * gx, s_ts, g.offsets, E, n_nt);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * (BM / WM) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row >= ti.rows) continue;
-        const int p = ti.row0 + row;
-        float gs = 1.f;
-        int64_t orow = p;
-        if (EPI != EPI_ACT) {
-          gs = g.gate_bf16 ? to_f32(reinterpret_cast<const bf16_t *>(g.gate_scal)[p])
-                           : reinterpret_cast<const float *>(g.gate_scal)[p];
-          if (EPI == EPI_OUT) orow = g.col_sorted[p];  // topk == 1: entry index == token
-        }
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int col = ti.n0 + wn * (BN / WN) + j * 32 + (lane & 31);
-          if (col >= Nout) continue;
-          float v;
-          if (EPI == EPI_ACT)
-            v = act_fn(g.act, acc[i][j][0][r], NSETS == 2 ? acc[i][j][NSETS - 1][r] : 0.f, g.prm);
-          else
-            v = acc[i][j][0][r] * gs;
-          C[orow * Nout + col] = from_f32<T>(v);
-        }
+            fb[ks][j][s] =
+                Mm::ld(lb + frag_addr(ks, s * BN + wn * (BN / WN) + j * 32 + (lane & 31)));
       }
+      if (grp && z + 1 < nz) wait_slice(z + 1);
+      barrier();
+      // MFMA phase
+      __builtin_amdgcn_s_setprio(1);
+      const int kt = z % nk;
+      if (kt == 0) zero_acc();
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int s = 0; s < NSETS; ++s)
+              acc[i][j][s] = Mm::mma(fb[ks][j][s], fa[ks][i], acc[i][j][s]);
+      __builtin_amdgcn_s_setprio(0);
+      if (kt == nk - 1) epilogue(z);
+      if (!grp && z + 1 < nz) wait_slice(z + 1);
+      barrier();
+    }
+    if (!grp) barrier();
+  } else {
+    for (int z = 0; z < nz; ++z) {
+      wait_slice(z);
+      barrier();
+      if (z + S - 1 < nz) issue(z + S - 1);
+      const int kt = z % nk;
+      if (kt == 0) zero_acc();
+      const char *la = smem + (z % S) * STAGE;
+      const char *lb = la + BM * RB;
+      // fragments of k-step ks + 1 are read while the MFMAs of k-step ks run
+      Frag fa[2][TM], fb[2][TN][NSETS];
+      auto load_frags = [&](int buf, int ks) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          fa[buf][i] = Mm::ld(la + frag_addr(ks, wm * (BM / WM) + i * 32 + (lane & 31)));
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int s = 0; s < NSETS; ++s)
+            fb[buf][j][s] =
+                Mm::ld(lb + frag_addr(ks, s * BN + wn * (BN / WN) + j * 32 + (lane & 31)));
+      };
+      load_frags(0, 0);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (ks + 1 < NKS) load_frags((ks + 1) & 1, ks + 1);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int s = 0; s < NSETS; ++s)
+              acc[i][j][s] = Mm::mma(fb[ks & 1][j][s], fa[ks & 1][i], acc[i][j][s]);
+      }
+      if (kt == nk - 1) epilogue(z);
     }
   }
 }
@@ -402,20 +571,21 @@ int device_cus() {
   return cus;
 }
 
-template <int BM_, int BN_, int WM_, int WN_, int S_> struct Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_;
+template <int BM_, int BN_, int WM_, int WN_, int S_, int RB_> struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_, RB = RB_;
 };
 // Tile configurations, largest first (rows x output columns, waves rows x
-// columns, ring stages).  Gated tiles carry 2 * BN weight rows.
-using GatedL = Cfg<256, 128, 4, 2, 2>;  // 8 waves, 64 x (64 + 64) each
-using GatedM = Cfg<128, 128, 2, 4, 3>;  // 8 waves, 64 x (32 + 32) each
-using GatedS = Cfg<32, 128, 1, 4, 4>;   // 4 waves, 32 x (32 + 32) each
-using PlainL = Cfg<256, 256, 4, 2, 2>;  // 8 waves, 64 x 128 each
-using PlainM = Cfg<128, 128, 2, 2, 3>;  // 4 waves, 64 x 64 each
-using PlainS = Cfg<32, 128, 1, 4, 4>;   // 4 waves, 32 x 32 each
+// columns, ring stages, LDS row bytes).  Gated tiles carry 2 * BN weight rows.
+using GatedL = Cfg<256, 128, 4, 2, 4, 64>;  // 8 waves, 64 x (64 + 64) each
+using GatedM = Cfg<128, 128, 2, 4, 3, 128>; // 8 waves, 64 x (32 + 32) each
+using GatedS = Cfg<32, 128, 1, 4, 4, 128>;  // 4 waves, 32 x (32 + 32) each
+using PlainL = Cfg<256, 256, 4, 2, 4, 64>;  // 8 waves, 64 x 128 each
+using PlainM = Cfg<128, 128, 2, 2, 3, 128>; // 4 waves, 64 x 64 each
+using PlainS = Cfg<32, 128, 1, 4, 4, 128>;  // 4 waves, 32 x 32 each
 
 template <typename C, int NSETS> constexpr int lds_bytes() {
-  return C::S * (C::BM + NSETS * C::BN) * kRowBytes + (kMaxExperts + 1) * 4;
+  return C::S * (C::BM + NSETS * C::BN) * C::RB + 2 * (kMaxExperts + 1) * 4 +
+         (C::S + 1) * (16 + C::BM * 8);
 }
 
 // Upper bound on the tiles of one launch: floor(M / BM) + min(E, M) m-tiles.
@@ -431,7 +601,8 @@ hipError_t launch_cfg(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
   int64_t grid = (int64_t)device_cus() * (per_cu < 2 ? per_cu : 2);
   if (grid > tiles) grid = tiles;
   grid = (grid + 7) / 8 * 8;  // whole XCD rounds; surplus workgroups get no tiles
-  hipLaunchKernelGGL((grouped_gemm<T, NSETS, EPI, C::BM, C::BN, C::WM, C::WN, C::S>),
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+  hipLaunchKernelGGL((grouped_gemm<T, NSETS, EPI, C::BM, C::BN, C::WM, C::WN, C::S, C::RB>),
                      dim3((unsigned)grid), dim3(64 * C::WM * C::WN), 0, s, a);
   return hipGetLastError();
 }
@@ -460,13 +631,17 @@ hipError_t launch_gemm1(const void *x, const void *w13, void *act_out, const int
   const int64_t M = n_tokens * topk;
   const size_t es = dt == MOE_BF16 ? 2 : 4;
   GemmArgs a{x, w13, act_out, offsets, col_sorted, nullptr, (uint32_t)(n_tokens * hidden * es),
-             0, n_experts, hidden, inter, topk, 1, layout == MOE_W13_INTERLEAVED, act, p};
+             (uint32_t)(M * inter * es), 0, n_experts, hidden, inter, topk, 1,
+             layout == MOE_W13_INTERLEAVED, act, p};
   const bool gated = act != MOE_ACT_RELU2;
+  const bool clamp = std::isfinite(p.limit);  // an infinite limit clamps nothing
   if (dt == MOE_BF16)
-    return gated ? launch_t<bf16_t, 2, EPI_ACT>(a, M, n_experts, s)
-                 : launch_t<bf16_t, 1, EPI_ACT>(a, M, n_experts, s);
-  return gated ? launch_t<float, 2, EPI_ACT>(a, M, n_experts, s)
-               : launch_t<float, 1, EPI_ACT>(a, M, n_experts, s);
+    return !gated  ? launch_t<bf16_t, 1, EPI_RELU2>(a, M, n_experts, s)
+           : clamp ? launch_t<bf16_t, 2, EPI_GATED_CLAMP>(a, M, n_experts, s)
+                   : launch_t<bf16_t, 2, EPI_GATED>(a, M, n_experts, s);
+  return !gated  ? launch_t<float, 1, EPI_RELU2>(a, M, n_experts, s)
+         : clamp ? launch_t<float, 2, EPI_GATED_CLAMP>(a, M, n_experts, s)
+                 : launch_t<float, 2, EPI_GATED>(a, M, n_experts, s);
 }
 
 hipError_t launch_gemm2(const void *act_in, const void *w2, void *y, const int32_t *offsets,
@@ -475,9 +650,10 @@ hipError_t launch_gemm2(const void *act_in, const void *w2, void *y, const int32
                         int inter, bool direct_out, hipStream_t s) {
   const int64_t M = n_tokens * topk;
   const size_t es = dt == MOE_BF16 ? 2 : 4;
+  const int64_t c_rows = direct_out ? n_tokens : M;
   GemmArgs a{act_in, w2, y, offsets, col_sorted, gate_scal, (uint32_t)(M * inter * es),
-             gate_dt == MOE_BF16, n_experts, inter, hidden, topk, 0, 0, 0,
-             ActParams{1.f, 0.f, 0.f}};
+             (uint32_t)(c_rows * hidden * es), gate_dt == MOE_BF16, n_experts, inter, hidden,
+             topk, 0, 0, 0, ActParams{1.f, 0.f, 0.f}};
   if (dt == MOE_BF16)
     return direct_out ? launch_t<bf16_t, 1, EPI_OUT>(a, M, n_experts, s)
                       : launch_t<bf16_t, 1, EPI_Y>(a, M, n_experts, s);

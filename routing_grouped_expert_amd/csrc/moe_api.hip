@@ -94,7 +94,7 @@ moe_status_t check_expert_args(moe_dtype_t dtype, int64_t n, int32_t hidden, int
   // with 32-bit byte offsets
   const int64_t lim = 0x7fffffff, es = (int64_t)dsize(dtype);
   if ((int64_t)2 * inter * hidden * es > lim || n * hidden * es > lim ||
-      n * k * (int64_t)inter * es > lim)
+      n * k * (int64_t)inter * es > lim || n * k * (int64_t)hidden * es > lim)
     return MOE_ERR_SHAPE;
   if ((st = act_params(act, layout, params, prm)) != MOE_OK) return st;
   return check_routing_struct(routing, false, n);

@@ -107,6 +107,8 @@ def test_experts_argument_checks(lib):
     assert experts(lib, h=100) == N.MOE_ERR_SHAPE
     assert experts(lib, i=0) == N.MOE_ERR_SHAPE
     assert experts(lib, k=3, e=2) == N.MOE_ERR_SHAPE
+    # sorted expert outputs n * k * hidden * 2 bytes = 2^32: over the 2^31 limit
+    assert experts(lib, n=1 << 19, h=1024, i=8, k=4) == N.MOE_ERR_SHAPE
     assert experts(lib, dt=9) == N.MOE_ERR_DTYPE
     assert experts(lib, act=7) == N.MOE_ERR_UNSUPPORTED
     assert experts(lib, layout=2) == N.MOE_ERR_UNSUPPORTED
