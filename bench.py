@@ -3,11 +3,18 @@
     python bench.py [--steps K] [--warmup W] [--workload NAME]
 
 One step is one pass of the whole layer over one batch of seeded synthetic
-inputs already resident in HBM: moe_route (top-k, softmax, bitmatrix,
-histogram, offsets, sorted indices), moe_experts_w13 (grouped GEMM + activation)
-and moe_experts_w2 (grouped GEMM + routing weight + combine), back to back on
-one stream.  HIP events between the three calls give per-stage device times;
-events around the K steps give the step time.  Rank 0 prints one JSON line.
+inputs already resident in HBM: one moe_forward call through the C ABI, which
+enqueues the routing kernels (top-k, softmax, bitmatrix, histogram, offsets,
+sorted indices), the w13 grouped GEMM with the activation and the w2 grouped
+GEMM with the routing weight and the combine.  W untimed steps, then K steps
+between two HIP events on the launch stream give the step time.
+
+Per-stage device times come from separate timed regions on the same stream:
+K back-to-back launches of each stage (moe_route, moe_experts_w13,
+moe_experts_w2) between two events, so a stage's average includes the short
+dispatch gap between back-to-back launches of its kernels.  The w13 average
+is the dominant kernel's launch duration used for the roofline line.
+Rank 0 prints one JSON line.
 
 The default workload is the small-model layer (8 x 512 tokens, hidden 512,
 intermediate 1408, top-1, 8 experts, SiLU-gated, bf16).  ``--workload`` picks
@@ -28,8 +35,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from routing_grouped_expert_amd import (Routing, moe_workspace_bytes, prepare_experts_w13,  # noqa: E402
-                                        prepare_experts_w2, prepare_route)
-from routing_grouped_expert_amd.synth import act_params, layer_spec, make_layer  # noqa: E402
+                                        prepare_experts_w2, prepare_forward, prepare_route)
+from routing_grouped_expert_amd.synth import (act_params, layer_spec, make_layer,  # noqa: E402
+                                              routing_logits)
 
 METRIC = "MoE layer tokens/s + routing µs/layer; % MFMA bf16 peak and % HBM BW"
 PEAK_HBM_GBS = 8000.0
@@ -112,6 +120,125 @@ def cpu_baseline(spec, layer, budget_s: float):
                       f"routing + masked per-expert FFN loop), {reps} passes in {dt:.1f} s"}
 
 
+def stored_traffic(workload_name: str, stage: str):
+    """HBM bytes per launch of a stage's kernel from the committed rocprofv3
+    counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter
+    reads for a copy kernel of known size), or None when there is none or when
+    the kernel source has changed since the counters were taken."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "gemm_counters.md")
+    src = os.path.join(ROOT, "routing_grouped_expert_amd", "csrc", "grouped_gemm.hip")
+    try:
+        text = open(path).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    except OSError:
+        return None
+    for m in re.finditer(r"traffic: workload=(\S+) stage=(\S+) src_sha256=(\S+) "
+                         r"fetch_bytes=(\d+) write_bytes=(\d+)", text):
+        if m.group(1) == workload_name and m.group(2) == stage and m.group(3) == sha:
+            return int(m.group(4)) + int(m.group(5))
+    return None
+
+
+def step_stats(fn, steps: int, stream) -> dict:
+    """Mean, and median / p10 / p90 over batches, of back-to-back step times."""
+    # batches: the largest divisor of steps up to 20 that leaves >= 5 steps each,
+    # so exactly `steps` steps are timed
+    nb = max([d for d in range(1, 21) if steps % d == 0 and steps // d >= 5] or [1])
+    per = steps // nb
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(nb + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for bi in range(nb):
+        for _ in range(per):
+            fn()
+        ev[bi + 1].record(stream)
+    torch.cuda.synchronize()
+    batch = sorted(ev[bi].elapsed_time(ev[bi + 1]) / per for bi in range(nb))
+    q = lambda f: batch[min(nb - 1, int(f * nb))]
+    return {"mean": ev[0].elapsed_time(ev[nb]) / (nb * per), "p10": q(0.1), "p50": q(0.5),
+            "p90": q(0.9), "steps": nb * per}
+
+
+def cold_stats(fns, reps: int, stream, dev) -> list:
+    """Median time of each fn() run alone after a 512 MB write (more than the
+    256 MB Infinity Cache and the L2s), outside the timed window."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    out = []
+    for fn in fns:
+        ts = []
+        for _ in range(reps):
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        ts.sort()
+        out.append(ts[len(ts) // 2])
+    del flush
+    return out
+
+
+def bench_route_only(args, name: str):
+    """Routing-metadata workloads: route_n<N>_e<E>_k<k> (bf16 logits)."""
+    import re
+    m = re.fullmatch(r"route_n(\d+)_e(\d+)_k(\d+)", name)
+    if not m:
+        raise SystemExit(f"unknown workload {name!r}")
+    n, e, k = (int(v) for v in m.groups())
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lg_cpu = routing_logits(n, e, "bf16", seed=0)
+    lg = lg_cpu.to(dev)
+    routing = Routing.empty(n, e, k, torch.bfloat16, dev)
+    ws = torch.empty(max(1, moe_workspace_bytes(n, e, k)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    p_route = prepare_route(lg, k, routing=routing, workspace=ws, stream=stream)
+    for _ in range(args.warmup):
+        p_route()
+    t0 = time.perf_counter()
+    st = step_stats(p_route, args.steps, stream)
+    wall = time.perf_counter() - t0
+    cold = cold_stats([p_route], 20, stream, dev)[0]
+    words = (e + 31) // 32
+    nbytes = n * e * 2 + n * k * (4 + 2 + 4 + 4 + 2) + n * words * 4 + (2 * e + 1) * 4
+    ach = nbytes / (st["mean"] * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": round(n / (st["mean"] * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": st["steps"], "warmup": args.warmup,
+        "ms_per_step": round(st["mean"], 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded Gaussian logits)",
+        "config": {"workload": f"{name}: routing metadata only, N={n} E={e} k={k} bf16 logits"},
+        "routing_us_per_layer": round(st["mean"] * 1e3, 2),
+        "step_us": {q: round(st[q] * 1e3, 2) for q in ("p10", "p50", "p90")},
+        "cold_routing_us": round(cold * 1e3, 2),
+        "wall_ms_per_step": round(wall / st["steps"] * 1e3, 4),
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                     "kernel": "routing (all routing kernels of one moe_route call)",
+                     "traffic": None, "algorithmic_bytes": nbytes,
+                     "avg_launch_us": round(st["mean"] * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        sample = min(n, 4096)
+        t0, reps = time.perf_counter(), 0
+        while True:
+            oracle.route(lg_cpu[:sample], k, "bf16")
+            reps += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(sample * reps / dt, 1), "unit": "tokens/s",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": f"first {sample} of {n} tokens, routing oracle, "
+                                            f"{reps} passes in {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +253,8 @@ def main():
               "(see DESIGN.md on how the layer would shard)", file=sys.stderr)
         sys.exit(2)
 
+    if args.workload.startswith("route_"):
+        return bench_route_only(args, args.workload)
     spec = workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -145,34 +274,42 @@ def main():
                                 act_out=act, stream=stream)
     p_w2 = prepare_experts_w2(act, w2, routing, out=out, workspace=ws, stream=stream)
 
+    p_fwd = prepare_forward(x, lg, w13, w2, k, spec.act, spec.layout, act_params(spec), out=out,
+                            routing=routing, workspace=ws, stream=stream)
+
     K, W = args.steps, args.warmup
+
+    def timed(fn, reps):
+        """Average device time of fn() over reps back-to-back calls (ms)."""
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
     for _ in range(W):
-        p_route(); p_w13(); p_w2()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+        p_fwd()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        ev[i][0].record(stream)
-        p_route()
-        ev[i][1].record(stream)
-        p_w13()
-        ev[i][2].record(stream)
-        p_w2()
-        ev[i][3].record(stream)
-    torch.cuda.synchronize()
+    st = step_stats(p_fwd, K, stream)
     wall = time.perf_counter() - t0
-    total_ms = ev[0][0].elapsed_time(ev[K - 1][3])
-    stage_ms = {name: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(K)) / K
-                for j, name in enumerate(("route", "w13", "w2"))}
-    ms_step = total_ms / K
+    ms_step = st["mean"]
+    # stages (the routing metadata of the last step stays valid for w13 / w2)
+    stage_ms = {name: timed(fn, K) for name, fn in (("route", p_route), ("w13", p_w13),
+                                                   ("w2", p_w2))}
+    cold_step, cold_route = cold_stats([p_fwd, p_route], 20, stream, dev)
     col_sum = routing.col_sum.cpu()
     work, et = algorithmic(spec, col_sum)
     # the w13 grouped GEMM is one kernel and the largest of the layer (it has
-    # n_sets x the flops of the w2 GEMM); its launch is bracketed by events
+    # n_sets x the flops of the w2 GEMM); its back-to-back launches are timed
     dom = "w13"
     f, b = work[dom]
     roof = roofline(spec, f, b, stage_ms[dom])
-    roof.update({"kernel": "grouped_gemm (w13 + activation)", "traffic": None,
+    roof.update({"kernel": "grouped_gemm (w13 + activation)",
+                 "traffic": stored_traffic(spec.name, dom),
                  "algorithmic_bytes": b, "algorithmic_flops": f,
                  "avg_launch_us": round(stage_ms[dom] * 1e3, 2)})
     result = {
@@ -180,9 +317,10 @@ def main():
         "value": round(n / (ms_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": st["steps"],
         "warmup": W,
         "ms_per_step": round(ms_step, 5),
+        "step_us": {q: round(st[q] * 1e3, 2) for q in ("p10", "p50", "p90")},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -192,6 +330,7 @@ def main():
                    "experts_touched": et, "max_expert_rows": int(col_sum.max())},
         "routing_us_per_layer": round(stage_ms["route"] * 1e3, 2),
         "stage_us": {s: round(v * 1e3, 2) for s, v in stage_ms.items()},
+        "cold_us": {"step": round(cold_step * 1e3, 2), "route": round(cold_route * 1e3, 2)},
         "wall_ms_per_step": round(wall / K * 1e3, 4),
         "roofline": roof,
     }

@@ -341,31 +341,37 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
   const int wm = wave % WM, wn = wave / WM;
   const float nal = -g.prm.alpha * 1.44269504088896341f;
 
-  // issue side: the tile whose slices are being loaded
+  // issue side: the tile whose slices are being loaded.  A tile's weight
+  // loads go out before its gather indices are read (the inline-asm loads are
+  // compiler memory barriers, so the index loads stay behind them), and the
+  // first weight slices travel while the indices make their round trip.
   uint32_t va[JA], vb[JB];
   __amdgpu_buffer_rsrc_t rb = ra;
-  auto setup_issue = [&](int i) {
-    const TileInfo ti = tile_info<BM, BN>(first + i * gx, s_ts, s_off, E, n_nt);
-    if (tid == 0) s_tile[i % NSL] = ti;
+  TileInfo cur;
+  auto setup_b = [&](int i) {
+    cur = tile_info<BM, BN>(first + i * gx, s_ts, s_off, E, n_nt);
+    if (tid == 0) s_tile[i % NSL] = cur;
     rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char *>(reinterpret_cast<const char *>(g.W)) + (size_t)ti.e * w_bytes,
+        const_cast<char *>(reinterpret_cast<const char *>(g.W)) + (size_t)cur.e * w_bytes,
         (short)0, (int)w_bytes, kRsrcWord3);
 #pragma unroll
     for (int j = 0; j < JB; ++j) {
       const int r = (wave * JB + j) * RPI + lrow;
-      const int set = r / BN, n = ti.n0 + r % BN;
+      const int set = r / BN, n = cur.n0 + r % BN;
       vb[j] = kOOB;
       if (n < Nout) {
         const int grow = NSETS == 1 ? n : (g.interleaved ? 2 * n + set : set * Nout + n);
         vb[j] = (uint32_t)grow * (uint32_t)kbytes + (((lane % CPR) ^ swz_key<RB>(r)) << 4);
       }
     }
+  };
+  auto setup_a = [&](int i) {
 #pragma unroll
     for (int j = 0; j < JA; ++j) {
       const int r = (wave * JA + j) * RPI + lrow;
       va[j] = kOOB;
-      if (r < ti.rows) {
-        const int p = ti.row0 + r;
+      if (r < cur.rows) {
+        const int p = cur.row0 + r;
         const uint32_t arow = g.gather ? (uint32_t)(g.col_sorted[p] / g.topk) : (uint32_t)p;
         va[j] = arow * (uint32_t)kbytes + (((lane % CPR) ^ swz_key<RB>(r)) << 4);
         if (META && lane % CPR == 0) {
@@ -381,30 +387,31 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
   };
   auto issue = [&](int z) {  // load slice z of the stream into ring slot z % S
     const int i = z / nk, kt = z - i * nk;
-    if (kt == 0) setup_issue(i);
     const uint32_t kb = (uint32_t)kt * RB;
     char *base = smem + (z % S) * STAGE;
     // kOOB + kb stays out of range, so invalid rows / columns need no test;
     // only a K-tail slice (kb + RB > row bytes) masks chunks past K.  Rows
     // are K * sizeof(T) bytes, a multiple of 16, so the tail is chunk-aligned.
-    if ((int)kb + RB <= kbytes) {
+    const bool tail = (int)kb + RB > kbytes;
+    if (kt == 0) setup_b(i);
 #pragma unroll
-      for (int j = 0; j < JB; ++j)
-        dma16(rb, base + BM * RB + (wave * JB + j) * 1024, vb[j] + kb);
-#pragma unroll
-      for (int j = 0; j < JA; ++j) dma16(ra, base + (wave * JA + j) * 1024, va[j] + kb);
-    } else {
-#pragma unroll
-      for (int j = 0; j < JB; ++j) {
+    for (int j = 0; j < JB; ++j) {
+      uint32_t off = vb[j] + kb;
+      if (tail) {
         const int coff = ((lane % CPR) ^ swz_key<RB>((wave * JB + j) * RPI + lrow)) << 4;
-        dma16(rb, base + BM * RB + (wave * JB + j) * 1024,
-              (int)kb + coff < kbytes ? vb[j] + kb : kOOB);
+        off = (int)kb + coff < kbytes ? off : kOOB;
       }
+      dma16(rb, base + BM * RB + (wave * JB + j) * 1024, off);
+    }
+    if (kt == 0) setup_a(i);
 #pragma unroll
-      for (int j = 0; j < JA; ++j) {
+    for (int j = 0; j < JA; ++j) {
+      uint32_t off = va[j] + kb;
+      if (tail) {
         const int coff = ((lane % CPR) ^ swz_key<RB>((wave * JA + j) * RPI + lrow)) << 4;
-        dma16(ra, base + (wave * JA + j) * 1024, (int)kb + coff < kbytes ? va[j] + kb : kOOB);
+        off = (int)kb + coff < kbytes ? off : kOOB;
       }
+      dma16(ra, base + (wave * JA + j) * 1024, off);
     }
   };
 
@@ -580,7 +587,7 @@ using GatedL = Cfg<256, 128, 4, 2, 4, 64>;  // 8 waves, 64 x (64 + 64) each
 using GatedM = Cfg<128, 128, 2, 4, 3, 128>; // 8 waves, 64 x (32 + 32) each
 using GatedS = Cfg<32, 128, 1, 4, 4, 128>;  // 4 waves, 32 x (32 + 32) each
 using PlainL = Cfg<256, 256, 4, 2, 4, 64>;  // 8 waves, 64 x 128 each
-using PlainM = Cfg<128, 128, 2, 2, 3, 128>; // 4 waves, 64 x 64 each
+using PlainM = Cfg<128, 128, 2, 4, 3, 128>; // 8 waves, 64 x 32 each
 using PlainS = Cfg<32, 128, 1, 4, 4, 128>;  // 4 waves, 32 x 32 each
 
 template <typename C, int NSETS> constexpr int lds_bytes() {
@@ -607,19 +614,40 @@ hipError_t launch_cfg(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
   return hipGetLastError();
 }
 
-// The largest tile whose tile count still covers the machine; rows per expert
-// below 48 take the 32-row tile (weight streaming, little MFMA waste).
+// Expected tiles when the M rows spread evenly over the experts: an expert's
+// last m-tile is half full on average, so about M / BM + E / 2 m-tiles.
+inline int64_t expected_tiles(int64_t M, int E, int Nout, int BM, int BN) {
+  const int64_t e = M < E ? M : E;
+  return (M / BM + (e + 1) / 2) * ((Nout + BN - 1) / BN);
+}
+
+// Relative duration of a launch: rounds of one tile per CU times the tile's
+// MFMA work, with a surcharge for tiles whose fixed per-tile cost (set-up,
+// epilogue, pipeline fill) is larger relative to that work.
+inline double launch_cost(int64_t tiles, int64_t cus, int BM, int BN, double surcharge) {
+  return (double)((tiles + cus - 1) / cus) * BM * BN * (1.0 + surcharge);
+}
+
+// Rows per expert below 48 take the 32-row tile (weight streaming, little MFMA
+// waste), and so do launches too small to give half the CUs a 128-row tile.
+// Up to one 256-row tile per expert on average, the layer streams each
+// expert's weights about once with 256-row tiles and about 1.5 times with
+// 128-row tiles, so it takes the 256-row tile; above that, whichever tile the
+// cost model favours (the 128-row tile wins where 256-row tiles would leave a
+// second, mostly empty round, e.g. at 256 rows per expert).
 template <typename T, int NSETS, int EPI>
 hipError_t launch_t(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
   using L = typename std::conditional<NSETS == 2, GatedL, PlainL>::type;
   using Md = typename std::conditional<NSETS == 2, GatedM, PlainM>::type;
   using Sm = typename std::conditional<NSETS == 2, GatedS, PlainS>::type;
   const int64_t cus = device_cus();
-  if (M < 48 * (int64_t)E) return launch_cfg<T, NSETS, EPI, Sm>(a, M, E, s);
-  if (est_tiles(M, E, a.Nout, L::BM, L::BN) >= cus) return launch_cfg<T, NSETS, EPI, L>(a, M, E, s);
-  if (est_tiles(M, E, a.Nout, Md::BM, Md::BN) >= cus / 2)
-    return launch_cfg<T, NSETS, EPI, Md>(a, M, E, s);
-  return launch_cfg<T, NSETS, EPI, Sm>(a, M, E, s);
+  const int64_t tm = expected_tiles(M, E, a.Nout, Md::BM, Md::BN);
+  if (M < 48 * (int64_t)E || tm < cus / 2) return launch_cfg<T, NSETS, EPI, Sm>(a, M, E, s);
+  if (M < (int64_t)L::BM * E) return launch_cfg<T, NSETS, EPI, L>(a, M, E, s);
+  const double cl = launch_cost(expected_tiles(M, E, a.Nout, L::BM, L::BN), cus, L::BM, L::BN, 0.0);
+  const double cm = launch_cost(tm, cus, Md::BM, Md::BN, 0.15);
+  if (cl <= cm) return launch_cfg<T, NSETS, EPI, L>(a, M, E, s);
+  return launch_cfg<T, NSETS, EPI, Md>(a, M, E, s);
 }
 
 }  // namespace

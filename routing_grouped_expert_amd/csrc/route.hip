@@ -7,21 +7,23 @@
 // snippets") and the stable sort-by-expert of the minimind issue #835 page ("It
 // is removable in plain PyTorch").  How it is computed is this file's own design:
 //
-//  * route_topk_rank: one workgroup per 256 tokens.  A token's logits row is
-//    read by a group of G lanes with 16-byte loads (G = E / values-per-load,
-//    rounded up to a power of two), each logit becomes an order-preserving
-//    integer key (value bits, then the inverted expert index, so equal values
-//    rank the lower index higher), and k rounds of an in-group max reduction
-//    (xor shuffles) pick the top-k.  Then every wave builds, with one ballot per
-//    expert, the 64-bit mask of its tokens that chose that expert; popcounts of
-//    those masks give per-wave counts and the stable in-wave rank of every
-//    entry, and a prefix over the four waves gives the rank within the block.
-//    No atomics: the result is the same on every run.
+//  * route_topk_rank: one workgroup of 1024 threads per 256 tokens.  A
+//    token's logits row is read by a group of G lanes with 16-byte loads
+//    (G = E / values-per-load, rounded up to a power of two), each logit
+//    becomes an order-preserving integer key (value bits, then the inverted
+//    expert index, so equal values rank the lower index higher), and k rounds
+//    of an in-group max reduction (DPP row permutes, then shuffles) pick the
+//    top-k.  Then, per wave of 64 tokens, one ballot per expert gives the mask
+//    of the tokens that chose it; popcounts of those masks give per-wave counts
+//    and the stable in-wave rank of every entry, and a prefix over the waves
+//    gives the rank within the block.  No atomics: every run gives the same
+//    result.
 //  * route_scatter: per-expert totals and this block's prefix over earlier
 //    blocks, an exclusive scan into offsets, and the scatter of every entry to
 //    p = offsets[e] + (entries of e in earlier blocks) + rank in block.
-//  * When all tokens fit one block, route_topk_rank does the scan and scatter
-//    itself (one launch for the whole routing step).
+//  * route_fused: batches of up to 512 tokens run both phases in one
+//    workgroup of 1024 threads with every per-entry value kept in LDS (one
+//    launch for the whole routing step).
 #include "moe_common.h"
 
 namespace moe {
@@ -365,6 +367,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter(
   __shared__ int s_off[kMaxExperts + 1];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
+  // the block's entries: token t = b * 256 + tid, slots 0..K-1.  They do not
+  // depend on the counts, so their loads go out first and overlap the sums.
+  const int64_t t = (int64_t)b * kRouteTokens + tid;
+  int ex[kMaxTopk], rk[kMaxTopk];
+  T w[kMaxTopk];
+  if (t < N) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j) {
+      if (j < K) {
+        ex[j] = topk_idx[t * K + j];
+        rk[j] = blk_rank[t * K + j];
+        w[j] = topk_w[t * K + j];
+      }
+    }
+  }
   // each thread: one expert, a quarter of the blocks (E <= 256 threads x 4 parts)
   {
     const int parts = kRouteThreads / E >= 4 ? 4 : (kRouteThreads / E >= 2 ? 2 : 1);
@@ -408,19 +425,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter(
   }
   for (int e = tid; e < E; e += kRouteThreads) s_base[e] += s_off[e];
   __syncthreads();
-  // the block's entries: token t = b * 256 + tid, slots 0..K-1 (all loads first)
-  const int64_t t = (int64_t)b * kRouteTokens + tid;
   if (t < N) {
-    int ex[kMaxTopk], rk[kMaxTopk];
-    T w[kMaxTopk];
-#pragma unroll
-    for (int j = 0; j < kMaxTopk; ++j) {
-      if (j < K) {
-        ex[j] = topk_idx[t * K + j];
-        rk[j] = blk_rank[t * K + j];
-        w[j] = topk_w[t * K + j];
-      }
-    }
 #pragma unroll
     for (int j = 0; j < kMaxTopk; ++j) {
       if (j < K) {
