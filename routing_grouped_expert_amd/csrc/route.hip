@@ -21,7 +21,7 @@
 //  * route_scatter: per-expert totals and this block's prefix over earlier
 //    blocks, an exclusive scan into offsets, and the scatter of every entry to
 //    p = offsets[e] + (entries of e in earlier blocks) + rank in block.
-//  * route_fused: batches of up to 512 tokens run both phases in one
+//  * route_fused: batches of up to 256 tokens run both phases in one
 //    workgroup of 1024 threads with every per-entry value kept in LDS (one
 //    launch for the whole routing step).
 #include "moe_common.h"
@@ -181,31 +181,36 @@ __device__ __forceinline__ void topk_chunk(const T *__restrict__ logits, int64_t
   const int tpp = 64 >> logG;  // tokens per wave pass
   const int grp = lane >> logG, lg = lane & (G - 1);
   const int words = (E + 31) >> 5;
-  // each of the THREADS / 64 waves takes TPW consecutive tokens of the chunk;
-  // many waves per SIMD overlap the serial reduction chains of their passes
-  constexpr int TPW = NT / (THREADS / 64);
-  const int npass = (TPW + tpp - 1) / tpp;
+  // Tokens are dealt round-robin over the NW = THREADS / 64 waves: pass p of
+  // wave w, group grp holds chunk token (p * tpp + grp) * NW + w, so a small
+  // batch still spreads over every wave, and many waves per SIMD overlap the
+  // serial reduction chains of their passes.
+  constexpr int NW = THREADS / 64;
+  const int npass = (NT / NW + tpp - 1) / tpp;
   // A lane's 16-byte logit chunks for kBatch passes are fetched before any is
   // used, so their loads overlap.  The batch is kept small: these kernels run
   // their code once per wave, so every extra unrolled copy is paid in cold
   // instruction-cache misses.
   constexpr int kBatch = 4;
-  for (int pass0 = 0; pass0 < npass; pass0 += kBatch) {
+  // A pass whose first token (group 0) is past N has no live token, nor has
+  // any later pass of the wave: the wave stops there (the rank phase treats
+  // chunk tokens past N as empty).
+  auto first_tok = [&](int p) { return tok0 + (int64_t)p * tpp * NW + wave; };
+  for (int pass0 = 0; pass0 < npass && first_tok(pass0) < N; pass0 += kBatch) {
     u32x4_t raw[kBatch];
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
-      const int slot = (pass0 + q) * tpp + grp;  // token slot within the wave
-      const int64_t t = tok0 + wave * TPW + slot;
+      const int tl = ((pass0 + q) * tpp + grp) * NW + wave;  // token within the chunk
+      const int64_t t = tok0 + tl;
       raw[q] = u32x4_t{0u, 0u, 0u, 0u};
-      if (slot < TPW && t < N && lg * V < E) raw[q] = fetch16(logits + t * E, lg * V, E, vec != 0);
+      if (tl < NT && t < N && lg * V < E) raw[q] = fetch16(logits + t * E, lg * V, E, vec != 0);
     }
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
-      const int slot = (pass0 + q) * tpp + grp;
-      if (pass0 + q < npass) {
-        const int tl = wave * TPW + slot;  // token within the chunk
+      if (pass0 + q < npass && first_tok(pass0 + q) < N) {
+        const int tl = ((pass0 + q) * tpp + grp) * NW + wave;
         const int64_t t = tok0 + tl;
-        const bool inwave = slot < TPW;
+        const bool inwave = tl < NT;
         const bool live = inwave && t < N;
         const int e0 = lg * V;
         Key key[V];
@@ -244,32 +249,59 @@ __device__ __forceinline__ void topk_chunk(const T *__restrict__ logits, int64_t
             bitmatrix[t * words + lg] = word;
             L.bits[tl][lg] = word;
           }
-        } else if (inwave && lg < words) {
-          L.bits[tl][lg] = 0u;
         }
       }
     }
   }
 }
 
-// Phase B: per-wave ballot masks per expert (thread tid owns chunk token tid),
-// exclusive wave bases in L.cnt, chunk totals in L.tot.  Ends synchronised.
-template <typename T, int NT>
-__device__ __forceinline__ void rank_chunk(int E, ChunkLds<T, NT> &L) {
+// Phase B: per-wave ballot masks per expert, exclusive wave bases in L.cnt,
+// chunk totals in L.tot.  Ends synchronised.  Token wave tw (64 tokens) is
+// handled by THREADS / NT waves, each taking a contiguous share of the
+// experts, so the per-expert ballot loop runs in parallel.
+template <typename T, int NT, int THREADS>
+__device__ __forceinline__ void rank_chunk(int E, int nlive, ChunkLds<T, NT> &L) {
+  constexpr int PARTS = THREADS / NT;
+  static_assert(PARTS >= 2 && PARTS * NT == THREADS, "rank split: at most 128 experts a share");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  if (tid < NT) {  // thread tid owns chunk token tid (wave-uniform condition)
-    uint32_t w = 0;
-    for (int e = 0; e < E; ++e) {  // a runtime loop keeps the code small
-      if ((e & 31) == 0) w = L.bits[tid][e >> 5];
-      const unsigned long long m = __ballot((w >> (e & 31)) & 1u);
-      if (lane == (e & 63)) {
-        L.mask[wave][e] = m;
-        L.cnt[wave][e] = popc64(m);
+  const int tw = wave % (NT / 64), part = wave / (NT / 64);  // wave-uniform
+  const int tok = tw * 64 + lane;                             // chunk token of this lane
+  const int per = (E + PARTS - 1) / PARTS;
+  const int e_beg = part * per, e_end = min(E, e_beg + per);
+  if (tw * 64 >= nlive) {
+    // no live token in this wave: empty masks and zero counts
+    for (int e = e_beg + lane; e < e_end; e += 64) {
+      L.mask[tw][e] = 0ull;
+      L.cnt[tw][e] = 0;
+    }
+  } else {
+    // Lane l keeps the masks of the (at most two) experts e of this share with
+    // e % 64 == l in registers and stores them after the loop, so the loop
+    // body touches no LDS (one bitmatrix word is read per 32 experts).
+    const bool has = tok < nlive;  // chunk tokens past N chose nothing
+    unsigned long long m0 = 0, m1 = 0;
+    for (int wi = e_beg >> 5; wi <= ((e_end - 1) >> 5) && e_beg < e_end; ++wi) {
+      const uint32_t w = has ? L.bits[tok][wi] : 0u;
+      const int lo = max(e_beg, wi * 32), hi = min(e_end, wi * 32 + 32);
+      for (int e = lo; e < hi; ++e) {  // a runtime loop keeps the code small
+        const unsigned long long m = __ballot((w >> (e & 31)) & 1u);
+        if (lane == (e & 63)) {
+          if (e - e_beg < 64) m0 = m; else m1 = m;
+        }
       }
+    }
+    const int ea = e_beg + ((lane - e_beg) & 63);  // this lane's experts: ea, ea + 64
+    if (ea < e_end) {
+      L.mask[tw][ea] = m0;
+      L.cnt[tw][ea] = popc64(m0);
+    }
+    if (ea + 64 < e_end) {
+      L.mask[tw][ea + 64] = m1;
+      L.cnt[tw][ea + 64] = popc64(m1);
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += blockDim.x) {
+  for (int e = tid; e < E; e += THREADS) {
     int run = 0;
 #pragma unroll
     for (int w2 = 0; w2 < NT / 64; ++w2) {
@@ -305,7 +337,7 @@ __global__ __launch_bounds__(THREADS) void route_fused(
   const int tid = threadIdx.x;
   topk_chunk<T, NT, THREADS>(logits, N, E, K, logG, vec, 0, topk_idx, topk_w, bitmatrix, L);
   __syncthreads();
-  rank_chunk<T, NT>(E, L);
+  rank_chunk<T, NT, THREADS>(E, (int)N, L);
   if (tid < N) {
 #pragma unroll
     for (int j = 0; j < kMaxTopk; ++j)
@@ -333,46 +365,54 @@ template <typename T>
 __global__ __launch_bounds__(kTopkThreads) void route_topk_rank(
     const T *__restrict__ logits, int64_t N, int E, int K, int logG, int vec,
     int32_t *__restrict__ topk_idx, T *__restrict__ topk_w, uint32_t *__restrict__ bitmatrix,
-    int32_t *__restrict__ blk_cnt, uint8_t *__restrict__ blk_rank) {
+    int32_t *__restrict__ blk_cnt, int nbp, uint8_t *__restrict__ blk_rank) {
   __shared__ ChunkLds<T, kRouteThreads> L;
   const int tid = threadIdx.x;
   const int64_t tok0 = (int64_t)blockIdx.x * kRouteTokens;
   topk_chunk<T, kRouteThreads, kTopkThreads>(logits, N, E, K, logG, vec, tok0, topk_idx, topk_w,
                                              bitmatrix, L);
   __syncthreads();
-  rank_chunk<T, kRouteThreads>(E, L);
+  rank_chunk<T, kRouteThreads, kTopkThreads>(E, (int)min<int64_t>(kRouteTokens, N - tok0), L);
   const int64_t t = tok0 + tid;
   if (tid < kRouteTokens && t < N) {
 #pragma unroll
     for (int j = 0; j < kMaxTopk; ++j)
       if (j < K) blk_rank[t * K + j] = (uint8_t)chunk_rank<T, kRouteThreads>(L, L.sel[tid * K + j]);
   }
-  for (int e = tid; e < E; e += kTopkThreads) blk_cnt[(int64_t)blockIdx.x * E + e] = L.tot[e];
+  // expert-major, row stride nbp (a multiple of 4): the scatter sums rows
+  for (int e = tid; e < E; e += kTopkThreads) blk_cnt[(int64_t)e * nbp + blockIdx.x] = L.tot[e];
 }
 
 // Multi-block path, kernel 2: workgroup b scatters routing block b.  It sums
-// the per-block counts (totals over all blocks, prefix over the blocks before
-// b) with the loads unrolled so they overlap, scans the totals into offsets
-// (workgroup 0 writes col_sum / offsets), and places every entry of its block
-// at offsets[e] + (entries of e in earlier blocks) + rank in the block.
+// the per-block counts (expert-major rows of nbp ints: totals over all blocks
+// and the prefix over the blocks before b) with 16-byte loads spread over all
+// threads, scans the totals into offsets (workgroup 0 writes col_sum /
+// offsets), and places every entry of its block at offsets[e] + (entries of e
+// in earlier blocks) + rank in the block.
+constexpr int kScatterThreads = 1024;
+
 template <typename T>
-__global__ __launch_bounds__(kRouteThreads) void route_scatter(
-    int64_t N, int E, int K, int nblocks, const int32_t *__restrict__ blk_cnt,
+__global__ __launch_bounds__(kScatterThreads) void route_scatter(
+    int64_t N, int E, int K, int nblocks, int nbp, const int32_t *__restrict__ blk_cnt,
     const uint8_t *__restrict__ blk_rank, const int32_t *__restrict__ topk_idx,
     const T *__restrict__ topk_w, int32_t *__restrict__ col_sum, int32_t *__restrict__ offsets,
     int32_t *__restrict__ col_sorted, int32_t *__restrict__ row_sorted,
     T *__restrict__ gate_scal) {
+  constexpr int kParts = kScatterThreads / 32;  // at most this many threads per expert
   __shared__ int s_tot[kMaxExperts];
   __shared__ int s_base[kMaxExperts];
   __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_pre[kParts][kMaxExperts];
+  __shared__ int s_all[kParts][kMaxExperts];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
   // the block's entries: token t = b * 256 + tid, slots 0..K-1.  They do not
   // depend on the counts, so their loads go out first and overlap the sums.
   const int64_t t = (int64_t)b * kRouteTokens + tid;
+  const bool own = tid < kRouteTokens && t < N;
   int ex[kMaxTopk], rk[kMaxTopk];
   T w[kMaxTopk];
-  if (t < N) {
+  if (own) {
 #pragma unroll
     for (int j = 0; j < kMaxTopk; ++j) {
       if (j < K) {
@@ -382,50 +422,54 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter(
       }
     }
   }
-  // each thread: one expert, a quarter of the blocks (E <= 256 threads x 4 parts)
-  {
-    const int parts = kRouteThreads / E >= 4 ? 4 : (kRouteThreads / E >= 2 ? 2 : 1);
-    const int e = tid % E, part = tid / E;
-    __shared__ int s_pre[4][kMaxExperts];
-    __shared__ int s_all[4][kMaxExperts];
-    if (part < parts) {
-      int pre = 0, all = 0;
-      constexpr int U = 8;
-      for (int bb0 = part * U; bb0 < nblocks; bb0 += parts * U) {
-        int c[U];
+  // thread (e, part): part-th share of row e, in 4-int chunks
+  const int parts = min(kParts, kScatterThreads / E);
+  const int e = tid % E, part = tid / E;
+  const int nch = nbp / 4;                       // 16-byte chunks per row
+  const int per = (nch + parts - 1) / parts;
+  if (part < parts) {
+    int pre = 0, all = 0;
+    const u32x4_t *row = reinterpret_cast<const u32x4_t *>(blk_cnt + (int64_t)e * nbp);
+    constexpr int U = 4;
+    for (int c0 = part * per; c0 < min(nch, (part + 1) * per); c0 += U) {
+      u32x4_t v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) c[u] = (bb0 + u < nblocks) ? blk_cnt[(int64_t)(bb0 + u) * E + e] : 0;
+      for (int u = 0; u < U; ++u)
+        v[u] = (c0 + u < min(nch, (part + 1) * per)) ? row[c0 + u] : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          all += c[u];
-          if (bb0 + u < b) pre += c[u];
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int bb = (c0 + u) * 4 + q;  // block index; entries past nblocks are padding
+          const int c = bb < nblocks ? (int)v[u][q] : 0;
+          all += c;
+          if (bb < b) pre += c;
         }
-      }
-      s_pre[part][e] = pre;
-      s_all[part][e] = all;
     }
-    __syncthreads();
-    for (int x = tid; x < E; x += kRouteThreads) {
-      int pre = 0, all = 0;
-      for (int q = 0; q < parts; ++q) {
-        pre += s_pre[q][x];
-        all += s_all[q][x];
-      }
-      s_base[x] = pre;
-      s_tot[x] = all;
-    }
-    __syncthreads();
+    s_pre[part][e] = pre;
+    s_all[part][e] = all;
   }
+  __syncthreads();
+  for (int x = tid; x < E; x += kScatterThreads) {
+    int pre = 0, all = 0;
+    for (int q = 0; q < parts; ++q) {
+      pre += s_pre[q][x];
+      all += s_all[q][x];
+    }
+    s_base[x] = pre;
+    s_tot[x] = all;
+  }
+  __syncthreads();
   block_exclusive_scan(s_tot, s_off, E);
   if (b == 0) {
-    for (int e = tid; e <= E; e += kRouteThreads) {
-      offsets[e] = s_off[e];
-      if (e < E) col_sum[e] = s_tot[e];
+    for (int x = tid; x <= E; x += kScatterThreads) {
+      offsets[x] = s_off[x];
+      if (x < E) col_sum[x] = s_tot[x];
     }
   }
-  for (int e = tid; e < E; e += kRouteThreads) s_base[e] += s_off[e];
+  for (int x = tid; x < E; x += kScatterThreads) s_base[x] += s_off[x];
   __syncthreads();
-  if (t < N) {
+  if (own) {
 #pragma unroll
     for (int j = 0; j < kMaxTopk; ++j) {
       if (j < K) {
@@ -440,7 +484,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter(
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-constexpr int kFusedTokens = 512;
+constexpr int kFusedTokens = 256;  // one workgroup is faster below; two kernels above
 // One workgroup routes everything when the batch fits one chunk.
 inline bool use_fused(int64_t N, int E) { return N <= kFusedTokens; }
 
@@ -461,12 +505,13 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, const moe_ro
     return hipGetLastError();
   }
   const int64_t nb = (N + kRouteTokens - 1) / kRouteTokens;
+  const int nbp = (int)((nb + 3) / 4 * 4);
   int32_t *blk_cnt = reinterpret_cast<int32_t *>(scratch);
-  uint8_t *blk_rank = reinterpret_cast<uint8_t *>(scratch) + align256((size_t)nb * E * 4);
+  uint8_t *blk_rank = reinterpret_cast<uint8_t *>(scratch) + align256((size_t)nbp * E * 4);
   hipLaunchKernelGGL(route_topk_rank<T>, dim3((unsigned)nb), dim3(kTopkThreads), 0, s, logits, N,
-                     E, K, logG, vec, r->topk_idx, tw, r->bitmatrix, blk_cnt, blk_rank);
-  hipLaunchKernelGGL(route_scatter<T>, dim3((unsigned)nb), dim3(kRouteThreads), 0, s, N, E, K,
-                     (int)nb, blk_cnt, blk_rank, r->topk_idx, tw, r->col_sum, r->offsets,
+                     E, K, logG, vec, r->topk_idx, tw, r->bitmatrix, blk_cnt, nbp, blk_rank);
+  hipLaunchKernelGGL(route_scatter<T>, dim3((unsigned)nb), dim3(kScatterThreads), 0, s, N, E, K,
+                     (int)nb, nbp, blk_cnt, blk_rank, r->topk_idx, tw, r->col_sum, r->offsets,
                      r->col_sorted, r->row_sorted, gs);
   return hipGetLastError();
 }
@@ -476,7 +521,8 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, const moe_ro
 size_t route_scratch_bytes(int64_t n_tokens, int n_experts, int topk) {
   if (use_fused(n_tokens, n_experts)) return 0;
   const int64_t nb = (n_tokens + kRouteTokens - 1) / kRouteTokens;
-  return align256((size_t)nb * n_experts * 4) + align256((size_t)n_tokens * topk);
+  const int64_t nbp = (nb + 3) / 4 * 4;
+  return align256((size_t)nbp * n_experts * 4) + align256((size_t)n_tokens * topk);
 }
 
 hipError_t launch_route(const void *logits, moe_dtype_t dt, int64_t n_tokens, int n_experts,
