@@ -247,12 +247,22 @@ def main():
     ap.add_argument("--workload", default="minimind_e8")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                    help="first copy MB mebibytes device to device three times: a plain copy "
+                         "of known size that hardware byte counters can be scaled by")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(see DESIGN.md on how the layer would shard)", file=sys.stderr)
         sys.exit(2)
 
+    if args.calibrate_copy > 0:
+        src = torch.ones(args.calibrate_copy << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.workload.startswith("route_"):
         return bench_route_only(args, args.workload)
     spec = workload(args.workload)

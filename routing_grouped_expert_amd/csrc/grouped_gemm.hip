@@ -589,6 +589,10 @@ using GatedS = Cfg<32, 128, 1, 4, 4, 128>;  // 4 waves, 32 x (32 + 32) each
 using PlainL = Cfg<256, 256, 4, 2, 4, 64>;  // 8 waves, 64 x 128 each
 using PlainM = Cfg<128, 128, 2, 4, 3, 128>; // 8 waves, 64 x 32 each
 using PlainS = Cfg<32, 128, 1, 4, 4, 128>;  // 4 waves, 32 x 32 each
+// one wave: a handful of rows against many weight columns (decode-sized
+// batches), where even 32 x 128 tiles leave CUs idle during weight streaming
+using GatedT = Cfg<32, 32, 1, 1, 4, 128>;   // 1 wave, 32 x (32 + 32)
+using PlainT = Cfg<32, 32, 1, 1, 4, 128>;   // 1 wave, 32 x 32
 
 template <typename C, int NSETS> constexpr int lds_bytes() {
   return C::S * (C::BM + NSETS * C::BN) * C::RB + 2 * (kMaxExperts + 1) * 4 +
@@ -629,7 +633,9 @@ inline double launch_cost(int64_t tiles, int64_t cus, int BM, int BN, double sur
 }
 
 // Rows per expert below 48 take the 32-row tile (weight streaming, little MFMA
-// waste), and so do launches too small to give half the CUs a 128-row tile.
+// waste), and so do launches too small to give half the CUs a 128-row tile;
+// when even the 32 x 128 tiles number fewer than the CUs, the 32 x 32
+// one-wave tile spreads the weight stream over more CUs.
 // Up to one 256-row tile per expert on average, the layer streams each
 // expert's weights about once with 256-row tiles and about 1.5 times with
 // 128-row tiles, so it takes the 256-row tile; above that, whichever tile the
@@ -640,9 +646,14 @@ hipError_t launch_t(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
   using L = typename std::conditional<NSETS == 2, GatedL, PlainL>::type;
   using Md = typename std::conditional<NSETS == 2, GatedM, PlainM>::type;
   using Sm = typename std::conditional<NSETS == 2, GatedS, PlainS>::type;
+  using Tn = typename std::conditional<NSETS == 2, GatedT, PlainT>::type;
   const int64_t cus = device_cus();
   const int64_t tm = expected_tiles(M, E, a.Nout, Md::BM, Md::BN);
-  if (M < 48 * (int64_t)E || tm < cus / 2) return launch_cfg<T, NSETS, EPI, Sm>(a, M, E, s);
+  if (M < 48 * (int64_t)E || tm < cus / 2) {
+    if (expected_tiles(M, E, a.Nout, Sm::BM, Sm::BN) < cus)
+      return launch_cfg<T, NSETS, EPI, Tn>(a, M, E, s);
+    return launch_cfg<T, NSETS, EPI, Sm>(a, M, E, s);
+  }
   if (M < (int64_t)L::BM * E) return launch_cfg<T, NSETS, EPI, L>(a, M, E, s);
   const double cl = launch_cost(expected_tiles(M, E, a.Nout, L::BM, L::BN), cus, L::BM, L::BN, 0.0);
   const double cm = launch_cost(tm, cus, Md::BM, Md::BN, 0.15);
