@@ -115,13 +115,15 @@ template <int N> __device__ __forceinline__ void wait_vm() {
 // outstanding, for the largest P <= pend (pend <= PMAX).  PER is the number of
 // load instructions per slice and NST the number of stores one epilogue
 // issues; vmcnt counts loads and stores together and retires them in order.
+// Counts above the 6-bit field wait for 63 instead (a stricter wait).
+constexpr int vm_cap(int n) { return n > 63 ? 63 : n; }
 template <int PER, int NST, int P>
 __device__ __forceinline__ void wait_pending(int pend, bool st) {
   if constexpr (P == 0) {
-    if (st) wait_vm<NST>(); else wait_vm<0>();
+    if (st) wait_vm<vm_cap(NST)>(); else wait_vm<0>();
   } else {
     if (pend >= P) {
-      if (st) wait_vm<P * PER + NST>(); else wait_vm<P * PER>();
+      if (st) wait_vm<vm_cap(P * PER + NST)>(); else wait_vm<vm_cap(P * PER)>();
     } else {
       wait_pending<PER, NST, P - 1>(pend, st);
     }
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
                 "tile rows vs waves");
   static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "wave tiles");
   static_assert(BK % Mm::KS == 0, "slice vs instruction K");
-  static_assert(S >= 2 && (S - 2) * (JA + JB) + NST < 64, "stages / vmcnt range");
+  static_assert(S >= 2 && (S - 2) * (JA + JB) < 64, "stages / vmcnt range");
   static_assert((EPI == EPI_RELU2 || EPI == EPI_Y || EPI == EPI_OUT) == (NSETS == 1),
                 "gated epilogues take two weight sets");
 

@@ -8,8 +8,9 @@
 // is removable in plain PyTorch").  How it is computed is this file's own design:
 //
 //  * route_topk_rank: one workgroup of 1024 threads per 256 tokens.  A
-//    token's logits row is read by a group of G lanes with 16-byte loads
-//    (G = E / values-per-load, rounded up to a power of two), each logit
+//    token's logits row is read by a group of G lanes with 16-byte loads, one
+//    or two per lane (G = E / values-per-lane, rounded up to a power of two),
+//    each logit
 //    becomes an order-preserving integer key (value bits, then the inverted
 //    expert index, so equal values rank the lower index higher), and k rounds
 //    of an in-group max reduction (DPP row permutes, then shuffles) pick the
@@ -151,28 +152,30 @@ __device__ void block_exclusive_scan(const int *in, int *out, int E) {
   __syncthreads();
 }
 
-constexpr int kWords = kMaxExperts / 32;
-
-// LDS of one routing chunk (NT tokens, one per thread in the rank phase).
-template <typename T, int NT> struct ChunkLds {
+// LDS of one routing chunk: NT tokens, at most MAXE experts and MAXK slots.
+template <typename T, int NT, int MAXE = kMaxExperts, int MAXK = kMaxTopk> struct ChunkLds {
+  static constexpr int kTokens = NT, kExperts = MAXE, kSlots = MAXK, kWords = (MAXE + 31) / 32;
   uint32_t bits[NT][kWords];               // bitmatrix rows of the chunk
-  uint8_t sel[NT * kMaxTopk];              // selected experts, slot order
-  T w[NT * kMaxTopk];                      // their weights (layer dtype)
-  float val[NT * kMaxTopk];                // their logits
-  unsigned long long mask[NT / 64][kMaxExperts];  // per-wave ballot masks
-  int cnt[NT / 64][kMaxExperts];           // per-wave counts -> exclusive wave bases
-  int tot[kMaxExperts];                    // chunk counts per expert
+  uint8_t sel[NT * MAXK];                  // selected experts, slot order
+  T w[NT * MAXK];                          // their weights (layer dtype)
+  float val[NT * MAXK];                    // their logits
+  unsigned long long mask[NT / 64][MAXE];  // per-wave ballot masks
+  int cnt[NT / 64][MAXE];                  // per-wave counts -> exclusive wave bases
+  int tot[MAXE];                           // chunk counts per expert
 };
 
 // Phase A for tokens [tok0, tok0 + NT): top-k, softmax, topk_idx / topk_w /
 // bitmatrix rows to HBM, selected experts and bitmatrix rows to LDS.
-template <typename T, int NT, int THREADS>
+// C: 16-byte logit chunks per lane (C * kVec consecutive experts per lane), so
+// G = ceil(E / (C * kVec)) lanes serve one token.  Fewer lanes per token cost
+// fewer VALU lane-operations per selection round, so wide expert sets use C = 2.
+template <typename T, int THREADS, int C, typename Lds>
 __device__ __forceinline__ void topk_chunk(const T *__restrict__ logits, int64_t N, int E, int K,
                                            int logG, int vec, int64_t tok0,
                                            int32_t *__restrict__ topk_idx,
                                            T *__restrict__ topk_w,
-                                           uint32_t *__restrict__ bitmatrix,
-                                           ChunkLds<T, NT> &L) {
+                                           uint32_t *__restrict__ bitmatrix, Lds &L) {
+  constexpr int NT = Lds::kTokens;
   using Lg = Logit<T>;
   using Key = typename Lg::Key;
   constexpr int V = Lg::kVec;
@@ -197,13 +200,17 @@ __device__ __forceinline__ void topk_chunk(const T *__restrict__ logits, int64_t
   // chunk tokens past N as empty).
   auto first_tok = [&](int p) { return tok0 + (int64_t)p * tpp * NW + wave; };
   for (int pass0 = 0; pass0 < npass && first_tok(pass0) < N; pass0 += kBatch) {
-    u32x4_t raw[kBatch];
+    u32x4_t raw[kBatch][C];
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       const int tl = ((pass0 + q) * tpp + grp) * NW + wave;  // token within the chunk
       const int64_t t = tok0 + tl;
-      raw[q] = u32x4_t{0u, 0u, 0u, 0u};
-      if (tl < NT && t < N && lg * V < E) raw[q] = fetch16(logits + t * E, lg * V, E, vec != 0);
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        const int ec = (lg * C + c) * V;
+        raw[q][c] = u32x4_t{0u, 0u, 0u, 0u};
+        if (tl < NT && t < N && ec < E) raw[q][c] = fetch16(logits + t * E, ec, E, vec != 0);
+      }
     }
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
@@ -212,20 +219,26 @@ __device__ __forceinline__ void topk_chunk(const T *__restrict__ logits, int64_t
         const int64_t t = tok0 + tl;
         const bool inwave = tl < NT;
         const bool live = inwave && t < N;
-        const int e0 = lg * V;
-        Key key[V];
-        Lg::decode(raw[q], e0, live ? E : 0, key);
+        const int e0 = lg * C * V;  // this lane's experts: e0 .. e0 + C * V - 1
+        Key key[C * V];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          Key kc[V];
+          Lg::decode(raw[q][c], e0 + c * V, live ? E : 0, kc);
+#pragma unroll
+          for (int i = 0; i < V; ++i) key[c * V + i] = kc[i];
+        }
         // k rounds: the group's largest remaining key; its owner clears it.
         // Slot j's expert and logit go to LDS (the group's lanes share them).
         uint32_t word = 0;  // bitmatrix word lg of this token
         for (int j = 0; j < K; ++j) {
           Key m = key[0];
 #pragma unroll
-          for (int i = 1; i < V; ++i) m = kmax(m, key[i]);
+          for (int i = 1; i < C * V; ++i) m = kmax(m, key[i]);
           m = group_max(m, G);
           const int e = Lg::expert(m);
 #pragma unroll
-          for (int i = 0; i < V; ++i)
+          for (int i = 0; i < C * V; ++i)
             if (e0 + i == e) key[i] = 0;  // only the owning lane matches
           if ((e >> 5) == lg) word |= 1u << (e & 31);
           if (lg == 0 && inwave) {
@@ -256,25 +269,31 @@ __device__ __forceinline__ void topk_chunk(const T *__restrict__ logits, int64_t
 }
 
 // Phase B: per-wave ballot masks per expert, exclusive wave bases in L.cnt,
-// chunk totals in L.tot.  Ends synchronised.  Token wave tw (64 tokens) is
-// handled by THREADS / NT waves, each taking a contiguous share of the
-// experts, so the per-expert ballot loop runs in parallel.
-template <typename T, int NT, int THREADS>
-__device__ __forceinline__ void rank_chunk(int E, int nlive, ChunkLds<T, NT> &L) {
-  constexpr int PARTS = THREADS / NT;
-  static_assert(PARTS >= 2 && PARTS * NT == THREADS, "rank split: at most 128 experts a share");
+// chunk totals in L.tot.  Ends synchronised.  With at least as many waves as
+// 64-token groups, group tw is handled by THREADS / NT waves, each taking a
+// contiguous share of the experts, so the per-expert ballot loop runs in
+// parallel; with fewer waves, each wave takes whole groups, all experts.
+template <int THREADS, typename Lds>
+__device__ __forceinline__ void rank_chunk(int E, int nlive, Lds &L) {
+  constexpr int NT = Lds::kTokens, TW = NT / 64, NWV = THREADS / 64;
+  constexpr int PARTS = NWV >= TW ? NWV / TW : 1;
+  static_assert(NWV >= TW ? PARTS * TW == NWV && PARTS >= (Lds::kExperts + 127) / 128
+                          : TW % NWV == 0 && Lds::kExperts <= 128,
+                "rank split: at most 128 experts a share");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int tw = wave % (NT / 64), part = wave / (NT / 64);  // wave-uniform
-  const int tok = tw * 64 + lane;                             // chunk token of this lane
+  const int part = NWV >= TW ? wave / TW : 0;                 // wave-uniform
   const int per = (E + PARTS - 1) / PARTS;
   const int e_beg = part * per, e_end = min(E, e_beg + per);
-  if (tw * 64 >= nlive) {
-    // no live token in this wave: empty masks and zero counts
-    for (int e = e_beg + lane; e < e_end; e += 64) {
-      L.mask[tw][e] = 0ull;
-      L.cnt[tw][e] = 0;
+  for (int tw = NWV >= TW ? wave % TW : wave; tw < TW; tw += NWV >= TW ? TW : NWV) {
+    const int tok = tw * 64 + lane;  // chunk token of this lane
+    if (tw * 64 >= nlive) {
+      // no live token in this group: empty masks and zero counts
+      for (int e = e_beg + lane; e < e_end; e += 64) {
+        L.mask[tw][e] = 0ull;
+        L.cnt[tw][e] = 0;
+      }
+      continue;
     }
-  } else {
     // Lane l keeps the masks of the (at most two) experts e of this share with
     // e % 64 == l in registers and stores them after the loop, so the loop
     // body touches no LDS (one bitmatrix word is read per 32 experts).
@@ -301,47 +320,52 @@ __device__ __forceinline__ void rank_chunk(int E, int nlive, ChunkLds<T, NT> &L)
     }
   }
   __syncthreads();
-  for (int e = tid; e < E; e += THREADS) {
-    int run = 0;
+  // exclusive prefix over the chunk's groups, one wave per expert and one
+  // lane per group (a shuffle scan)
+  static_assert(TW <= 64, "one lane per 64-token group");
+  for (int e = wave; e < E; e += NWV) {
+    const int c = lane < TW ? L.cnt[lane][e] : 0;
+    int incl = c;
 #pragma unroll
-    for (int w2 = 0; w2 < NT / 64; ++w2) {
-      const int c = L.cnt[w2][e];
-      L.cnt[w2][e] = run;  // exclusive prefix over the chunk's waves
-      run += c;
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
     }
-    L.tot[e] = run;
+    if (lane < TW) L.cnt[lane][e] = incl - c;
+    if (lane == 63) L.tot[e] = incl;
   }
   __syncthreads();
 }
 
-// Rank within the chunk of slot j of chunk token tid (expert e = L.sel[...]).
-template <typename T, int NT>
-__device__ __forceinline__ int chunk_rank(const ChunkLds<T, NT> &L, int e) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
-  return L.cnt[wave][e] + popc64(L.mask[wave][e] & below);
+// Rank within the chunk of an entry of chunk token t for expert e.
+template <typename Lds>
+__device__ __forceinline__ int chunk_rank(const Lds &L, int t, int e) {
+  const int tw = t >> 6, ln = t & 63;
+  const unsigned long long below = ln ? (~0ull >> (64 - ln)) : 0ull;
+  return L.cnt[tw][e] + popc64(L.mask[tw][e] & below);
 }
 
-// Small batches (N <= NT tokens): one workgroup, one launch.  Every per-entry
+// Batches of at most NT tokens: one workgroup, one launch.  Every per-entry
 // value stays in LDS; the scan and the scatter follow the rank phase directly.
-template <typename T, int NT, int THREADS>
+template <typename T, int THREADS, int C, typename Lds>
 __global__ __launch_bounds__(THREADS) void route_fused(
     const T *__restrict__ logits, int64_t N, int E, int K, int logG, int vec,
     int32_t *__restrict__ topk_idx, T *__restrict__ topk_w, uint32_t *__restrict__ bitmatrix,
     int32_t *__restrict__ col_sum, int32_t *__restrict__ offsets,
     int32_t *__restrict__ col_sorted, int32_t *__restrict__ row_sorted,
     T *__restrict__ gate_scal) {
-  __shared__ ChunkLds<T, NT> L;
-  __shared__ uint16_t s_rank[NT * kMaxTopk];
-  __shared__ int s_off[kMaxExperts + 1];
+  constexpr int NT = Lds::kTokens;
+  __shared__ Lds L;
+  __shared__ uint16_t s_rank[NT * Lds::kSlots];
+  __shared__ int s_off[Lds::kExperts + 1];
   const int tid = threadIdx.x;
-  topk_chunk<T, NT, THREADS>(logits, N, E, K, logG, vec, 0, topk_idx, topk_w, bitmatrix, L);
+  topk_chunk<T, THREADS, C>(logits, N, E, K, logG, vec, 0, topk_idx, topk_w, bitmatrix, L);
   __syncthreads();
-  rank_chunk<T, NT, THREADS>(E, (int)N, L);
-  if (tid < N) {
+  rank_chunk<THREADS>(E, (int)N, L);
+  for (int t = tid; t < N; t += THREADS) {
 #pragma unroll
-    for (int j = 0; j < kMaxTopk; ++j)
-      if (j < K) s_rank[tid * K + j] = (uint16_t)chunk_rank<T, NT>(L, L.sel[tid * K + j]);
+    for (int j = 0; j < Lds::kSlots; ++j)
+      if (j < K) s_rank[t * K + j] = (uint16_t)chunk_rank(L, t, L.sel[t * K + j]);
   }
   block_exclusive_scan(L.tot, s_off, E);  // synchronises
   for (int e = tid; e <= E; e += THREADS) {
@@ -361,23 +385,22 @@ __global__ __launch_bounds__(THREADS) void route_fused(
 // per-block expert counts and per-entry in-block ranks to the workspace.
 constexpr int kTopkThreads = 1024;
 
-template <typename T>
+template <typename T, int C>
 __global__ __launch_bounds__(kTopkThreads) void route_topk_rank(
     const T *__restrict__ logits, int64_t N, int E, int K, int logG, int vec,
     int32_t *__restrict__ topk_idx, T *__restrict__ topk_w, uint32_t *__restrict__ bitmatrix,
     int32_t *__restrict__ blk_cnt, int nbp, uint8_t *__restrict__ blk_rank) {
-  __shared__ ChunkLds<T, kRouteThreads> L;
+  __shared__ ChunkLds<T, kRouteTokens> L;
   const int tid = threadIdx.x;
   const int64_t tok0 = (int64_t)blockIdx.x * kRouteTokens;
-  topk_chunk<T, kRouteThreads, kTopkThreads>(logits, N, E, K, logG, vec, tok0, topk_idx, topk_w,
-                                             bitmatrix, L);
+  topk_chunk<T, kTopkThreads, C>(logits, N, E, K, logG, vec, tok0, topk_idx, topk_w, bitmatrix, L);
   __syncthreads();
-  rank_chunk<T, kRouteThreads, kTopkThreads>(E, (int)min<int64_t>(kRouteTokens, N - tok0), L);
+  rank_chunk<kTopkThreads>(E, (int)min<int64_t>(kRouteTokens, N - tok0), L);
   const int64_t t = tok0 + tid;
   if (tid < kRouteTokens && t < N) {
 #pragma unroll
     for (int j = 0; j < kMaxTopk; ++j)
-      if (j < K) blk_rank[t * K + j] = (uint8_t)chunk_rank<T, kRouteThreads>(L, L.sel[tid * K + j]);
+      if (j < K) blk_rank[t * K + j] = (uint8_t)chunk_rank(L, tid, L.sel[tid * K + j]);
   }
   // expert-major, row stride nbp (a multiple of 4): the scatter sums rows
   for (int e = tid; e < E; e += kTopkThreads) blk_cnt[(int64_t)e * nbp + blockIdx.x] = L.tot[e];
@@ -484,32 +507,56 @@ __global__ __launch_bounds__(kScatterThreads) void route_scatter(
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-constexpr int kFusedTokens = 256;  // one workgroup is faster below; two kernels above
-// One workgroup routes everything when the batch fits one chunk.
-inline bool use_fused(int64_t N, int E) { return N <= kFusedTokens; }
+// Which routing path a batch takes: one workgroup for up to 256 tokens,
+// otherwise one workgroup per 256 tokens plus the scatter kernel.  (One
+// workgroup for up to 4096 tokens of a few experts was measured slower than
+// the two kernels: 16.8 against 11.1 us at N = 4096, E = 8.)
+constexpr int kFusedTokens = 256;
+enum RoutePath { kPathFused, kPathBlocks };
+inline RoutePath route_path(int64_t N, int E, int K) {
+  (void)E;
+  (void)K;
+  return N <= kFusedTokens ? kPathFused : kPathBlocks;
+}
 
 template <typename T>
 hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, const moe_routing_t *r,
                           void *scratch, hipStream_t s) {
   constexpr int V = Logit<T>::kVec;
-  const int need = (E + V - 1) / V;
+  // two chunks a lane when one would need more than 8 lanes a token, unless the
+  // batch is so small that spreading it over more lanes matters more
+  const bool wide = (E + V - 1) / V > 8 && N > 64;
+  const int C = wide ? 2 : 1;
+  const int need = (E + C * V - 1) / (C * V);
   int logG = 0;
   while ((1 << logG) < need) ++logG;
   const int vec = (E % V) == 0;
   T *tw = reinterpret_cast<T *>(r->topk_w);
   T *gs = reinterpret_cast<T *>(r->gate_scal);
-  if (use_fused(N, E)) {
-    hipLaunchKernelGGL((route_fused<T, kFusedTokens, 1024>), dim3(1), dim3(1024), 0, s, logits,
-                       N, E, K, logG, vec, r->topk_idx, tw, r->bitmatrix, r->col_sum, r->offsets,
-                       r->col_sorted, r->row_sorted, gs);
+  const RoutePath path = route_path(N, E, K);
+  if (path == kPathFused) {
+    if (wide)
+      hipLaunchKernelGGL((route_fused<T, 1024, 2, ChunkLds<T, kFusedTokens>>), dim3(1), dim3(1024),
+                         0, s, logits, N, E, K, logG, vec, r->topk_idx, tw, r->bitmatrix,
+                         r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs);
+    else
+      hipLaunchKernelGGL((route_fused<T, 1024, 1, ChunkLds<T, kFusedTokens>>), dim3(1), dim3(1024),
+                         0, s, logits, N, E, K, logG, vec, r->topk_idx, tw, r->bitmatrix,
+                         r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs);
     return hipGetLastError();
   }
   const int64_t nb = (N + kRouteTokens - 1) / kRouteTokens;
   const int nbp = (int)((nb + 3) / 4 * 4);
   int32_t *blk_cnt = reinterpret_cast<int32_t *>(scratch);
   uint8_t *blk_rank = reinterpret_cast<uint8_t *>(scratch) + align256((size_t)nbp * E * 4);
-  hipLaunchKernelGGL(route_topk_rank<T>, dim3((unsigned)nb), dim3(kTopkThreads), 0, s, logits, N,
-                     E, K, logG, vec, r->topk_idx, tw, r->bitmatrix, blk_cnt, nbp, blk_rank);
+  if (wide)
+    hipLaunchKernelGGL((route_topk_rank<T, 2>), dim3((unsigned)nb), dim3(kTopkThreads), 0, s,
+                       logits, N, E, K, logG, vec, r->topk_idx, tw, r->bitmatrix, blk_cnt, nbp,
+                       blk_rank);
+  else
+    hipLaunchKernelGGL((route_topk_rank<T, 1>), dim3((unsigned)nb), dim3(kTopkThreads), 0, s,
+                       logits, N, E, K, logG, vec, r->topk_idx, tw, r->bitmatrix, blk_cnt, nbp,
+                       blk_rank);
   hipLaunchKernelGGL(route_scatter<T>, dim3((unsigned)nb), dim3(kScatterThreads), 0, s, N, E, K,
                      (int)nb, nbp, blk_cnt, blk_rank, r->topk_idx, tw, r->col_sum, r->offsets,
                      r->col_sorted, r->row_sorted, gs);
@@ -519,7 +566,7 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, const moe_ro
 }  // namespace
 
 size_t route_scratch_bytes(int64_t n_tokens, int n_experts, int topk) {
-  if (use_fused(n_tokens, n_experts)) return 0;
+  if (route_path(n_tokens, n_experts, topk) != kPathBlocks) return 0;
   const int64_t nb = (n_tokens + kRouteTokens - 1) / kRouteTokens;
   const int64_t nbp = (nb + 3) / 4 * 4;
   return align256((size_t)nbp * n_experts * 4) + align256((size_t)n_tokens * topk);

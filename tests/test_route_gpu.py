@@ -39,6 +39,10 @@ EDGE = [
     (300, 1, 1, "bf16"),     # single expert
     (40, 64, 8, "bf16"),     # N*k < E-ish: many empty experts
     (5000, 128, 1, "f32"),
+    (4096, 32, 2, "bf16"),   # compact single-workgroup path at its limits
+    (4097, 8, 1, "bf16"),    # one token past it: multi-block
+    (4096, 16, 1, "f32"),    # compact path, fp32 logits
+    (2049, 3, 2, "bf16"),    # compact path, scalar loads, ragged 64-token groups
 ]
 
 
