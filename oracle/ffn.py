@@ -143,3 +143,16 @@ def moe_ffn_sorted(x, topk_idx, topk_w, w13, w2, act: str, layout: str = "packed
             out[tok[lo:hi]] += wsort[lo:hi, None] * y
         lo = hi
     return out
+
+
+def moe_ffn_share(x, topk_idx, topk_w, w13, w2, act: str, local_offset: int,
+                  layout: str = "packed", params: dict | None = None,
+                  tokens=None) -> np.ndarray:
+    """Contribution of one expert-parallel share: ``w13``/``w2`` hold the
+    experts [local_offset, local_offset + len(w13)) and ``topk_idx`` the global
+    selection.  The selection is remapped to local ids (-1 outside the share)
+    and the masked per-expert loop runs over the local experts, so slots routed
+    elsewhere add nothing and a token with none of them gets a zero row."""
+    from .routing import remap_to_share
+    loc = remap_to_share(topk_idx, local_offset, np.asarray(w13).shape[0])
+    return moe_ffn(x, loc, topk_w, w13, w2, act, layout, params, tokens=tokens)

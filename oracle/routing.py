@@ -12,7 +12,13 @@ What is computed, and where the pages define it:
 * the ragged per-expert offsets ``[0] + cumulative counts`` -- the segment bounds
   of the sorted dispatch in the minimind issue #835 page, section "It is
   removable in plain PyTorch" (stable sort by expert, group ends by
-  ``searchsorted(right=True)``).
+  ``searchsorted(right=True)``);
+* the expert-parallel share (``route_ep``): the selected expert ids remapped to
+  the ids local to one GPU's experts, then the bitmatrix re-packed and the
+  metadata rebuilt from the remapped ids -- the expert-map branch of the PR
+  #45457 report ("implementation breakdown"); the share is the
+  (local_expert_offset, num_local_experts) pair of the kernel call in the vLLM
+  PR #47106 report ("key source snippets").
 
 Readings where the pages are silent (each listed in the design doc):
 ties in top-k go to the lowest expert index; slots are ordered by descending
@@ -125,13 +131,16 @@ def topk_softmax(v: np.ndarray, idx: np.ndarray, w_dtype: str) -> np.ndarray:
 
 def bitmatrix(idx: np.ndarray, n_experts: int) -> np.ndarray:
     """``[N, ceil(E/32)]`` uint32; bit (e % 32) of word e // 32 in row t is set iff
-    token t selected expert e.  Bits past E are zero."""
+    token t selected expert e.  Bits past E are zero; an id of -1 (a slot whose
+    expert is outside an expert-parallel share) sets no bit."""
     n, k = idx.shape
     words = (n_experts + 31) // 32
     bm = np.zeros((n, words), dtype=np.uint64)
     for j in range(k):
         e = idx[:, j].astype(np.int64)
-        np.bitwise_or.at(bm, (np.arange(n), e // 32), (np.uint64(1) << (e % 32).astype(np.uint64)))
+        rows = np.flatnonzero(e >= 0)
+        e = e[rows]
+        np.bitwise_or.at(bm, (rows, e // 32), (np.uint64(1) << (e % 32).astype(np.uint64)))
     return bm.astype(np.uint32)
 
 
@@ -156,11 +165,13 @@ def sorted_indices(idx: np.ndarray, n_experts: int):
     are grouped by expert (ascending) and kept in flat order inside a group;
     ``row_sorted[f]`` is the position p of entry f (its inverse permutation).
     Built with one masked scan per expert, which is stable by construction.
+    Entries with id -1 (outside an expert-parallel share) get no position:
+    ``col_sorted`` then lists only the others and their ``row_sorted`` is -1.
     """
     flat = idx.reshape(-1)
     parts = [np.flatnonzero(flat == e) for e in range(n_experts)]
     col_sorted = (np.concatenate(parts) if parts else np.zeros(0, np.int64)).astype(np.int64)
-    row_sorted = np.empty_like(col_sorted)
+    row_sorted = np.full(flat.size, -1, dtype=np.int64)
     row_sorted[col_sorted] = np.arange(col_sorted.size)
     return col_sorted.astype(np.int32), row_sorted.astype(np.int32)
 
@@ -178,7 +189,8 @@ class RoutingRef:
 
     @property
     def token_of_row(self) -> np.ndarray:
-        """Token feeding sorted row p: col_sorted[p] // k."""
+        """Token feeding sorted row p: col_sorted[p] // k (rows past an expert
+        share's last local entry hold col_sorted -1 and have no token)."""
         k = self.topk_idx.shape[1]
         return self.col_sorted // k
 
@@ -200,4 +212,48 @@ def route(logits, topk: int, w_dtype: str) -> RoutingRef:
         col_sorted=col_sorted,
         row_sorted=row_sorted,
         gate_scal=w.reshape(-1)[col_sorted],
+    )
+
+
+def remap_to_share(idx: np.ndarray, local_offset: int, n_local: int) -> np.ndarray:
+    """Global expert ids -> ids local to the share [local_offset, local_offset +
+    n_local): ``e - local_offset`` inside the share, -1 outside."""
+    g = np.asarray(idx, dtype=np.int64)
+    inside = (g >= local_offset) & (g < local_offset + n_local)
+    return np.where(inside, g - local_offset, -1).astype(np.int32)
+
+
+def route_ep(logits, topk: int, w_dtype: str, local_offset: int, n_local: int) -> RoutingRef:
+    """Routing of one GPU's expert share [local_offset, local_offset + n_local).
+
+    Top-k and softmax over all E logits (``topk_idx`` keeps the global ids);
+    then the selected ids are remapped to local ids (-1 outside the share) and
+    the bitmatrix, histogram, offsets and sorted indices are built from the
+    remapped ids over the n_local experts.  ``col_sorted`` and ``gate_scal`` keep
+    their N*k length: positions past the M_local = offsets[n_local] local entries
+    hold -1 and 0.
+    """
+    v = to_f64(logits)
+    n, e = v.shape
+    if not (0 <= local_offset and 1 <= n_local and local_offset + n_local <= e):
+        raise ValueError("expert share outside [0, n_experts)")
+    idx = topk_select(v, topk)
+    w = topk_softmax(v, idx, w_dtype)
+    loc = remap_to_share(idx, local_offset, n_local)
+    cs = histogram(loc, n_local)
+    col, row_sorted = sorted_indices(loc, n_local)
+    m, ml = n * topk, col.size
+    col_sorted = np.full(m, -1, dtype=np.int32)
+    col_sorted[:ml] = col
+    gate = np.zeros(m, dtype=np.float64)
+    gate[:ml] = w.reshape(-1)[col]
+    return RoutingRef(
+        topk_idx=idx,
+        topk_w=w,
+        bitmatrix=bitmatrix(loc, n_local),
+        col_sum=cs,
+        offsets=offsets_from_hist(cs),
+        col_sorted=col_sorted,
+        row_sorted=row_sorted,
+        gate_scal=gate,
     )

@@ -187,6 +187,46 @@ def pin_empty_experts():
     assert np.array_equal(r0.offsets, np.zeros(9, dtype=np.int32))
 
 
+def pin_share_routing(seed=14):
+    """An expert share's routing against the whole layer's (which the pins above
+    fix): the share's sorted entries are the contiguous slice of the layer's
+    expert-major order between offsets[lo] and offsets[lo + n]; counts and
+    offsets are the layer's restricted and rebased; a slot's position moves down
+    by offsets[lo], or is -1 when its expert is outside the share; local bit l
+    of the bitmatrix is the layer's bit lo + l (unpacked little-endian)."""
+    rng = np.random.default_rng(seed)
+    cases = [(300, 64, 4, "bf16", [(0, 64), (0, 8), (8, 8), (56, 8), (5, 37), (63, 1), (30, 2)]),
+             (97, 8, 2, "f32", [(0, 1), (3, 4), (7, 1), (0, 8)]),
+             (40, 128, 8, "bf16", [(96, 32), (17, 33), (0, 128)])]
+    for n, e, k, wdt, shares in cases:
+        v = rng.normal(size=(n, e))
+        if wdt == "bf16":
+            v = torch.from_numpy(v).to(torch.bfloat16).double().numpy()
+        g = orout.route(v, k, wdt)
+        flat = g.topk_idx.reshape(-1)
+        gb = np.unpackbits(g.bitmatrix.view(np.uint8), axis=1, bitorder="little")[:, :e]
+        for lo, nl in shares:
+            r = orout.route_ep(v, k, wdt, lo, nl)
+            a, b = int(g.offsets[lo]), int(g.offsets[lo + nl])
+            assert np.array_equal(r.topk_idx, g.topk_idx) and np.array_equal(r.topk_w, g.topk_w)
+            assert np.array_equal(r.col_sum, g.col_sum[lo:lo + nl])
+            assert np.array_equal(r.offsets, g.offsets[lo:lo + nl + 1] - a)
+            assert r.col_sorted.shape == (n * k,) and r.gate_scal.shape == (n * k,)
+            assert np.array_equal(r.col_sorted[:b - a], g.col_sorted[a:b])
+            assert np.all(r.col_sorted[b - a:] == -1)
+            assert np.array_equal(r.gate_scal[:b - a], g.gate_scal[a:b])
+            assert np.all(r.gate_scal[b - a:] == 0)
+            inside = (flat >= lo) & (flat < lo + nl)
+            assert np.array_equal(r.row_sorted, np.where(inside, g.row_sorted - a, -1))
+            assert r.bitmatrix.shape == (n, (nl + 31) // 32)
+            lb = np.unpackbits(r.bitmatrix.view(np.uint8), axis=1, bitorder="little")
+            assert np.array_equal(lb[:, :nl], gb[:, lo:lo + nl]) and not lb[:, nl:].any()
+        whole = orout.route_ep(v, k, wdt, 0, e)
+        for f in ("topk_idx", "topk_w", "bitmatrix", "col_sum", "offsets", "col_sorted",
+                  "row_sorted", "gate_scal"):
+            assert np.array_equal(getattr(whole, f), getattr(g, f)), f
+
+
 # --------------------------------------------------------------------------
 # FFN pins
 # --------------------------------------------------------------------------
@@ -374,9 +414,40 @@ def pin_ffn_token_subset(seed=13):
     assert np.allclose(sub, full[sel], rtol=1e-13, atol=1e-13)
 
 
+def pin_ffn_shares(seed=15):
+    """Expert shares: their contributions summed over a partition of the experts
+    give the whole layer; one share equals the brute-force token loop with the
+    weights of slots outside the share set to zero; a share that no token chose
+    gives zero rows."""
+    rng = np.random.default_rng(seed)
+    for act, layout, params in [("silu", "packed", {}), ("relu2", "packed", {}),
+                                ("swiglu_oai", "interleaved",
+                                 {"alpha": 1.702, "beta": 1.0, "limit": 0.9})]:
+        x, r, w13, w2 = _tiny_case(rng, act, layout, n=12, h=6, inter=4, e=5, k=2)
+        full = offn.moe_ffn(x, r.topk_idx, r.topk_w, w13, w2, act, layout, params)
+        tot = np.zeros_like(full)
+        for lo, nl in [(0, 2), (2, 1), (3, 2)]:
+            tot += offn.moe_ffn_share(x, r.topk_idx, r.topk_w, w13[lo:lo + nl], w2[lo:lo + nl],
+                                      act, lo, layout, params)
+        assert np.allclose(tot, full, rtol=1e-12, atol=1e-12)
+        lo, nl = 1, 3
+        idx = r.topk_idx
+        wz = np.where((idx >= lo) & (idx < lo + nl), r.topk_w, 0.0)
+        bf = brute_ffn(x, idx, wz, w13, w2, act, layout, params)
+        sh = offn.moe_ffn_share(x, idx, r.topk_w, w13[lo:lo + nl], w2[lo:lo + nl], act, lo,
+                                layout, params)
+        assert np.allclose(sh, bf, rtol=1e-11, atol=1e-11)
+    x, r, w13, w2 = _tiny_case(rng, "silu", "packed", n=9, h=4, inter=4, e=4, k=2)
+    v = rng.normal(size=(9, 4))
+    v[:, 3] = -50.0                                   # expert 3 is never in a top-2
+    r = orout.route(v, 2, "f32")
+    z = offn.moe_ffn_share(x, r.topk_idx, r.topk_w, w13[3:], w2[3:], "silu", 3)
+    assert z.shape == x.shape and not z.any()
+
+
 ROUTING_PINS = [pin_golden_routing, pin_topk_bruteforce, pin_topk_lexsort, pin_topk_special_cases,
                 pin_bf16_rounding, pin_weights_closed_forms, pin_metadata_invariants,
-                pin_empty_experts]
+                pin_empty_experts, pin_share_routing]
 FFN_PINS = [pin_ffn_bruteforce, pin_ffn_masked_equals_sorted, pin_ffn_layout_invariance,
             pin_ffn_dense_special_case, pin_activation_closed_forms, pin_ffn_linearity,
-            pin_ffn_token_subset]
+            pin_ffn_token_subset, pin_ffn_shares]

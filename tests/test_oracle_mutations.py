@@ -132,6 +132,23 @@ def moe_ffn_no_weight(x, topk_idx, topk_w, *a, **kw):
 
 
 _orig_moe = offn.moe_ffn
+_orig_remap = orout.remap_to_share
+
+
+def remap_off_by_one(idx, lo, nl):
+    r = _orig_remap(idx, lo, nl)
+    return np.where(r >= 0, np.minimum(r + 1, nl - 1), -1).astype(np.int32)
+
+
+def remap_upper_inclusive(idx, lo, nl):
+    g = np.asarray(idx, dtype=np.int64)
+    inside = (g >= lo) & (g <= lo + nl)
+    return np.where(inside, g - lo, -1).astype(np.int32)
+
+
+def remap_none(idx, lo, nl):
+    # global ids used as local ones
+    return np.asarray(idx, dtype=np.int32)
 
 MUTATIONS = [
     ("topk ties high", orout, "topk_select", topk_ties_high, "routing"),
@@ -151,6 +168,11 @@ MUTATIONS = [
     ("sigmoid sign", offn, "activation", act_sigmoid_sign, "ffn"),
     ("w2 transposed", offn, "expert_ffn", expert_transposed_w2, "ffn"),
     ("routing weight dropped", offn, "moe_ffn", moe_ffn_no_weight, "ffn"),
+    ("share remap off by one", orout, "remap_to_share", remap_off_by_one, "routing"),
+    ("share upper bound inclusive", orout, "remap_to_share", remap_upper_inclusive, "routing"),
+    ("share ids not remapped (routing)", orout, "remap_to_share", remap_none, "routing"),
+    ("share ids not remapped (ffn)", orout, "remap_to_share", remap_none, "ffn"),
+    ("share remap off by one (ffn)", orout, "remap_to_share", remap_off_by_one, "ffn"),
 ]
 
 
