@@ -34,8 +34,10 @@ import torch
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from routing_grouped_expert_amd import (Routing, moe_workspace_bytes, prepare_experts_w13,  # noqa: E402
-                                        prepare_experts_w2, prepare_forward, prepare_route)
+from routing_grouped_expert_amd import (Routing, moe_workspace_bytes,  # noqa: E402
+                                        prepare_experts_w13, prepare_experts_w2,
+                                        prepare_forward, prepare_forward_ep, prepare_route,
+                                        prepare_route_ep)
 from routing_grouped_expert_amd.synth import (act_params, layer_spec, make_layer,  # noqa: E402
                                               routing_logits)
 
@@ -45,6 +47,12 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 
 
 def workload(name: str):
+    if name.startswith("gptoss_ep"):
+        # one GPU of an expert-parallel group of G: the first E/G experts of the
+        # gpt-oss-sized layer, every token routed over all E
+        g, n = name[len("gptoss_ep"):].split("_n")
+        base = layer_spec("gptoss", n_tokens=int(n))
+        return base.with_(name=name, local_offset=0, n_local=base.n_experts // int(g))
     if name.startswith("minimind_e"):
         return layer_spec("minimind", n_experts=int(name[len("minimind_e"):]), name=name)
     if name.startswith("gptoss_n"):
@@ -58,19 +66,23 @@ def workload(name: str):
 
 def describe(spec) -> str:
     extra = f" zipf_s={spec.zipf_s}" if spec.zipf_s else ""
+    if spec.n_local is not None:
+        extra += f" share=experts[{spec.local_offset}:{spec.local_offset + spec.n_local}]"
     return (f"N={spec.n_tokens} H={spec.hidden} I={spec.inter} E={spec.n_experts} "
             f"k={spec.topk} {spec.act} {spec.layout} {spec.dtype}{extra}")
 
 
 def algorithmic(spec, col_sum):
     """Algorithmic flops / bytes per launch of each stage (weights of touched
-    experts read once, activations read and written once)."""
+    experts read once, activations read and written once).  ``col_sum`` is the
+    measured histogram; its total is the number of routed rows (N*k, or the
+    rows of the local experts for an expert-parallel share)."""
     s = 2 if spec.dtype == "bf16" else 4
     n, h, i, e, k = spec.n_tokens, spec.hidden, spec.inter, spec.n_experts, spec.topk
-    m = n * k
+    m = int(col_sum.sum())
     g = 2 if spec.act != "relu2" else 1
     et = int((col_sum > 0).sum())
-    words = (e + 31) // 32
+    words = (spec.n_weights + 31) // 32
     route_b = n * e * s + n * k * (4 + s + 4 + 4 + s) + n * words * 4 + (2 * e + 1) * 4
     w13_f = 2 * m * g * i * h
     w13_b = et * g * i * h * s + n * h * s + m * i * s
@@ -101,15 +113,21 @@ def cpu_baseline(spec, layer, budget_s: float):
         threads = os.cpu_count()
     wd = "bf16" if spec.dtype == "bf16" else "f32"
     n = spec.n_tokens
+    share = spec.n_local is not None
     # a contiguous token sample sized so one oracle pass takes a few seconds at most
     sample = min(n, max(1, int(4096 * 512 * 1408 / (spec.hidden * spec.inter))))
     lg, x = layer.logits[:sample], layer.x[:sample]
     done, t0 = 0, time.perf_counter()
     reps = 0
     while True:
-        r = oracle.route(lg, spec.topk, wd)
-        oracle.moe_ffn(x, r.topk_idx, r.topk_w, layer.w13, layer.w2, spec.act, spec.layout,
-                       act_params(spec))
+        if share:
+            r = oracle.route_ep(lg, spec.topk, wd, spec.local_offset, spec.n_local)
+            oracle.moe_ffn_share(x, r.topk_idx, r.topk_w, layer.w13, layer.w2, spec.act,
+                                 spec.local_offset, spec.layout, act_params(spec))
+        else:
+            r = oracle.route(lg, spec.topk, wd)
+            oracle.moe_ffn(x, r.topk_idx, r.topk_w, layer.w13, layer.w2, spec.act, spec.layout,
+                           act_params(spec))
         done += sample
         reps += 1
         if time.perf_counter() - t0 >= budget_s:
@@ -272,20 +290,29 @@ def main():
     x, lg = layer.x.to(dev), layer.logits.to(dev)
     w13, w2 = layer.w13.to(dev), layer.w2.to(dev)
     n, e, k = spec.n_tokens, spec.n_experts, spec.topk
+    share = spec.n_local is not None
     dt = x.dtype
-    routing = Routing.empty(n, e, k, dt, dev)
+    routing = Routing.empty(n, spec.n_weights, k, dt, dev)
     act = torch.empty(n * k, spec.inter, dtype=dt, device=dev)
     out = torch.empty_like(x)
     ws = torch.empty(moe_workspace_bytes(n, e, k, spec.hidden, spec.inter, dt), dtype=torch.uint8,
                      device=dev)
     stream = torch.cuda.current_stream(dev)
-    p_route = prepare_route(lg, k, routing=routing, workspace=ws, stream=stream)
+    if share:
+        p_route = prepare_route_ep(lg, k, spec.local_offset, spec.n_local, routing=routing,
+                                   workspace=ws, stream=stream)
+        p_fwd = prepare_forward_ep(x, lg, w13, w2, k, spec.local_offset, spec.act, spec.layout,
+                                   act_params(spec), out=out, routing=routing, workspace=ws,
+                                   stream=stream)
+    else:
+        p_route = prepare_route(lg, k, routing=routing, workspace=ws, stream=stream)
+        p_fwd = prepare_forward(x, lg, w13, w2, k, spec.act, spec.layout, act_params(spec),
+                                out=out, routing=routing, workspace=ws, stream=stream)
+    # the halves run the same kernels as the full call (k > 1 for every share
+    # workload, so the combine skips the slots routed to other GPUs)
     p_w13 = prepare_experts_w13(x, w13, routing, spec.act, spec.layout, act_params(spec),
                                 act_out=act, stream=stream)
     p_w2 = prepare_experts_w2(act, w2, routing, out=out, workspace=ws, stream=stream)
-
-    p_fwd = prepare_forward(x, lg, w13, w2, k, spec.act, spec.layout, act_params(spec), out=out,
-                            routing=routing, workspace=ws, stream=stream)
 
     K, W = args.steps, args.warmup
 

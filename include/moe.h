@@ -8,6 +8,9 @@
  *   moe_experts  routing metadata + x -> grouped expert FFN -> weighted combine
  *   moe_forward  moe_route followed by moe_experts, on one stream
  *
+ * and their expert-parallel-share variants moe_route_ep, moe_experts_ep and
+ * moe_forward_ep (one GPU's contiguous share of the experts; see below).
+ *
  * moe_experts is also exported as its two halves, moe_experts_w13 (grouped
  * GEMM with w13 + activation) and moe_experts_w2 (grouped GEMM with w2 +
  * routing weight + combine).
@@ -173,6 +176,55 @@ moe_status_t moe_forward(const void *x, const void *logits, moe_dtype_t dtype,
                          moe_w13_layout_t layout, const moe_act_params_t *params,
                          const moe_routing_t *routing_out, void *out, void *workspace,
                          size_t ws_bytes, void *stream);
+
+/* ---- Expert-parallel share ---------------------------------------------------
+ * One GPU of an expert-parallel group holds the contiguous share of experts
+ * [local_offset, local_offset + n_local) of the layer's n_experts and computes
+ * those experts' contribution for every token; the group's outputs summed over
+ * all shares give the layer output.  The share is the (local_expert_offset,
+ * num_local_experts) pair the experts kernel call of the vLLM PR #47106 report
+ * takes ("key source snippets"); remapping the selected expert ids to local
+ * ids and re-packing the bitmatrix after the remap is the expert-map branch of
+ * the vLLM PR #45457 report ("implementation breakdown").
+ *
+ * moe_route_ep: top-k and softmax over all n_experts logits, then
+ *   topk_idx [N, topk]   selected experts, GLOBAL ids (as moe_route)
+ *   topk_w   [N, topk]   softmax over the selected logits (as moe_route)
+ *   bitmatrix [N, ceil(n_local/32)]  bit l: token chose local expert l
+ *   col_sum [n_local], offsets [n_local+1]  over local experts; offsets[n_local]
+ *            = M_local, the number of slots whose expert is in the share
+ *   col_sorted [N*topk]  positions p < M_local as in moe_route (local experts
+ *            in ascending order, token order inside each); p >= M_local: -1
+ *   row_sorted [N*topk]  p for slots in the share, -1 for the others
+ *   gate_scal [N*topk]   topk_w flat[col_sorted[p]] for p < M_local; 0 after
+ *   Needs 0 <= local_offset, 1 <= n_local, local_offset + n_local <= n_experts
+ *   (else MOE_ERR_SHAPE), and the workspace moe_workspace_bytes(n_tokens,
+ *   n_experts, ...) gives.  local_offset = 0, n_local = n_experts gives exactly
+ *   the moe_route result.
+ *
+ * moe_experts_ep: moe_experts over the n_local experts of a share, from a
+ *   moe_route_ep routing: w13 [n_local, ...], w2 [n_local, ...].  out[t] is the
+ *   weighted sum over the token's slots in the share (fp32, slot order); a
+ *   token with none gets a zero row.  n_local may be smaller than topk.
+ *   Workspace: moe_workspace_bytes(n_tokens, n_experts, topk, hidden, inter,
+ *   dtype) with any n_experts >= topk.
+ *
+ * moe_forward_ep: moe_route_ep then moe_experts_ep, on one stream. */
+moe_status_t moe_route_ep(const void *logits, moe_dtype_t logits_dtype, int64_t n_tokens,
+                          int32_t n_experts, int32_t topk, int32_t local_offset, int32_t n_local,
+                          const moe_routing_t *out, void *workspace, size_t ws_bytes,
+                          void *stream);
+moe_status_t moe_experts_ep(const void *x, moe_dtype_t dtype, int64_t n_tokens, int32_t hidden,
+                            const void *w13, const void *w2, int32_t n_local, int32_t inter,
+                            int32_t topk, moe_act_t act, moe_w13_layout_t layout,
+                            const moe_act_params_t *params, const moe_routing_t *routing,
+                            void *out, void *workspace, size_t ws_bytes, void *stream);
+moe_status_t moe_forward_ep(const void *x, const void *logits, moe_dtype_t dtype,
+                            int64_t n_tokens, int32_t hidden, const void *w13, const void *w2,
+                            int32_t n_experts, int32_t local_offset, int32_t n_local,
+                            int32_t inter, int32_t topk, moe_act_t act, moe_w13_layout_t layout,
+                            const moe_act_params_t *params, const moe_routing_t *routing_out,
+                            void *out, void *workspace, size_t ws_bytes, void *stream);
 
 /* Static, human-readable name of a status code. */
 const char *moe_status_str(moe_status_t status);

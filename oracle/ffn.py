@@ -154,5 +154,5 @@ def moe_ffn_share(x, topk_idx, topk_w, w13, w2, act: str, local_offset: int,
     and the masked per-expert loop runs over the local experts, so slots routed
     elsewhere add nothing and a token with none of them gets a zero row."""
     from .routing import remap_to_share
-    loc = remap_to_share(topk_idx, local_offset, np.asarray(w13).shape[0])
+    loc = remap_to_share(topk_idx, local_offset, int(w13.shape[0]))
     return moe_ffn(x, loc, topk_w, w13, w2, act, layout, params, tokens=tokens)

@@ -12,6 +12,14 @@ they raise if the library is missing.
     out, routing = moe_forward(x, logits, w13, w2, topk, act="swiglu_oai",
                                layout="interleaved",
                                params={"alpha": 1.702, "beta": 1.0, "limit": 7.0})
+
+One GPU of an expert-parallel group (experts [lo, lo + n) of the layer's E,
+weights w13 [n, ...], w2 [n, ...]) uses the ``_ep`` variants; summing their
+outputs over the group's shares gives the layer output:
+
+    routing = moe_route_ep(logits, topk, lo, n)
+    out = moe_experts_ep(x, w13, w2, routing, act="silu")
+    out, routing = moe_forward_ep(x, logits, w13, w2, topk, lo, act="silu")
 """
 from __future__ import annotations
 
@@ -26,6 +34,8 @@ from . import _native as N
 __all__ = ["Routing", "MoeError", "Prepared", "moe_route", "moe_experts", "moe_experts_w13",
            "moe_experts_w2", "moe_forward", "prepare_route", "prepare_experts",
            "prepare_experts_w13", "prepare_experts_w2", "prepare_forward",
+           "moe_route_ep", "moe_experts_ep", "moe_forward_ep", "prepare_route_ep",
+           "prepare_experts_ep", "prepare_forward_ep",
            "moe_workspace_bytes", "moe_status_str", "ACTS", "LAYOUTS"]
 
 _DT = {torch.float32: N.MOE_F32, torch.bfloat16: N.MOE_BF16}
@@ -65,8 +75,9 @@ def _dev(*ts: torch.Tensor):
     return dev
 
 
-def _shapes(x, w13, w2, act, out=None, logits=None):
-    """Every buffer size the kernels assume, checked before any launch."""
+def _shapes(x, w13, w2, act, out=None, logits=None, n_experts=None):
+    """Every buffer size the kernels assume, checked before any launch.
+    ``n_experts`` is the logits' expert count when w13/w2 hold only a share."""
     if act not in ACTS:
         raise ValueError(f"unknown activation {act!r}")
     if x.dim() != 2 or w13.dim() != 3 or w2.dim() != 3:
@@ -81,7 +92,8 @@ def _shapes(x, w13, w2, act, out=None, logits=None):
         raise TypeError("x, w13 and w2 must share a dtype")
     if out is not None and (tuple(out.shape) != (n, hidden) or out.dtype != x.dtype):
         raise ValueError("out must be [N, H] in the layer dtype")
-    if logits is not None and (logits.dim() != 2 or tuple(logits.shape) != (n, e)):
+    if logits is not None and (logits.dim() != 2 or
+                               tuple(logits.shape) != (n, e if n_experts is None else n_experts)):
         raise ValueError("logits must be [N, E]")
 
 
@@ -198,20 +210,49 @@ def _nbytes(t: torch.Tensor) -> int:
     return t.numel() * t.element_size()
 
 
+def _share(e: int, local_offset: int, n_local: int):
+    if not (0 <= local_offset and 1 <= n_local and local_offset + n_local <= e):
+        raise ValueError(f"expert share [{local_offset}, {local_offset + n_local}) is not "
+                         f"inside [0, {e})")
+
+
 def prepare_route(logits: torch.Tensor, topk: int, *, routing: Optional[Routing] = None,
-                  workspace: Optional[torch.Tensor] = None, stream=None) -> Prepared:
+                  workspace: Optional[torch.Tensor] = None, stream=None,
+                  _share_of: Optional[tuple] = None) -> Prepared:
     dev = _dev(logits)
     if logits.dim() != 2:
         raise ValueError("logits must be [N, E]")
     n, e = logits.shape
+    lo, nl = _share_of if _share_of is not None else (0, e)
+    _share(e, lo, nl)
     if routing is None:
-        routing = Routing.empty(n, e, topk, logits.dtype, dev)
-    _check_routing(routing, n, e, topk)
+        routing = Routing.empty(n, nl, topk, logits.dtype, dev)
+    _check_routing(routing, n, nl, topk)
     ws = _workspace(workspace, moe_workspace_bytes(n, e, topk, 0, 0, logits.dtype), dev)
     r = routing.as_c()
-    args = (logits.data_ptr(), _dt(logits), n, e, topk, ctypes.byref(r), ws.data_ptr(),
+    if _share_of is None:
+        args = (logits.data_ptr(), _dt(logits), n, e, topk, ctypes.byref(r), ws.data_ptr(),
+                _nbytes(ws), _stream(dev, stream))
+        return Prepared("moe_route", args, (r, logits, ws, routing), routing)
+    args = (logits.data_ptr(), _dt(logits), n, e, topk, lo, nl, ctypes.byref(r), ws.data_ptr(),
             _nbytes(ws), _stream(dev, stream))
-    return Prepared("moe_route", args, (r, logits, ws, routing), routing)
+    return Prepared("moe_route_ep", args, (r, logits, ws, routing), routing)
+
+
+def prepare_route_ep(logits: torch.Tensor, topk: int, local_offset: int, n_local: int, *,
+                     routing: Optional[Routing] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> Prepared:
+    return prepare_route(logits, topk, routing=routing, workspace=workspace, stream=stream,
+                         _share_of=(local_offset, n_local))
+
+
+def moe_route_ep(logits: torch.Tensor, topk: int, local_offset: int, n_local: int, *,
+                 routing: Optional[Routing] = None, workspace: Optional[torch.Tensor] = None,
+                 stream=None) -> Routing:
+    """Routing for the expert share [local_offset, local_offset + n_local) of
+    ``logits [N, E]``: global top-k, metadata over the local experts (moe.h)."""
+    return prepare_route_ep(logits, topk, local_offset, n_local, routing=routing,
+                            workspace=workspace, stream=stream)()
 
 
 def moe_route(logits: torch.Tensor, topk: int, *, routing: Optional[Routing] = None,
@@ -222,7 +263,7 @@ def moe_route(logits: torch.Tensor, topk: int, *, routing: Optional[Routing] = N
 
 def prepare_experts(x, w13, w2, routing: Routing, act: str, layout: str = "packed",
                     params: Optional[dict] = None, *, out=None, workspace=None,
-                    stream=None) -> Prepared:
+                    stream=None, _ep: bool = False) -> Prepared:
     dev = _dev(x, w13, w2)
     _shapes(x, w13, w2, act, out)
     n, hidden = x.shape
@@ -231,13 +272,33 @@ def prepare_experts(x, w13, w2, routing: Routing, act: str, layout: str = "packe
     _check_routing(routing, n, e, k)
     if out is None:
         out = torch.empty_like(x)
-    ws = _workspace(workspace, moe_workspace_bytes(n, e, k, hidden, inter, x.dtype), dev)
+    # the experts' workspace does not depend on the expert count (any E >= k)
+    ws = _workspace(workspace, moe_workspace_bytes(n, max(e, k), k, hidden, inter, x.dtype),
+                    dev)
     r = routing.as_c()
     p = _params(params)
     args = (x.data_ptr(), _dt(x), n, hidden, w13.data_ptr(), w2.data_ptr(), e, inter, k,
             ACTS[act], LAYOUTS[layout], ctypes.byref(p) if p else None, ctypes.byref(r),
             out.data_ptr(), ws.data_ptr(), _nbytes(ws), _stream(dev, stream))
-    return Prepared("moe_experts", args, (r, p, x, w13, w2, out, ws, routing), out)
+    return Prepared("moe_experts_ep" if _ep else "moe_experts", args,
+                    (r, p, x, w13, w2, out, ws, routing), out)
+
+
+def prepare_experts_ep(x, w13, w2, routing: Routing, act: str, layout: str = "packed",
+                       params: Optional[dict] = None, *, out=None, workspace=None,
+                       stream=None) -> Prepared:
+    return prepare_experts(x, w13, w2, routing, act, layout, params, out=out,
+                           workspace=workspace, stream=stream, _ep=True)
+
+
+def moe_experts_ep(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, routing: Routing,
+                   act: str, layout: str = "packed", params: Optional[dict] = None, *,
+                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                   stream=None) -> torch.Tensor:
+    """Expert FFN of one expert share (w13/w2 hold its n_local experts) from a
+    moe_route_ep routing; tokens with no slot in the share get zero rows."""
+    return prepare_experts_ep(x, w13, w2, routing, act, layout, params, out=out,
+                              workspace=workspace, stream=stream)()
 
 
 def moe_experts(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor, routing: Routing,
@@ -329,6 +390,44 @@ def prepare_forward(x, logits, w13, w2, topk: int, act: str, layout: str = "pack
             ctypes.byref(r), out.data_ptr(), ws.data_ptr(), _nbytes(ws), _stream(dev, stream))
     return Prepared("moe_forward", args, (r, p, x, logits, w13, w2, out, ws, routing),
                     (out, routing))
+
+
+def prepare_forward_ep(x, logits, w13, w2, topk: int, local_offset: int, act: str,
+                       layout: str = "packed", params: Optional[dict] = None, *, out=None,
+                       routing=None, workspace=None, stream=None) -> Prepared:
+    dev = _dev(x, logits, w13, w2)
+    n, hidden = x.shape
+    e = logits.shape[1]
+    nl, inter = w2.shape[0], w2.shape[2]
+    _shapes(x, w13, w2, act, out, logits, n_experts=e)
+    _share(e, local_offset, nl)
+    if logits.dtype != x.dtype:
+        raise TypeError("moe_forward_ep takes logits in the layer dtype")
+    if routing is None:
+        routing = Routing.empty(n, nl, topk, logits.dtype, dev)
+    _check_routing(routing, n, nl, topk)
+    if out is None:
+        out = torch.empty_like(x)
+    ws = _workspace(workspace, moe_workspace_bytes(n, e, topk, hidden, inter, x.dtype), dev)
+    r = routing.as_c()
+    p = _params(params)
+    args = (x.data_ptr(), logits.data_ptr(), _dt(x), n, hidden, w13.data_ptr(), w2.data_ptr(),
+            e, local_offset, nl, inter, topk, ACTS[act], LAYOUTS[layout],
+            ctypes.byref(p) if p else None, ctypes.byref(r), out.data_ptr(), ws.data_ptr(),
+            _nbytes(ws), _stream(dev, stream))
+    return Prepared("moe_forward_ep", args, (r, p, x, logits, w13, w2, out, ws, routing),
+                    (out, routing))
+
+
+def moe_forward_ep(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor,
+                   topk: int, local_offset: int, act: str, layout: str = "packed",
+                   params: Optional[dict] = None, *, out: Optional[torch.Tensor] = None,
+                   routing: Optional[Routing] = None, workspace: Optional[torch.Tensor] = None,
+                   stream=None):
+    """moe_route_ep then moe_experts_ep for the share of w13/w2's experts that
+    starts at ``local_offset``; returns ``(out, routing)``."""
+    return prepare_forward_ep(x, logits, w13, w2, topk, local_offset, act, layout, params,
+                              out=out, routing=routing, workspace=workspace, stream=stream)()
 
 
 def moe_forward(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor,

@@ -6,7 +6,9 @@
 // index_add_ uses atomics on the GPU when k > 1; here each thread owns one
 // 16-byte chunk of one output row and sums the k chunks in slot order in fp32,
 // so the result is deterministic.  The loads are 16-byte vectors; each token
-// row is read from k places and written once (HBM bound).
+// row is read from k places and written once (HBM bound).  A slot with
+// row_sorted = -1 (its expert is outside this GPU's expert-parallel share)
+// adds nothing; a token with no slot in the share gets a zero row.
 #include "moe_common.h"
 
 namespace moe {
@@ -53,12 +55,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y,
   for (int i = 0; i < CH; ++i) acc[i] = 0.f;
   for (int j = 0; j < K; ++j) {
     const int64_t p = row_sorted[t * K + j];
-    add_chunk(acc, *reinterpret_cast<const u32x4_t *>(y + p * H + (int64_t)c * CH), T());
+    if (p >= 0) add_chunk(acc, *reinterpret_cast<const u32x4_t *>(y + p * H + (int64_t)c * CH), T());
   }
   *reinterpret_cast<u32x4_t *>(out + t * H + (int64_t)c * CH) = pack_chunk(acc, T());
 }
 
+// Top-1 layer of an expert-parallel share: GEMM2 writes the rows of tokens
+// whose expert is local; this kernel writes zero rows for the others
+// (row_sorted = -1).  The two write disjoint rows, so their order is free.
+__global__ __launch_bounds__(256) void zero_unrouted_kernel(const int32_t *__restrict__ row_sorted,
+                                                            u32x4_t *__restrict__ out, int64_t N,
+                                                            int nch) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= N * nch) return;
+  const int64_t t = idx / nch;
+  if (row_sorted[t] < 0) out[idx] = u32x4_t{0u, 0u, 0u, 0u};
+}
+
 }  // namespace
+
+hipError_t launch_zero_unrouted(const int32_t *row_sorted, void *out, moe_dtype_t dt,
+                                int64_t n_tokens, int hidden, hipStream_t s) {
+  const int nch = hidden / (dt == MOE_BF16 ? 8 : 4);  // 16-byte chunks per row
+  const int64_t total = n_tokens * nch;
+  hipLaunchKernelGGL(zero_unrouted_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                     row_sorted, reinterpret_cast<u32x4_t *>(out), n_tokens, nch);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const void *y_sorted, const int32_t *row_sorted, void *out,
                           moe_dtype_t dt, int64_t n_tokens, int topk, int hidden, hipStream_t s) {

@@ -16,9 +16,10 @@ inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 inline bool dtype_ok(int d) { return d == MOE_F32 || d == MOE_BF16; }
 inline size_t dsize(int d) { return d == MOE_BF16 ? 2 : 4; }
 
-// Sizes shared by all entry points.
-moe_status_t check_sizes(int64_t n, int32_t e, int32_t k) {
-  if (n < 0 || e < 1 || e > moe::kMaxExperts || k < 1 || k > moe::kMaxTopk || k > e)
+// Sizes shared by all entry points.  An expert-parallel share may hold fewer
+// experts than a token selects (k_le_e = false for its expert count).
+moe_status_t check_sizes(int64_t n, int32_t e, int32_t k, bool k_le_e = true) {
+  if (n < 0 || e < 1 || e > moe::kMaxExperts || k < 1 || k > moe::kMaxTopk || (k_le_e && k > e))
     return MOE_ERR_SHAPE;
   if (n > (int64_t)0x7fffffff / k) return MOE_ERR_SHAPE;
   return MOE_OK;
@@ -85,8 +86,8 @@ moe_status_t act_params(moe_act_t act, moe_w13_layout_t layout, const moe_act_pa
 moe_status_t check_expert_args(moe_dtype_t dtype, int64_t n, int32_t hidden, int32_t e,
                                int32_t inter, int32_t k, moe_act_t act, moe_w13_layout_t layout,
                                const moe_act_params_t *params, const moe_routing_t *routing,
-                               ActParams *prm) {
-  moe_status_t st = check_sizes(n, e, k);
+                               ActParams *prm, bool share = false) {
+  moe_status_t st = check_sizes(n, e, k, !share);
   if (st != MOE_OK) return st;
   if ((st = check_ffn_sizes(hidden, inter)) != MOE_OK) return st;
   if (!dtype_ok(dtype)) return MOE_ERR_DTYPE;
@@ -123,9 +124,9 @@ moe_status_t check_experts(const void *x, moe_dtype_t dtype, int64_t n, int32_t 
                            const void *w13, const void *w2, int32_t e, int32_t inter, int32_t k,
                            moe_act_t act, moe_w13_layout_t layout, const moe_act_params_t *params,
                            const moe_routing_t *routing, void *out, void *ws, size_t ws_bytes,
-                           ActParams *prm) {
+                           ActParams *prm, bool share = false) {
   moe_status_t st = check_expert_args(dtype, n, hidden, e, inter, k, act, layout, params,
-                                      routing, prm);
+                                      routing, prm, share);
   if (st != MOE_OK || n == 0) return st;
   if ((st = check_ptrs({x, w13, w2, out})) != MOE_OK) return st;
   return check_ws(ws, ws_bytes, experts_ws_bytes(n, k, hidden, inter, dtype));
@@ -147,6 +148,12 @@ moe_status_t check_route(const void *logits, moe_dtype_t dt, int64_t n, int32_t 
   return MOE_OK;
 }
 
+// The expert-parallel share [lo, lo + nl) must lie inside [0, e).
+moe_status_t check_share(int32_t e, int32_t lo, int32_t nl) {
+  if (lo < 0 || nl < 1 || lo > e - nl) return MOE_ERR_SHAPE;
+  return MOE_OK;
+}
+
 hipError_t run_w13(const void *x, moe_dtype_t dtype, int64_t n, int32_t hidden, const void *w13,
                    int32_t e, int32_t inter, int32_t k, moe_act_t act, moe_w13_layout_t layout,
                    const ActParams &prm, const moe_routing_t *r, void *a, hipStream_t s) {
@@ -156,26 +163,30 @@ hipError_t run_w13(const void *x, moe_dtype_t dtype, int64_t n, int32_t hidden, 
 
 hipError_t run_w2(const void *a, moe_dtype_t dtype, int64_t n, int32_t hidden, const void *w2,
                   int32_t e, int32_t inter, int32_t k, const moe_routing_t *r, void *out, void *y,
-                  hipStream_t s) {
+                  hipStream_t s, bool share = false) {
   const bool direct = k == 1;  // one row per token: GEMM2 writes the output rows itself
   hipError_t err = moe::launch_gemm2(a, w2, direct ? out : y, r->offsets, r->col_sorted,
                                      r->gate_scal, (moe_dtype_t)r->w_dtype, dtype, n, k, e,
                                      hidden, inter, direct, s);
-  if (err != hipSuccess || direct) return err;
+  if (err != hipSuccess) return err;
+  // an expert share leaves the rows of tokens routed elsewhere to be zeroed
+  if (direct) return share ? moe::launch_zero_unrouted(r->row_sorted, out, dtype, n, hidden, s)
+                           : err;
   return moe::launch_combine(y, r->row_sorted, out, dtype, n, k, hidden, s);
 }
 
 moe_status_t run_experts(const void *x, moe_dtype_t dtype, int64_t n, int32_t hidden,
                          const void *w13, const void *w2, int32_t e, int32_t inter, int32_t k,
                          moe_act_t act, moe_w13_layout_t layout, const ActParams &prm,
-                         const moe_routing_t *r, void *out, void *ws, hipStream_t s) {
+                         const moe_routing_t *r, void *out, void *ws, hipStream_t s,
+                         bool share = false) {
   // workspace: activation rows a[M, inter], then (topk > 1) weighted rows y[M, hidden]
   char *base = reinterpret_cast<char *>(ws);
   void *a = base;
   void *y = base + align256((size_t)n * k * inter * dsize(dtype));
   if (run_w13(x, dtype, n, hidden, w13, e, inter, k, act, layout, prm, r, a, s) != hipSuccess)
     return MOE_ERR_HIP;
-  if (run_w2(a, dtype, n, hidden, w2, e, inter, k, r, out, y, s) != hipSuccess)
+  if (run_w2(a, dtype, n, hidden, w2, e, inter, k, r, out, y, s, share) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }
@@ -203,8 +214,8 @@ moe_status_t moe_route(const void *logits, moe_dtype_t logits_dtype, int64_t n_t
   moe_status_t st =
       check_route(logits, logits_dtype, n_tokens, n_experts, topk, out, workspace, ws_bytes);
   if (st != MOE_OK || n_tokens == 0) return st;
-  if (moe::launch_route(logits, logits_dtype, n_tokens, n_experts, topk, out, workspace,
-                        (hipStream_t)stream) != hipSuccess)
+  if (moe::launch_route(logits, logits_dtype, n_tokens, n_experts, topk, 0, n_experts, out,
+                        workspace, (hipStream_t)stream) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }
@@ -270,11 +281,60 @@ moe_status_t moe_forward(const void *x, const void *logits, moe_dtype_t dtype, i
   hipStream_t s = (hipStream_t)stream;
   // the routing scratch is dead once the routing kernels ran (stream order), so
   // the expert intermediates reuse the same workspace bytes
-  if (moe::launch_route(logits, dtype, n_tokens, n_experts, topk, routing_out, workspace, s) !=
-      hipSuccess)
+  if (moe::launch_route(logits, dtype, n_tokens, n_experts, topk, 0, n_experts, routing_out,
+                        workspace, s) != hipSuccess)
     return MOE_ERR_HIP;
   return run_experts(x, dtype, n_tokens, hidden, w13, w2, n_experts, inter, topk, act, layout,
                      prm, routing_out, out, workspace, s);
+}
+
+moe_status_t moe_route_ep(const void *logits, moe_dtype_t logits_dtype, int64_t n_tokens,
+                          int32_t n_experts, int32_t topk, int32_t local_offset, int32_t n_local,
+                          const moe_routing_t *out, void *workspace, size_t ws_bytes,
+                          void *stream) {
+  moe_status_t st = check_share(n_experts, local_offset, n_local);
+  if (st != MOE_OK) return st;
+  st = check_route(logits, logits_dtype, n_tokens, n_experts, topk, out, workspace, ws_bytes);
+  if (st != MOE_OK || n_tokens == 0) return st;
+  if (moe::launch_route(logits, logits_dtype, n_tokens, n_experts, topk, local_offset, n_local,
+                        out, workspace, (hipStream_t)stream) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status_t moe_experts_ep(const void *x, moe_dtype_t dtype, int64_t n_tokens, int32_t hidden,
+                            const void *w13, const void *w2, int32_t n_local, int32_t inter,
+                            int32_t topk, moe_act_t act, moe_w13_layout_t layout,
+                            const moe_act_params_t *params, const moe_routing_t *routing,
+                            void *out, void *workspace, size_t ws_bytes, void *stream) {
+  ActParams prm;
+  moe_status_t st = check_experts(x, dtype, n_tokens, hidden, w13, w2, n_local, inter, topk, act,
+                                  layout, params, routing, out, workspace, ws_bytes, &prm, true);
+  if (st != MOE_OK || n_tokens == 0) return st;
+  return run_experts(x, dtype, n_tokens, hidden, w13, w2, n_local, inter, topk, act, layout, prm,
+                     routing, out, workspace, (hipStream_t)stream, true);
+}
+
+moe_status_t moe_forward_ep(const void *x, const void *logits, moe_dtype_t dtype,
+                            int64_t n_tokens, int32_t hidden, const void *w13, const void *w2,
+                            int32_t n_experts, int32_t local_offset, int32_t n_local,
+                            int32_t inter, int32_t topk, moe_act_t act, moe_w13_layout_t layout,
+                            const moe_act_params_t *params, const moe_routing_t *routing_out,
+                            void *out, void *workspace, size_t ws_bytes, void *stream) {
+  ActParams prm;
+  moe_status_t st = check_share(n_experts, local_offset, n_local);
+  if (st != MOE_OK) return st;
+  st = check_route(logits, dtype, n_tokens, n_experts, topk, routing_out, workspace, ws_bytes);
+  if (st != MOE_OK) return st;
+  st = check_experts(x, dtype, n_tokens, hidden, w13, w2, n_local, inter, topk, act, layout,
+                     params, routing_out, out, workspace, ws_bytes, &prm, true);
+  if (st != MOE_OK || n_tokens == 0) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (moe::launch_route(logits, dtype, n_tokens, n_experts, topk, local_offset, n_local,
+                        routing_out, workspace, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return run_experts(x, dtype, n_tokens, hidden, w13, w2, n_local, inter, topk, act, layout, prm,
+                     routing_out, out, workspace, s, true);
 }
 
 const char *moe_status_str(moe_status_t status) {

@@ -44,8 +44,11 @@ constexpr int kRouteThreads = 256;
 constexpr int kRouteTokens = 256;  // tokens per routing block (one per thread in the rank phase)
 
 size_t route_scratch_bytes(int64_t n_tokens, int n_experts, int topk);
+// Routing for the expert share [local_offset, local_offset + n_local) of the
+// n_experts (0 and n_experts for the whole layer).
 hipError_t launch_route(const void *logits, moe_dtype_t dt, int64_t n_tokens, int n_experts,
-                        int topk, const moe_routing_t *r, void *scratch, hipStream_t s);
+                        int topk, int local_offset, int n_local, const moe_routing_t *r,
+                        void *scratch, hipStream_t s);
 
 struct ActParams {
   float alpha, beta, limit;
@@ -62,7 +65,11 @@ hipError_t launch_gemm2(const void *act_in, const void *w2, void *y, const int32
                         const int32_t *col_sorted, const void *gate_scal, moe_dtype_t gate_dt,
                         moe_dtype_t dt, int64_t n_tokens, int topk, int n_experts, int hidden,
                         int inter, bool direct_out, hipStream_t s);
-// out[t] = sum_j y_sorted[row_sorted[t*topk + j]] (fp32, slot order).
+// out[t] = sum_j y_sorted[row_sorted[t*topk + j]] (fp32, slot order), slots
+// with row_sorted = -1 skipped.
 hipError_t launch_combine(const void *y_sorted, const int32_t *row_sorted, void *out,
                           moe_dtype_t dt, int64_t n_tokens, int topk, int hidden, hipStream_t s);
+// topk == 1: out[t] = 0 where row_sorted[t] = -1.
+hipError_t launch_zero_unrouted(const int32_t *row_sorted, void *out, moe_dtype_t dt,
+                                int64_t n_tokens, int hidden, hipStream_t s);
 }  // namespace moe

@@ -25,6 +25,18 @@
 //  * route_fused: batches of up to 256 tokens run both phases in one
 //    workgroup of 1024 threads with every per-entry value kept in LDS (one
 //    launch for the whole routing step).
+//
+// Expert-parallel share: every kernel takes the share [lo, lo + nl) of the E
+// experts that this GPU holds (lo = 0, nl = E for the whole layer).  Top-k and
+// softmax run over all E logits; the selected ids are then remapped to local
+// ids e - lo, and the bitmatrix, counts, ranks, offsets and sorted indices are
+// over the nl local experts only.  A slot whose expert lies outside the share
+// gets row_sorted = -1 and no sorted position; sorted positions past the last
+// local entry get col_sorted = -1 and gate weight 0.  The remap and re-packing
+// of the bitmatrix follow the expert-map branch described in the vLLM PR
+// #45457 report ("implementation breakdown"), with the share given as the
+// (local_expert_offset, num_local_experts) pair of the kernel call in the PR
+// #47106 report ("key source snippets").
 #include "moe_common.h"
 
 namespace moe {
@@ -171,7 +183,7 @@ template <typename T, int NT, int MAXE = kMaxExperts, int MAXK = kMaxTopk> struc
 // fewer VALU lane-operations per selection round, so wide expert sets use C = 2.
 template <typename T, int THREADS, int C, typename Lds>
 __device__ __forceinline__ void topk_chunk(const T *__restrict__ logits, int64_t N, int E, int K,
-                                           int logG, int vec, int64_t tok0,
+                                           int lo, int nl, int logG, int vec, int64_t tok0,
                                            int32_t *__restrict__ topk_idx,
                                            T *__restrict__ topk_w,
                                            uint32_t *__restrict__ bitmatrix, Lds &L) {
@@ -183,7 +195,7 @@ __device__ __forceinline__ void topk_chunk(const T *__restrict__ logits, int64_t
   const int G = 1 << logG;
   const int tpp = 64 >> logG;  // tokens per wave pass
   const int grp = lane >> logG, lg = lane & (G - 1);
-  const int words = (E + 31) >> 5;
+  const int words = (nl + 31) >> 5;  // bitmatrix words over the local experts
   // Tokens are dealt round-robin over the NW = THREADS / 64 waves: pass p of
   // wave w, group grp holds chunk token (p * tpp + grp) * NW + w, so a small
   // batch still spreads over every wave, and many waves per SIMD overlap the
@@ -230,7 +242,7 @@ __device__ __forceinline__ void topk_chunk(const T *__restrict__ logits, int64_t
         }
         // k rounds: the group's largest remaining key; its owner clears it.
         // Slot j's expert and logit go to LDS (the group's lanes share them).
-        uint32_t word = 0;  // bitmatrix word lg of this token
+        uint32_t word = 0;  // bitmatrix word lg of this token (local expert ids)
         for (int j = 0; j < K; ++j) {
           Key m = key[0];
 #pragma unroll
@@ -240,7 +252,8 @@ __device__ __forceinline__ void topk_chunk(const T *__restrict__ logits, int64_t
 #pragma unroll
           for (int i = 0; i < C * V; ++i)
             if (e0 + i == e) key[i] = 0;  // only the owning lane matches
-          if ((e >> 5) == lg) word |= 1u << (e & 31);
+          const int l = e - lo;
+          if ((unsigned)l < (unsigned)nl && (l >> 5) == lg) word |= 1u << (l & 31);
           if (lg == 0 && inwave) {
             L.sel[tl * K + j] = (uint8_t)e;
             L.val[tl * K + j] = Lg::value(m);
@@ -349,7 +362,7 @@ __device__ __forceinline__ int chunk_rank(const Lds &L, int t, int e) {
 // value stays in LDS; the scan and the scatter follow the rank phase directly.
 template <typename T, int THREADS, int C, typename Lds>
 __global__ __launch_bounds__(THREADS) void route_fused(
-    const T *__restrict__ logits, int64_t N, int E, int K, int logG, int vec,
+    const T *__restrict__ logits, int64_t N, int E, int K, int lo, int nl, int logG, int vec,
     int32_t *__restrict__ topk_idx, T *__restrict__ topk_w, uint32_t *__restrict__ bitmatrix,
     int32_t *__restrict__ col_sum, int32_t *__restrict__ offsets,
     int32_t *__restrict__ col_sorted, int32_t *__restrict__ row_sorted,
@@ -359,25 +372,37 @@ __global__ __launch_bounds__(THREADS) void route_fused(
   __shared__ uint16_t s_rank[NT * Lds::kSlots];
   __shared__ int s_off[Lds::kExperts + 1];
   const int tid = threadIdx.x;
-  topk_chunk<T, THREADS, C>(logits, N, E, K, logG, vec, 0, topk_idx, topk_w, bitmatrix, L);
+  topk_chunk<T, THREADS, C>(logits, N, E, K, lo, nl, logG, vec, 0, topk_idx, topk_w, bitmatrix,
+                            L);
   __syncthreads();
-  rank_chunk<THREADS>(E, (int)N, L);
+  rank_chunk<THREADS>(nl, (int)N, L);
   for (int t = tid; t < N; t += THREADS) {
 #pragma unroll
-    for (int j = 0; j < Lds::kSlots; ++j)
-      if (j < K) s_rank[t * K + j] = (uint16_t)chunk_rank(L, t, L.sel[t * K + j]);
+    for (int j = 0; j < Lds::kSlots; ++j) {
+      const int l = (int)L.sel[t * K + j] - lo;
+      if (j < K && (unsigned)l < (unsigned)nl) s_rank[t * K + j] = (uint16_t)chunk_rank(L, t, l);
+    }
   }
-  block_exclusive_scan(L.tot, s_off, E);  // synchronises
-  for (int e = tid; e <= E; e += THREADS) {
+  block_exclusive_scan(L.tot, s_off, nl);  // synchronises
+  for (int e = tid; e <= nl; e += THREADS) {
     offsets[e] = s_off[e];
-    if (e < E) col_sum[e] = L.tot[e];
+    if (e < nl) col_sum[e] = L.tot[e];
   }
-  const int M = (int)N * K;
+  const int M = (int)N * K, m_local = s_off[nl];
   for (int f = tid; f < M; f += THREADS) {
-    const int p = s_off[L.sel[f]] + s_rank[f];
-    col_sorted[p] = f;
-    row_sorted[f] = p;
-    gate_scal[p] = L.w[f];
+    const int l = (int)L.sel[f] - lo;
+    if ((unsigned)l < (unsigned)nl) {
+      const int p = s_off[l] + s_rank[f];
+      col_sorted[p] = f;
+      row_sorted[f] = p;
+      gate_scal[p] = L.w[f];
+    } else {
+      row_sorted[f] = -1;
+    }
+  }
+  for (int p = m_local + tid; p < M; p += THREADS) {
+    col_sorted[p] = -1;
+    gate_scal[p] = from_f32<T>(0.f);
   }
 }
 
@@ -387,23 +412,29 @@ constexpr int kTopkThreads = 1024;
 
 template <typename T, int C>
 __global__ __launch_bounds__(kTopkThreads) void route_topk_rank(
-    const T *__restrict__ logits, int64_t N, int E, int K, int logG, int vec,
+    const T *__restrict__ logits, int64_t N, int E, int K, int lo, int nl, int logG, int vec,
     int32_t *__restrict__ topk_idx, T *__restrict__ topk_w, uint32_t *__restrict__ bitmatrix,
     int32_t *__restrict__ blk_cnt, int nbp, uint8_t *__restrict__ blk_rank) {
   __shared__ ChunkLds<T, kRouteTokens> L;
   const int tid = threadIdx.x;
   const int64_t tok0 = (int64_t)blockIdx.x * kRouteTokens;
-  topk_chunk<T, kTopkThreads, C>(logits, N, E, K, logG, vec, tok0, topk_idx, topk_w, bitmatrix, L);
+  topk_chunk<T, kTopkThreads, C>(logits, N, E, K, lo, nl, logG, vec, tok0, topk_idx, topk_w,
+                                 bitmatrix, L);
   __syncthreads();
-  rank_chunk<kTopkThreads>(E, (int)min<int64_t>(kRouteTokens, N - tok0), L);
+  rank_chunk<kTopkThreads>(nl, (int)min<int64_t>(kRouteTokens, N - tok0), L);
   const int64_t t = tok0 + tid;
   if (tid < kRouteTokens && t < N) {
 #pragma unroll
-    for (int j = 0; j < kMaxTopk; ++j)
-      if (j < K) blk_rank[t * K + j] = (uint8_t)chunk_rank(L, tid, L.sel[tid * K + j]);
+    for (int j = 0; j < kMaxTopk; ++j) {
+      if (j < K) {
+        // slots outside the share get rank 0; the scatter never places them
+        const int l = (int)L.sel[tid * K + j] - lo;
+        blk_rank[t * K + j] = (unsigned)l < (unsigned)nl ? (uint8_t)chunk_rank(L, tid, l) : 0;
+      }
+    }
   }
   // expert-major, row stride nbp (a multiple of 4): the scatter sums rows
-  for (int e = tid; e < E; e += kTopkThreads) blk_cnt[(int64_t)e * nbp + blockIdx.x] = L.tot[e];
+  for (int e = tid; e < nl; e += kTopkThreads) blk_cnt[(int64_t)e * nbp + blockIdx.x] = L.tot[e];
 }
 
 // Multi-block path, kernel 2: workgroup b scatters routing block b.  It sums
@@ -416,7 +447,7 @@ constexpr int kScatterThreads = 1024;
 
 template <typename T>
 __global__ __launch_bounds__(kScatterThreads) void route_scatter(
-    int64_t N, int E, int K, int nblocks, int nbp, const int32_t *__restrict__ blk_cnt,
+    int64_t N, int K, int lo, int nl, int nblocks, int nbp, const int32_t *__restrict__ blk_cnt,
     const uint8_t *__restrict__ blk_rank, const int32_t *__restrict__ topk_idx,
     const T *__restrict__ topk_w, int32_t *__restrict__ col_sum, int32_t *__restrict__ offsets,
     int32_t *__restrict__ col_sorted, int32_t *__restrict__ row_sorted,
@@ -439,13 +470,14 @@ __global__ __launch_bounds__(kScatterThreads) void route_scatter(
 #pragma unroll
     for (int j = 0; j < kMaxTopk; ++j) {
       if (j < K) {
-        ex[j] = topk_idx[t * K + j];
+        ex[j] = topk_idx[t * K + j] - lo;  // local id; outside the share if not in [0, nl)
         rk[j] = blk_rank[t * K + j];
         w[j] = topk_w[t * K + j];
       }
     }
   }
   // thread (e, part): part-th share of row e, in 4-int chunks
+  const int E = nl;  // counts, offsets and positions are over the local experts
   const int parts = min(kParts, kScatterThreads / E);
   const int e = tid % E, part = tid / E;
   const int nch = nbp / 4;                       // 16-byte chunks per row
@@ -496,12 +528,25 @@ __global__ __launch_bounds__(kScatterThreads) void route_scatter(
 #pragma unroll
     for (int j = 0; j < kMaxTopk; ++j) {
       if (j < K) {
-        const int p = s_base[ex[j]] + rk[j];
-        col_sorted[p] = (int32_t)(t * K + j);
-        row_sorted[t * K + j] = p;
-        gate_scal[p] = w[j];
+        if ((unsigned)ex[j] < (unsigned)E) {
+          const int p = s_base[ex[j]] + rk[j];
+          col_sorted[p] = (int32_t)(t * K + j);
+          row_sorted[t * K + j] = p;
+          gate_scal[p] = w[j];
+        } else {
+          row_sorted[t * K + j] = -1;
+        }
       }
     }
+  }
+  // sorted positions past the local entries: this block clears its share of
+  // [m_local, N*K), the positions [b*256*K, (b+1)*256*K)
+  const int64_t M = N * K, m_local = s_off[E];
+  const int64_t p_end = min(M, ((int64_t)b + 1) * kRouteTokens * K);
+  for (int64_t p = max(m_local, (int64_t)b * kRouteTokens * K) + tid; p < p_end;
+       p += kScatterThreads) {
+    col_sorted[p] = -1;
+    gate_scal[p] = from_f32<T>(0.f);
   }
 }
 
@@ -520,8 +565,8 @@ inline RoutePath route_path(int64_t N, int E, int K) {
 }
 
 template <typename T>
-hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, const moe_routing_t *r,
-                          void *scratch, hipStream_t s) {
+hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int nl,
+                          const moe_routing_t *r, void *scratch, hipStream_t s) {
   constexpr int V = Logit<T>::kVec;
   // two chunks a lane when one would need more than 8 lanes a token, unless the
   // batch is so small that spreading it over more lanes matters more
@@ -537,11 +582,11 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, const moe_ro
   if (path == kPathFused) {
     if (wide)
       hipLaunchKernelGGL((route_fused<T, 1024, 2, ChunkLds<T, kFusedTokens>>), dim3(1), dim3(1024),
-                         0, s, logits, N, E, K, logG, vec, r->topk_idx, tw, r->bitmatrix,
+                         0, s, logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw, r->bitmatrix,
                          r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs);
     else
       hipLaunchKernelGGL((route_fused<T, 1024, 1, ChunkLds<T, kFusedTokens>>), dim3(1), dim3(1024),
-                         0, s, logits, N, E, K, logG, vec, r->topk_idx, tw, r->bitmatrix,
+                         0, s, logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw, r->bitmatrix,
                          r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs);
     return hipGetLastError();
   }
@@ -551,14 +596,14 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, const moe_ro
   uint8_t *blk_rank = reinterpret_cast<uint8_t *>(scratch) + align256((size_t)nbp * E * 4);
   if (wide)
     hipLaunchKernelGGL((route_topk_rank<T, 2>), dim3((unsigned)nb), dim3(kTopkThreads), 0, s,
-                       logits, N, E, K, logG, vec, r->topk_idx, tw, r->bitmatrix, blk_cnt, nbp,
+                       logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw, r->bitmatrix, blk_cnt, nbp,
                        blk_rank);
   else
     hipLaunchKernelGGL((route_topk_rank<T, 1>), dim3((unsigned)nb), dim3(kTopkThreads), 0, s,
-                       logits, N, E, K, logG, vec, r->topk_idx, tw, r->bitmatrix, blk_cnt, nbp,
+                       logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw, r->bitmatrix, blk_cnt, nbp,
                        blk_rank);
-  hipLaunchKernelGGL(route_scatter<T>, dim3((unsigned)nb), dim3(kScatterThreads), 0, s, N, E, K,
-                     (int)nb, nbp, blk_cnt, blk_rank, r->topk_idx, tw, r->col_sum, r->offsets,
+  hipLaunchKernelGGL(route_scatter<T>, dim3((unsigned)nb), dim3(kScatterThreads), 0, s, N, K, lo,
+                     nl, (int)nb, nbp, blk_cnt, blk_rank, r->topk_idx, tw, r->col_sum, r->offsets,
                      r->col_sorted, r->row_sorted, gs);
   return hipGetLastError();
 }
@@ -573,12 +618,13 @@ size_t route_scratch_bytes(int64_t n_tokens, int n_experts, int topk) {
 }
 
 hipError_t launch_route(const void *logits, moe_dtype_t dt, int64_t n_tokens, int n_experts,
-                        int topk, const moe_routing_t *r, void *scratch, hipStream_t s) {
+                        int topk, int local_offset, int n_local, const moe_routing_t *r,
+                        void *scratch, hipStream_t s) {
   if (dt == MOE_BF16)
     return launch_route_t<bf16_t>(reinterpret_cast<const bf16_t *>(logits), n_tokens, n_experts,
-                                  topk, r, scratch, s);
+                                  topk, local_offset, n_local, r, scratch, s);
   return launch_route_t<float>(reinterpret_cast<const float *>(logits), n_tokens, n_experts,
-                               topk, r, scratch, s);
+                               topk, local_offset, n_local, r, scratch, s);
 }
 
 }  // namespace moe

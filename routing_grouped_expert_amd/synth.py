@@ -17,6 +17,10 @@ then rounded to the layer dtype with torch's round-to-nearest-even cast):
    ``-s * ln(perm[e] + 1)`` (a Zipf(s) prior in log space over a seeded rank
    permutation), added to the logits before rounding.
 
+Expert-parallel share layers (``n_local`` set) draw the logits over all E
+experts and the weights (steps 3-4) for their ``n_local`` experts only: one
+GPU's share [local_offset, local_offset + n_local) of a layer.
+
 ``w13`` is built from the same gate/up draws in either layout: packed rows
 ``[gate; up]`` or interleaved rows ``[g0, u0, g1, u1, ...]``, the two gated
 layouts described in the vLLM PR #47106 report (section on the w13 reorder
@@ -53,6 +57,13 @@ class LayerSpec:
     limit: Optional[float] = None
     zipf_s: Optional[float] = None   # skewed logit bias strength
     seed: int = 0
+    local_offset: int = 0            # expert-parallel share: first local expert
+    n_local: Optional[int] = None    # share size; None -> the whole layer
+
+    @property
+    def n_weights(self) -> int:
+        """Experts whose weights this GPU holds."""
+        return self.n_experts if self.n_local is None else self.n_local
 
     @property
     def gated(self) -> bool:
@@ -158,15 +169,16 @@ def make_layer(spec: LayerSpec, keep_parts: bool = False) -> Layer:
     dt = DTYPES[spec.dtype]
     gen = torch.Generator("cpu").manual_seed(spec.seed)
     E, I, H, N = spec.n_experts, spec.inter, spec.hidden, spec.n_tokens
+    EW = spec.n_weights
     lg = draw_logits(gen, N, E)
     x = torch.randn(N, H, generator=gen, dtype=torch.float32).to(dt)
     s13 = _std(spec.sigma13, H)
     s2 = _std(spec.sigma2, I)
     gate = None
     if spec.gated:
-        gate = _randn_cast(gen, (E, I, H), s13, dt)
-    up = _randn_cast(gen, (E, I, H), s13, dt)
-    w2 = _randn_cast(gen, (E, H, I), s2, dt)
+        gate = _randn_cast(gen, (EW, I, H), s13, dt)
+    up = _randn_cast(gen, (EW, I, H), s13, dt)
+    w2 = _randn_cast(gen, (EW, H, I), s2, dt)
     if spec.zipf_s is not None:
         lg = lg + zipf_bias(gen, E, spec.zipf_s)[None, :]
     logits = lg.to(dt)

@@ -49,10 +49,14 @@ def assert_routing_equal(gpu, ref: "oracle.RoutingRef", where: str = "routing") 
         stats[f + "_max_ulp"] = int(d.max()) if d.size else 0
         stats[f + "_n_off"] = int((d > 0).sum())
         assert d.size == 0 or d.max() <= tol, f"{where}.{f}: {d.max()} ulp off (tolerance {tol})"
-    # inside the GPU result, gate_scal is exactly topk_w in sorted order
+    # inside the GPU result, gate_scal is exactly topk_w in sorted order (and 0
+    # past an expert share's local entries, where col_sorted is -1)
     tw = gpu.topk_w.reshape(-1)
     cs = gpu.col_sorted.long()
-    assert torch.equal(gpu.gate_scal, tw[cs]), f"{where}.gate_scal != topk_w.flat[col_sorted]"
+    live = cs >= 0
+    assert torch.equal(gpu.gate_scal[live], tw[cs[live]]), \
+        f"{where}.gate_scal != topk_w.flat[col_sorted]"
+    assert not gpu.gate_scal[~live].any(), f"{where}.gate_scal past the local entries != 0"
     return stats
 
 

@@ -158,3 +158,37 @@ def test_half_entry_points_argument_checks(lib):
     assert w2(a=None) == N.MOE_ERR_NULL
     assert w2(ws=None) == N.MOE_ERR_WORKSPACE            # topk 2 needs the weighted rows
     assert w2(wsb=64) == N.MOE_ERR_WORKSPACE
+
+
+def test_share_entry_points_argument_checks(lib):
+    r = routing()
+
+    def route_ep(lo, nl, n=33, e=32, k=4, lg=FAKE, ws=FAKE):
+        return lib.moe_route_ep(lg, N.MOE_BF16, n, e, k, lo, nl, ctypes.byref(r), ws, 1 << 30,
+                                None)
+    assert route_ep(0, 8, n=0, lg=None, ws=None) == N.MOE_OK          # empty: nothing enqueued
+    for lo, nl in [(-1, 4), (0, 0), (29, 4), (32, 1), (0, 33), (1 << 30, 8)]:
+        assert route_ep(lo, nl) == N.MOE_ERR_SHAPE, (lo, nl)
+    assert route_ep(0, 8, k=33) == N.MOE_ERR_SHAPE                    # k > E still rejected
+    assert route_ep(0, 8, lg=None) == N.MOE_ERR_NULL
+    assert route_ep(0, 8, lg=MISALIGNED) == N.MOE_ERR_ALIGN
+    assert route_ep(0, 8, n=4096, ws=None) == N.MOE_ERR_WORKSPACE
+
+    def experts_ep(nl=2, k=4, n=33, x=FAKE, wsb=1 << 30):
+        return lib.moe_experts_ep(x, N.MOE_BF16, n, 128, FAKE, FAKE, nl, 256, k, N.MOE_ACT_SILU,
+                                  N.MOE_W13_PACKED, None, ctypes.byref(r), FAKE, FAKE, wsb, None)
+    assert experts_ep(n=0, x=None) == N.MOE_OK
+    assert experts_ep(nl=0) == N.MOE_ERR_SHAPE
+    assert experts_ep(nl=257) == N.MOE_ERR_SHAPE
+    assert experts_ep(k=17) == N.MOE_ERR_SHAPE
+    assert experts_ep(x=None) == N.MOE_ERR_NULL
+    assert experts_ep(wsb=1024) == N.MOE_ERR_WORKSPACE
+
+    def fwd_ep(lo, nl, e=16, k=4, n=33):
+        return lib.moe_forward_ep(FAKE, FAKE, N.MOE_BF16, n, 128, FAKE, FAKE, e, lo, nl, 256, k,
+                                  N.MOE_ACT_SILU, N.MOE_W13_PACKED, None, ctypes.byref(r), FAKE,
+                                  FAKE, 1 << 30, None)
+    assert fwd_ep(4, 4, n=0) == N.MOE_OK
+    assert fwd_ep(13, 4) == N.MOE_ERR_SHAPE
+    assert fwd_ep(-2, 4) == N.MOE_ERR_SHAPE
+    assert fwd_ep(0, 4, k=17) == N.MOE_ERR_SHAPE
