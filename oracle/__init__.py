@@ -10,6 +10,8 @@ Python binding, and imports neither.
   offsets, stable expert-sorted gather/scatter indices, permuted gate weights).
 * :mod:`oracle.ffn` -- the expert FFN (SiLU-gated, SwiGLU-OAI, ReLU^2) run as the
   masked per-expert loop, the weighted combine, and the sorted-dispatch variant.
+* :mod:`oracle.routing` also gives the router logits from the gate weight
+  (``gate_logits``, ``route_gate``).
 * both also give one GPU's expert-parallel share (``route_ep``,
   ``moe_ffn_share``): the selected experts remapped to local ids, -1 outside.
 
@@ -18,12 +20,14 @@ library routines, closed forms, invariants and the hand-derived fixtures in
 ``tests/golden/``; the one part with no such pin (the SwiGLU-OAI formula relative
 to the pages) is marked "parity unpinned" where it is defined.
 """
-from .routing import (RoutingRef, bitmatrix, histogram, offsets_from_hist, remap_to_share, route,
-                      route_ep, round_to_dtype, sorted_indices, topk_select, topk_softmax)
+from .routing import (RoutingRef, bitmatrix, gate_logits, histogram, offsets_from_hist,
+                      remap_to_share, route, route_ep, route_gate, round_to_dtype, sorted_indices,
+                      topk_select, topk_softmax)
 from .ffn import activation, moe_ffn, moe_ffn_share, moe_ffn_sorted, split_gate_up
 
 __all__ = [
     "RoutingRef", "route", "topk_select", "topk_softmax", "bitmatrix", "histogram",
     "offsets_from_hist", "sorted_indices", "round_to_dtype", "remap_to_share", "route_ep",
+    "gate_logits", "route_gate",
     "activation", "split_gate_up", "moe_ffn", "moe_ffn_sorted", "moe_ffn_share",
 ]

@@ -13,6 +13,9 @@ What is computed, and where the pages define it:
   of the sorted dispatch in the minimind issue #835 page, section "It is
   removable in plain PyTorch" (stable sort by expert, group ends by
   ``searchsorted(right=True)``);
+* the router logits themselves (``gate_logits``): the router's gate matmul
+  ``x . W_gate^T``, the step just before the top-k that the PR #45457 report
+  leaves to its own kernel (section "motivation");
 * the expert-parallel share (``route_ep``): the selected expert ids remapped to
   the ids local to one GPU's experts, then the bitmatrix re-packed and the
   metadata rebuilt from the remapped ids -- the expert-map branch of the PR
@@ -257,3 +260,17 @@ def route_ep(logits, topk: int, w_dtype: str, local_offset: int, n_local: int) -
         row_sorted=row_sorted,
         gate_scal=gate,
     )
+
+
+def gate_logits(x, w_gate, dtype: str) -> np.ndarray:
+    """Router logits ``[N, E]``: ``x [N, H]`` times the gate weight ``w_gate [E, H]``
+    (nn.Linear out x in) transposed, evaluated in float64 and rounded once,
+    nearest-even, to ``dtype`` (the router's output dtype)."""
+    return round_to_dtype(to_f64(x) @ to_f64(w_gate).T, dtype)
+
+
+def route_gate(x, w_gate, topk: int, w_dtype: str):
+    """Logits from the router's gate matmul, then the routing of those logits;
+    returns ``(logits, RoutingRef)``."""
+    lg = gate_logits(x, w_gate, w_dtype)
+    return lg, route(lg, topk, w_dtype)

@@ -227,6 +227,29 @@ def pin_share_routing(seed=14):
             assert np.array_equal(getattr(whole, f), getattr(g, f)), f
 
 
+def pin_gate_logits(seed=16):
+    """Router logits against scalar dot products summed with math.fsum (inputs
+    on the bf16 grid, so every product is exact and fsum gives the exactly
+    rounded sum), on non-square shapes in both dtypes; an identity gate gives
+    x's first E columns exactly; route_gate routes exactly those logits."""
+    rng = np.random.default_rng(seed)
+    bf = lambda a: orout.round_to_dtype(a, "bf16")
+    for n, e, h, dt in [(5, 3, 7, "f32"), (4, 6, 9, "bf16"), (3, 8, 40, "f32")]:
+        x, w = bf(rng.normal(size=(n, h))), bf(rng.normal(size=(e, h)) * 0.3)
+        lg = orout.gate_logits(x, w, dt)
+        assert lg.shape == (n, e)
+        for t in range(n):
+            for ex in range(e):
+                v = math.fsum(float(x[t, c]) * float(w[ex, c]) for c in range(h))
+                assert lg[t, ex] == orout.round_to_dtype(np.array([v]), dt)[0], (t, ex)
+    x = bf(rng.normal(size=(8, 16)))
+    assert np.array_equal(orout.gate_logits(x, np.eye(16)[:5], "bf16"), x[:, :5])
+    w = bf(rng.normal(size=(6, 16)))
+    lg, r = orout.route_gate(x, w, 2, "bf16")
+    ref = orout.route(lg, 2, "bf16")
+    assert np.array_equal(r.topk_idx, ref.topk_idx) and np.array_equal(r.col_sorted, ref.col_sorted)
+
+
 # --------------------------------------------------------------------------
 # FFN pins
 # --------------------------------------------------------------------------
@@ -447,7 +470,7 @@ def pin_ffn_shares(seed=15):
 
 ROUTING_PINS = [pin_golden_routing, pin_topk_bruteforce, pin_topk_lexsort, pin_topk_special_cases,
                 pin_bf16_rounding, pin_weights_closed_forms, pin_metadata_invariants,
-                pin_empty_experts, pin_share_routing]
+                pin_empty_experts, pin_share_routing, pin_gate_logits]
 FFN_PINS = [pin_ffn_bruteforce, pin_ffn_masked_equals_sorted, pin_ffn_layout_invariance,
             pin_ffn_dense_special_case, pin_activation_closed_forms, pin_ffn_linearity,
             pin_ffn_token_subset, pin_ffn_shares]

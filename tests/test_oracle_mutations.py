@@ -135,6 +135,24 @@ _orig_moe = offn.moe_ffn
 _orig_remap = orout.remap_to_share
 
 
+_orig_gate = orout.gate_logits
+
+
+def gate_not_rounded(x, w, dtype):
+    return orout.to_f64(x) @ orout.to_f64(w).T
+
+
+def gate_rows_swapped(x, w, dtype):
+    # the first two gate rows trade places (a wrong expert index)
+    w = orout.to_f64(w).copy()
+    w[[0, 1]] = w[[1, 0]]
+    return _orig_gate(x, w, dtype)
+
+
+def gate_dropped_last_column(x, w, dtype):
+    return _orig_gate(orout.to_f64(x)[:, :-1], orout.to_f64(w)[:, :-1], dtype)
+
+
 def remap_off_by_one(idx, lo, nl):
     r = _orig_remap(idx, lo, nl)
     return np.where(r >= 0, np.minimum(r + 1, nl - 1), -1).astype(np.int32)
@@ -173,6 +191,9 @@ MUTATIONS = [
     ("share ids not remapped (routing)", orout, "remap_to_share", remap_none, "routing"),
     ("share ids not remapped (ffn)", orout, "remap_to_share", remap_none, "ffn"),
     ("share remap off by one (ffn)", orout, "remap_to_share", remap_off_by_one, "ffn"),
+    ("gate logits not rounded", orout, "gate_logits", gate_not_rounded, "routing"),
+    ("gate rows swapped", orout, "gate_logits", gate_rows_swapped, "routing"),
+    ("gate last hidden unit dropped", orout, "gate_logits", gate_dropped_last_column, "routing"),
 ]
 
 
