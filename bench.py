@@ -36,10 +36,10 @@ sys.path.insert(0, ROOT)
 
 from routing_grouped_expert_amd import (Routing, moe_workspace_bytes,  # noqa: E402
                                         prepare_experts_w13, prepare_experts_w2,
-                                        prepare_forward, prepare_forward_ep, prepare_route,
-                                        prepare_route_ep)
+                                        prepare_forward, prepare_forward_ep,
+                                        prepare_gate_route, prepare_route, prepare_route_ep)
 from routing_grouped_expert_amd.synth import (act_params, layer_spec, make_layer,  # noqa: E402
-                                              routing_logits)
+                                              router_inputs, routing_logits)
 
 METRIC = "MoE layer tokens/s + routing µs/layer; % MFMA bf16 peak and % HBM BW"
 PEAK_HBM_GBS = 8000.0
@@ -102,15 +102,19 @@ def roofline(spec, flops, nbytes, ms):
             "frac": round(ach / PEAK_HBM_GBS, 4)}
 
 
-def cpu_baseline(spec, layer, budget_s: float):
-    """The CPU oracle as it stands, on this host, over a bounded token sample."""
-    import numpy as np
-    import oracle
+def _oracle_threads() -> int:
+    """Threads the oracle's numpy (BLAS) calls run on."""
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+        return os.cpu_count()
+
+
+def cpu_baseline(spec, layer, budget_s: float):
+    """The CPU oracle as it stands, on this host, over a bounded token sample."""
+    import oracle
+    threads = _oracle_threads()
     wd = "bf16" if spec.dtype == "bf16" else "f32"
     n = spec.n_tokens
     share = spec.n_local is not None
@@ -257,6 +261,73 @@ def bench_route_only(args, name: str):
     print(json.dumps(result), flush=True)
 
 
+def bench_gate_route(args, name: str):
+    """Router GEMM + routing workloads: gate_n<N>_e<E>_h<H>_k<k> (bf16): x [N, H]
+    and the gate weight [E, H] in, logits and routing metadata out, one
+    moe_gate_route call per step; moe_route on the same logits is timed beside
+    it (the routing alone)."""
+    import re
+    m = re.fullmatch(r"gate_n(\d+)_e(\d+)_h(\d+)_k(\d+)", name)
+    if not m:
+        raise SystemExit(f"unknown workload {name!r}")
+    n, e, h, k = (int(v) for v in m.groups())
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x_cpu, w_cpu = router_inputs(n, e, h, "bf16", seed=0)
+    x, w = x_cpu.to(dev), w_cpu.to(dev)
+    lg = torch.empty(n, e, dtype=torch.bfloat16, device=dev)
+    routing = Routing.empty(n, e, k, torch.bfloat16, dev)
+    ws = torch.empty(max(1, moe_workspace_bytes(n, e, k)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    p_gate = prepare_gate_route(x, w, k, logits=lg, routing=routing, workspace=ws, stream=stream)
+    p_route = prepare_route(lg, k, routing=routing, workspace=ws, stream=stream)
+    for _ in range(args.warmup):
+        p_gate()
+    t0 = time.perf_counter()
+    st = step_stats(p_gate, args.steps, stream)
+    wall = time.perf_counter() - t0
+    st_route = step_stats(p_route, args.steps, stream)
+    cold = cold_stats([p_gate], 20, stream, dev)[0]
+    words = (e + 31) // 32
+    route_b = n * e * 2 + n * k * (4 + 2 + 4 + 4 + 2) + n * words * 4 + (2 * e + 1) * 4
+    nbytes = n * h * 2 + e * h * 2 + n * e * 2 + route_b   # x, gate weight, logits out, routing
+    flops = 2 * n * e * h
+    spec_like = type("S", (), {"dtype": "bf16"})()
+    roof = roofline(spec_like, flops, nbytes, st["mean"])
+    roof.update({"kernel": "router GEMM + routing (all kernels of one moe_gate_route call)",
+                 "traffic": None, "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+                 "avg_launch_us": round(st["mean"] * 1e3, 2)})
+    result = {
+        "metric": METRIC, "value": round(n / (st["mean"] * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": st["steps"], "warmup": args.warmup,
+        "ms_per_step": round(st["mean"], 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian token rows and gate weight)",
+        "config": {"workload": f"{name}: router GEMM + routing, N={n} E={e} H={h} k={k} bf16"},
+        "routing_us_per_layer": round(st["mean"] * 1e3, 2),
+        "route_only_us": round(st_route["mean"] * 1e3, 2),
+        "step_us": {q: round(st[q] * 1e3, 2) for q in ("p10", "p50", "p90")},
+        "cold_routing_us": round(cold * 1e3, 2),
+        "wall_ms_per_step": round(wall / st["steps"] * 1e3, 4),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        sample = min(n, 2048)
+        t0, reps = time.perf_counter(), 0
+        while True:
+            oracle.route_gate(x_cpu[:sample], w_cpu, k, "bf16")
+            reps += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": round(sample * reps / dt, 1), "unit": "tokens/s",
+                                  "cores": _oracle_threads(), "kind": "oracle",
+                                  "sample": f"first {sample} of {n} tokens, router logits + "
+                                            f"routing oracle, {reps} passes in {dt:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -283,6 +354,8 @@ def main():
         del src, dst
     if args.workload.startswith("route_"):
         return bench_route_only(args, args.workload)
+    if args.workload.startswith("gate_"):
+        return bench_gate_route(args, args.workload)
     spec = workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

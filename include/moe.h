@@ -8,8 +8,10 @@
  *   moe_experts  routing metadata + x -> grouped expert FFN -> weighted combine
  *   moe_forward  moe_route followed by moe_experts, on one stream
  *
- * and their expert-parallel-share variants moe_route_ep, moe_experts_ep and
- * moe_forward_ep (one GPU's contiguous share of the experts; see below).
+ * with the router GEMM in front (moe_gate_route, moe_gate_forward: logits from
+ * the token rows and the gate weight), and the expert-parallel-share variants
+ * moe_route_ep, moe_experts_ep and moe_forward_ep (one GPU's contiguous share
+ * of the experts; see below).
  *
  * moe_experts is also exported as its two halves, moe_experts_w13 (grouped
  * GEMM with w13 + activation) and moe_experts_w2 (grouped GEMM with w2 +
@@ -176,6 +178,31 @@ moe_status_t moe_forward(const void *x, const void *logits, moe_dtype_t dtype,
                          moe_w13_layout_t layout, const moe_act_params_t *params,
                          const moe_routing_t *routing_out, void *out, void *workspace,
                          size_t ws_bytes, void *stream);
+
+/* ---- Router GEMM ahead of the routing ----------------------------------------
+ * The router's gate matmul, logits = x . w_gate^T, is the step just before
+ * the top-k; the vLLM PR #45457 report leaves it to its own kernel
+ * ("motivation").  Here it is part of the routing step.
+ *
+ * moe_gate_route: x [N, hidden] and w_gate [n_experts, hidden] (nn.Linear
+ *   out x in, row-major) in `dtype`; logits_out [N, n_experts] in `dtype`
+ *   receives logits[t][e] = sum_h x[t][h] * w_gate[e][h], accumulated in fp32
+ *   and rounded once (nearest-even) to `dtype`; then everything moe_route
+ *   computes from those logits goes to *out (out->w_dtype == dtype).  The same
+ *   result as writing the logits and calling moe_route on them.  Workspace and
+ *   limits as moe_route; hidden a positive multiple of 8; x and logits_out
+ *   below 2^31 bytes.
+ * moe_gate_forward: moe_gate_route then moe_experts, on one stream. */
+moe_status_t moe_gate_route(const void *x, const void *w_gate, moe_dtype_t dtype,
+                            int64_t n_tokens, int32_t hidden, int32_t n_experts, int32_t topk,
+                            void *logits_out, const moe_routing_t *out, void *workspace,
+                            size_t ws_bytes, void *stream);
+moe_status_t moe_gate_forward(const void *x, const void *w_gate, moe_dtype_t dtype,
+                              int64_t n_tokens, int32_t hidden, const void *w13, const void *w2,
+                              int32_t n_experts, int32_t inter, int32_t topk, moe_act_t act,
+                              moe_w13_layout_t layout, const moe_act_params_t *params,
+                              void *logits_out, const moe_routing_t *routing_out, void *out,
+                              void *workspace, size_t ws_bytes, void *stream);
 
 /* ---- Expert-parallel share ---------------------------------------------------
  * One GPU of an expert-parallel group holds the contiguous share of experts

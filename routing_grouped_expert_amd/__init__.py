@@ -13,6 +13,10 @@ they raise if the library is missing.
                                layout="interleaved",
                                params={"alpha": 1.702, "beta": 1.0, "limit": 7.0})
 
+With the router's gate weight ``w_gate [E, H]`` the routing step also computes
+the logits (router GEMM): ``logits, routing = moe_gate_route(x, w_gate, topk)``;
+``moe_gate_forward`` runs the whole layer from ``x`` and ``w_gate``.
+
 One GPU of an expert-parallel group (experts [lo, lo + n) of the layer's E,
 weights w13 [n, ...], w2 [n, ...]) uses the ``_ep`` variants; summing their
 outputs over the group's shares gives the layer output:
@@ -35,7 +39,8 @@ __all__ = ["Routing", "MoeError", "Prepared", "moe_route", "moe_experts", "moe_e
            "moe_experts_w2", "moe_forward", "prepare_route", "prepare_experts",
            "prepare_experts_w13", "prepare_experts_w2", "prepare_forward",
            "moe_route_ep", "moe_experts_ep", "moe_forward_ep", "prepare_route_ep",
-           "prepare_experts_ep", "prepare_forward_ep",
+           "prepare_experts_ep", "prepare_forward_ep", "moe_gate_route", "moe_gate_forward",
+           "prepare_gate_route", "prepare_gate_forward",
            "moe_workspace_bytes", "moe_status_str", "ACTS", "LAYOUTS"]
 
 _DT = {torch.float32: N.MOE_F32, torch.bfloat16: N.MOE_BF16}
@@ -437,3 +442,77 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor, w2: to
     """Routing then experts on one stream; returns ``(out, routing)``."""
     return prepare_forward(x, logits, w13, w2, topk, act, layout, params, out=out,
                            routing=routing, workspace=workspace, stream=stream)()
+
+
+def _gate_args(x, w_gate, logits):
+    dev = _dev(x, w_gate)
+    if x.dim() != 2 or w_gate.dim() != 2 or x.shape[1] != w_gate.shape[1]:
+        raise ValueError("expected x [N, H] and w_gate [E, H]")
+    if x.dtype != w_gate.dtype:
+        raise TypeError("x and w_gate must share a dtype")
+    n, e = x.shape[0], w_gate.shape[0]
+    if logits is None:
+        logits = torch.empty(n, e, dtype=x.dtype, device=dev)
+    _dev(x, logits)
+    if tuple(logits.shape) != (n, e) or logits.dtype != x.dtype:
+        raise ValueError("logits must be [N, E] in the layer dtype")
+    return dev, n, e, logits
+
+
+def prepare_gate_route(x: torch.Tensor, w_gate: torch.Tensor, topk: int, *,
+                       logits: Optional[torch.Tensor] = None, routing: Optional[Routing] = None,
+                       workspace: Optional[torch.Tensor] = None, stream=None) -> Prepared:
+    dev, n, e, logits = _gate_args(x, w_gate, logits)
+    if routing is None:
+        routing = Routing.empty(n, e, topk, x.dtype, dev)
+    _check_routing(routing, n, e, topk)
+    ws = _workspace(workspace, moe_workspace_bytes(n, e, topk, 0, 0, x.dtype), dev)
+    r = routing.as_c()
+    args = (x.data_ptr(), w_gate.data_ptr(), _dt(x), n, x.shape[1], e, topk, logits.data_ptr(),
+            ctypes.byref(r), ws.data_ptr(), _nbytes(ws), _stream(dev, stream))
+    return Prepared("moe_gate_route", args, (r, x, w_gate, logits, ws, routing),
+                    (logits, routing))
+
+
+def moe_gate_route(x: torch.Tensor, w_gate: torch.Tensor, topk: int, *,
+                   logits: Optional[torch.Tensor] = None, routing: Optional[Routing] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None):
+    """Router GEMM ``logits = x . w_gate^T`` then the routing step; returns
+    ``(logits, routing)`` (see moe.h)."""
+    return prepare_gate_route(x, w_gate, topk, logits=logits, routing=routing,
+                              workspace=workspace, stream=stream)()
+
+
+def prepare_gate_forward(x, w_gate, w13, w2, topk: int, act: str, layout: str = "packed",
+                         params: Optional[dict] = None, *, out=None, logits=None, routing=None,
+                         workspace=None, stream=None) -> Prepared:
+    dev, n, e, logits = _gate_args(x, w_gate, logits)
+    _dev(x, w13, w2)
+    _shapes(x, w13, w2, act, out, logits)
+    hidden, inter = x.shape[1], w2.shape[2]
+    if routing is None:
+        routing = Routing.empty(n, e, topk, x.dtype, dev)
+    _check_routing(routing, n, e, topk)
+    if out is None:
+        out = torch.empty_like(x)
+    ws = _workspace(workspace, moe_workspace_bytes(n, e, topk, hidden, inter, x.dtype), dev)
+    r = routing.as_c()
+    p = _params(params)
+    args = (x.data_ptr(), w_gate.data_ptr(), _dt(x), n, hidden, w13.data_ptr(), w2.data_ptr(),
+            e, inter, topk, ACTS[act], LAYOUTS[layout], ctypes.byref(p) if p else None,
+            logits.data_ptr(), ctypes.byref(r), out.data_ptr(), ws.data_ptr(), _nbytes(ws),
+            _stream(dev, stream))
+    return Prepared("moe_gate_forward", args,
+                    (r, p, x, w_gate, w13, w2, out, logits, ws, routing), (out, logits, routing))
+
+
+def moe_gate_forward(x: torch.Tensor, w_gate: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor,
+                     topk: int, act: str, layout: str = "packed", params: Optional[dict] = None,
+                     *, out: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                     routing: Optional[Routing] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None):
+    """The whole layer from the token rows and the router's gate weight;
+    returns ``(out, logits, routing)``."""
+    return prepare_gate_forward(x, w_gate, w13, w2, topk, act, layout, params, out=out,
+                                logits=logits, routing=routing, workspace=workspace,
+                                stream=stream)()

@@ -51,6 +51,11 @@ SIGNATURES = {
     "moe_forward_ep": (c_i32, [c_vp, c_vp, c_i32, c_i64, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32,
                                c_i32, c_i32, c_i32, c_i32, _P_PARAMS, _P_ROUTING, c_vp, c_vp,
                                c_sz, c_vp]),
+    "moe_gate_route": (c_i32, [c_vp, c_vp, c_i32, c_i64, c_i32, c_i32, c_i32, c_vp, _P_ROUTING,
+                               c_vp, c_sz, c_vp]),
+    "moe_gate_forward": (c_i32, [c_vp, c_vp, c_i32, c_i64, c_i32, c_vp, c_vp, c_i32, c_i32,
+                                 c_i32, c_i32, c_i32, _P_PARAMS, c_vp, _P_ROUTING, c_vp, c_vp,
+                                 c_sz, c_vp]),
     "moe_status_str": (ctypes.c_char_p, [c_i32]),
 }
 

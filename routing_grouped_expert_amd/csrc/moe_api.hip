@@ -148,6 +148,18 @@ moe_status_t check_route(const void *logits, moe_dtype_t dt, int64_t n, int32_t 
   return MOE_OK;
 }
 
+// Router GEMM operands: x [n, hidden], w_gate [e, hidden], logits_out [n, e].
+moe_status_t check_gate(const void *x, const void *w_gate, moe_dtype_t dt, int64_t n,
+                        int32_t hidden, int32_t e, void *logits_out) {
+  if (!dtype_ok(dt)) return MOE_ERR_DTYPE;
+  if (hidden < 8 || hidden % 8 || hidden > (1 << 24) || e < 1 || e > moe::kMaxExperts || n < 0)
+    return MOE_ERR_SHAPE;
+  const int64_t lim = 0x7fffffff, es = (int64_t)dsize(dt);
+  if (n * hidden * es > lim || n * e * es > lim) return MOE_ERR_SHAPE;
+  if (n == 0) return MOE_OK;
+  return check_ptrs({x, w_gate, logits_out});
+}
+
 // The expert-parallel share [lo, lo + nl) must lie inside [0, e).
 moe_status_t check_share(int32_t e, int32_t lo, int32_t nl) {
   if (lo < 0 || nl < 1 || lo > e - nl) return MOE_ERR_SHAPE;
@@ -335,6 +347,43 @@ moe_status_t moe_forward_ep(const void *x, const void *logits, moe_dtype_t dtype
     return MOE_ERR_HIP;
   return run_experts(x, dtype, n_tokens, hidden, w13, w2, n_local, inter, topk, act, layout, prm,
                      routing_out, out, workspace, s, true);
+}
+
+moe_status_t moe_gate_route(const void *x, const void *w_gate, moe_dtype_t dtype,
+                            int64_t n_tokens, int32_t hidden, int32_t n_experts, int32_t topk,
+                            void *logits_out, const moe_routing_t *out, void *workspace,
+                            size_t ws_bytes, void *stream) {
+  moe_status_t st = check_gate(x, w_gate, dtype, n_tokens, hidden, n_experts, logits_out);
+  if (st != MOE_OK) return st;
+  st = check_route(logits_out, dtype, n_tokens, n_experts, topk, out, workspace, ws_bytes);
+  if (st != MOE_OK || n_tokens == 0) return st;
+  if (moe::launch_route(logits_out, dtype, n_tokens, n_experts, topk, 0, n_experts, out,
+                        workspace, (hipStream_t)stream, x, w_gate, hidden) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+moe_status_t moe_gate_forward(const void *x, const void *w_gate, moe_dtype_t dtype,
+                              int64_t n_tokens, int32_t hidden, const void *w13, const void *w2,
+                              int32_t n_experts, int32_t inter, int32_t topk, moe_act_t act,
+                              moe_w13_layout_t layout, const moe_act_params_t *params,
+                              void *logits_out, const moe_routing_t *routing_out, void *out,
+                              void *workspace, size_t ws_bytes, void *stream) {
+  ActParams prm;
+  moe_status_t st = check_gate(x, w_gate, dtype, n_tokens, hidden, n_experts, logits_out);
+  if (st != MOE_OK) return st;
+  st = check_route(logits_out, dtype, n_tokens, n_experts, topk, routing_out, workspace,
+                   ws_bytes);
+  if (st != MOE_OK) return st;
+  st = check_experts(x, dtype, n_tokens, hidden, w13, w2, n_experts, inter, topk, act, layout,
+                     params, routing_out, out, workspace, ws_bytes, &prm);
+  if (st != MOE_OK || n_tokens == 0) return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (moe::launch_route(logits_out, dtype, n_tokens, n_experts, topk, 0, n_experts, routing_out,
+                        workspace, s, x, w_gate, hidden) != hipSuccess)
+    return MOE_ERR_HIP;
+  return run_experts(x, dtype, n_tokens, hidden, w13, w2, n_experts, inter, topk, act, layout,
+                     prm, routing_out, out, workspace, s);
 }
 
 const char *moe_status_str(moe_status_t status) {

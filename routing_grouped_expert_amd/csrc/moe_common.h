@@ -45,10 +45,13 @@ constexpr int kRouteTokens = 256;  // tokens per routing block (one per thread i
 
 size_t route_scratch_bytes(int64_t n_tokens, int n_experts, int topk);
 // Routing for the expert share [local_offset, local_offset + n_local) of the
-// n_experts (0 and n_experts for the whole layer).
+// n_experts (0 and n_experts for the whole layer).  With x != nullptr the
+// logits [N, E] are first computed as x [N, hidden] . w_gate [E, hidden]^T and
+// written to `logits` (router GEMM).
 hipError_t launch_route(const void *logits, moe_dtype_t dt, int64_t n_tokens, int n_experts,
                         int topk, int local_offset, int n_local, const moe_routing_t *r,
-                        void *scratch, hipStream_t s);
+                        void *scratch, hipStream_t s, const void *x = nullptr,
+                        const void *w_gate = nullptr, int hidden = 0);
 
 struct ActParams {
   float alpha, beta, limit;

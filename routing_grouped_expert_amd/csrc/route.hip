@@ -26,6 +26,17 @@
 //    workgroup of 1024 threads with every per-entry value kept in LDS (one
 //    launch for the whole routing step).
 //
+// Router GEMM (moe_gate_route): the logits are computed from the token rows and
+// the router's gate weight (logits = x . W_gate^T, fp32 accumulation on MFMA,
+// rounded once to the layer dtype) and written out; top-k then runs on them.
+// The router's own matmul is the step ahead of the routing that the vLLM PR
+// #45457 report leaves as a separate kernel ("motivation").  Batches of at
+// most kGateFusedTokens tokens compute their logits in the prologue of the
+// one-workgroup routing kernel (one launch for the whole step); larger batches
+// run the same device function as a kernel of its own, one workgroup per 64
+// tokens, because the prologue of a 256-token routing block would put all of
+// that block's router matmul on one compute unit.
+//
 // Expert-parallel share: every kernel takes the share [lo, lo + nl) of the E
 // experts that this GPU holds (lo = 0, nl = E for the whole layer).  Top-k and
 // softmax run over all E logits; the selected ids are then remapped to local
@@ -182,7 +193,7 @@ template <typename T, int NT, int MAXE = kMaxExperts, int MAXK = kMaxTopk> struc
 // G = ceil(E / (C * kVec)) lanes serve one token.  Fewer lanes per token cost
 // fewer VALU lane-operations per selection round, so wide expert sets use C = 2.
 template <typename T, int THREADS, int C, typename Lds>
-__device__ __forceinline__ void topk_chunk(const T *__restrict__ logits, int64_t N, int E, int K,
+__device__ __forceinline__ void topk_chunk(const T *logits, int64_t N, int E, int K,
                                            int lo, int nl, int logG, int vec, int64_t tok0,
                                            int32_t *__restrict__ topk_idx,
                                            T *__restrict__ topk_w,
@@ -358,20 +369,177 @@ __device__ __forceinline__ int chunk_rank(const Lds &L, int t, int e) {
   return L.cnt[tw][e] + popc64(L.mask[tw][e] & below);
 }
 
+
+// ---- router GEMM -------------------------------------------------------------
+// MFMA of the router matmul: bf16 v_mfma_f32_32x32x16_bf16 (16 K per step,
+// 8 per lane), fp32 v_mfma_f32_32x32x2_f32 (2 K per step, 1 per lane).
+template <typename T> struct GateMma;
+template <> struct GateMma<bf16_t> {
+  static constexpr int KS = 16, EPL = 8;
+  typedef bf16x8_t Frag;
+  __device__ static Frag ld(const char *p) { return *reinterpret_cast<const bf16x8_t *>(p); }
+  __device__ static f32x16_t mma(Frag a, Frag b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct GateMma<float> {
+  static constexpr int KS = 2, EPL = 1;
+  typedef float Frag;
+  __device__ static Frag ld(const char *p) { return *reinterpret_cast<const float *>(p); }
+  __device__ static f32x16_t mma(Frag a, Frag b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+};
+
+constexpr int kGateRowBytes = 128;  // one K-slice of a row in LDS
+// Batches up to this size run the router GEMM in the one-workgroup routing
+// kernel's prologue; larger ones launch gate_gemm first.
+constexpr int kGateFusedTokens = 64;
+// LDS bytes of gate_logits<.., NT, ..>: NT token rows + up to 256 gate rows
+constexpr int gate_lds_bytes(int nt) { return (nt + kMaxExperts) * kGateRowBytes; }
+
+// Byte offset of 16-byte chunk c of LDS row r: chunks are XOR-swizzled with
+// (r / 2) % 8, so the 16 lanes of a fragment read (16 consecutive rows, same
+// chunk) land in different bank groups.
+__device__ __forceinline__ int gate_swz(int r, int c) {
+  return r * kGateRowBytes + ((c ^ ((r >> 1) & 7)) << 4);
+}
+
+// logits[t][e] for tokens t in [tok0, min(tok0 + NT, N)) and all E experts:
+// sum over h of x[t][h] * wg[e][h] in fp32, rounded once to T.  The token rows
+// and the gate rows go through LDS one 128-byte K-slice at a time (the next
+// slice's loads are in flight while the current one is multiplied); 32x32
+// output blocks (gate rows as the first MFMA operand, so a lane holds one token
+// and runs of 4 experts) are dealt to the waves.  Ends with every thread past
+// a barrier, its logits stored.
+template <typename T, int NT, int THREADS>
+__device__ __forceinline__ void gate_logits(const T *__restrict__ x, const T *__restrict__ wg,
+                                            int64_t N, int H, int E, int64_t tok0,
+                                            T *__restrict__ logits, char *lds) {
+  using Mm = GateMma<T>;
+  constexpr int NW = THREADS / 64;
+  constexpr int MAXB = ((NT / 32) * (kMaxExperts / 32) + NW - 1) / NW;  // output blocks a wave
+  constexpr int U = ((NT + kMaxExperts) * 8 + THREADS - 1) / THREADS;  // chunk loads a thread
+  constexpr int KSTEPS = kGateRowBytes / (Mm::KS * (int)sizeof(T));
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int live = (int)min<int64_t>(NT, N - tok0);
+  const int tbn = (live + 31) >> 5, ebn = (E + 31) >> 5;
+  const int xrows = tbn * 32, nchunks = (xrows + ebn * 32) * 8;
+  const int rowb = H * (int)sizeof(T);  // bytes of one x / gate row (a multiple of 16)
+  const int nslice = (rowb + kGateRowBytes - 1) / kGateRowBytes;
+  const char *xb = reinterpret_cast<const char *>(x);
+  const char *wb = reinterpret_cast<const char *>(wg);
+
+  u32x4_t pre[U];
+  auto fetch = [&](int sl) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = tid + u * THREADS;
+      const int r = q >> 3, kb = sl * kGateRowBytes + (q & 7) * 16;
+      pre[u] = u32x4_t{0u, 0u, 0u, 0u};
+      if (q < nchunks && kb < rowb) {
+        if (r < xrows) {
+          const int64_t t = tok0 + r;
+          if (t < N) pre[u] = *reinterpret_cast<const u32x4_t *>(xb + t * rowb + kb);
+        } else if (r - xrows < E) {
+          pre[u] = *reinterpret_cast<const u32x4_t *>(wb + (int64_t)(r - xrows) * rowb + kb);
+        }
+      }
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int q = tid + u * THREADS;
+      if (q < nchunks) {
+        const int r = q >> 3;
+        const int lr = r < xrows ? r : NT + (r - xrows);  // gate rows live after NT
+        *reinterpret_cast<u32x4_t *>(lds + gate_swz(lr, q & 7)) = pre[u];
+      }
+    }
+  };
+
+  f32x16_t acc[MAXB];
+#pragma unroll
+  for (int j = 0; j < MAXB; ++j)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[j][i] = 0.f;
+  const int nb = tbn * ebn;
+  fetch(0);
+  for (int sl = 0; sl < nslice; ++sl) {
+    stash();
+    __syncthreads();
+    if (sl + 1 < nslice) fetch(sl + 1);
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int bo = (ks * Mm::KS + (lane >> 5) * Mm::EPL) * (int)sizeof(T);
+#pragma unroll
+      for (int j = 0; j < MAXB; ++j) {
+        const int b = wave + j * NW;
+        if (b < nb) {
+          const int tb = b % tbn, eb = b / tbn;
+          const int ra = NT + eb * 32 + (lane & 31), rx = tb * 32 + (lane & 31);
+          const typename Mm::Frag fa = Mm::ld(lds + gate_swz(ra, bo >> 4) + (bo & 15));
+          const typename Mm::Frag fx = Mm::ld(lds + gate_swz(rx, bo >> 4) + (bo & 15));
+          acc[j] = Mm::mma(fa, fx, acc[j]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // lane: token tb*32 + lane%32; register r: expert eb*32 + 8(r/4) + 4(lane/32) + r%4
+#pragma unroll
+  for (int j = 0; j < MAXB; ++j) {
+    const int b = wave + j * NW;
+    if (b < nb) {
+      const int tb = b % tbn, eb = b / tbn;
+      const int64_t t = tok0 + tb * 32 + (lane & 31);
+      if (t < N) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int e = eb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (e < E) logits[t * E + e] = from_f32<T>(acc[j][r]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Router GEMM alone: one workgroup of 256 threads per 64 tokens.
+constexpr int kGateTokens = 64, kGateThreads = 256;
+template <typename T>
+__global__ __launch_bounds__(kGateThreads) void gate_gemm(const T *__restrict__ x,
+                                                          const T *__restrict__ wg, int64_t N,
+                                                          int H, int E, T *__restrict__ logits) {
+  __shared__ __align__(16) char lds[gate_lds_bytes(kGateTokens)];
+  gate_logits<T, kGateTokens, kGateThreads>(x, wg, N, H, E, (int64_t)blockIdx.x * kGateTokens,
+                                            logits, lds);
+}
+
 // Batches of at most NT tokens: one workgroup, one launch.  Every per-entry
 // value stays in LDS; the scan and the scatter follow the rank phase directly.
-template <typename T, int THREADS, int C, typename Lds>
+// GATE: the logits are first computed from x and the gate weight (router GEMM
+// prologue) and stored to `logits`, which the top-k phase then reads.
+// (The logits pointer carries no __restrict__: with GATE the same buffer is
+// written through logits_out first.)
+template <typename T, int THREADS, int C, typename Lds, bool GATE = false>
 __global__ __launch_bounds__(THREADS) void route_fused(
-    const T *__restrict__ logits, int64_t N, int E, int K, int lo, int nl, int logG, int vec,
+    const T *logits, int64_t N, int E, int K, int lo, int nl, int logG, int vec,
     int32_t *__restrict__ topk_idx, T *__restrict__ topk_w, uint32_t *__restrict__ bitmatrix,
     int32_t *__restrict__ col_sum, int32_t *__restrict__ offsets,
     int32_t *__restrict__ col_sorted, int32_t *__restrict__ row_sorted,
-    T *__restrict__ gate_scal) {
+    T *__restrict__ gate_scal, const T *__restrict__ x = nullptr, const T *__restrict__ wg = nullptr,
+    int H = 0, T *logits_out = nullptr) {
   constexpr int NT = Lds::kTokens;
   __shared__ Lds L;
   __shared__ uint16_t s_rank[NT * Lds::kSlots];
   __shared__ int s_off[Lds::kExperts + 1];
   const int tid = threadIdx.x;
+  if constexpr (GATE) {  // N <= kGateFusedTokens
+    __shared__ __align__(16) char s_gemm[gate_lds_bytes(kGateFusedTokens)];
+    gate_logits<T, kGateFusedTokens, THREADS>(x, wg, N, H, E, 0, logits_out, s_gemm);
+  }
   topk_chunk<T, THREADS, C>(logits, N, E, K, lo, nl, logG, vec, 0, topk_idx, topk_w, bitmatrix,
                             L);
   __syncthreads();
@@ -564,9 +732,12 @@ inline RoutePath route_path(int64_t N, int E, int K) {
   return N <= kFusedTokens ? kPathFused : kPathBlocks;
 }
 
+// With x != nullptr (router GEMM), `logits` is written from x and the gate
+// weight wg [E, H] before the top-k reads it.
 template <typename T>
 hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int nl,
-                          const moe_routing_t *r, void *scratch, hipStream_t s) {
+                          const moe_routing_t *r, void *scratch, hipStream_t s,
+                          const T *x = nullptr, const T *wg = nullptr, int H = 0) {
   constexpr int V = Logit<T>::kVec;
   // two chunks a lane when one would need more than 8 lanes a token, unless the
   // batch is so small that spreading it over more lanes matters more
@@ -579,6 +750,21 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
   T *tw = reinterpret_cast<T *>(r->topk_w);
   T *gs = reinterpret_cast<T *>(r->gate_scal);
   const RoutePath path = route_path(N, E, K);
+  T *lw = const_cast<T *>(logits);
+  if (x && N <= kGateFusedTokens) {  // router GEMM in the routing kernel's prologue
+    // (batches this small take one logit chunk a lane: `wide` is false)
+    hipLaunchKernelGGL((route_fused<T, 1024, 1, ChunkLds<T, kFusedTokens>, true>), dim3(1),
+                       dim3(1024), 0, s, logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw,
+                       r->bitmatrix, r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs, x,
+                       wg, H, lw);
+    return hipGetLastError();
+  }
+  if (x) {  // router GEMM as a kernel of its own, then the routing kernels
+    hipLaunchKernelGGL(gate_gemm<T>, dim3((unsigned)((N + kGateTokens - 1) / kGateTokens)),
+                       dim3(kGateThreads), 0, s, x, wg, N, H, E, lw);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   if (path == kPathFused) {
     if (wide)
       hipLaunchKernelGGL((route_fused<T, 1024, 2, ChunkLds<T, kFusedTokens>>), dim3(1), dim3(1024),
@@ -619,12 +805,17 @@ size_t route_scratch_bytes(int64_t n_tokens, int n_experts, int topk) {
 
 hipError_t launch_route(const void *logits, moe_dtype_t dt, int64_t n_tokens, int n_experts,
                         int topk, int local_offset, int n_local, const moe_routing_t *r,
-                        void *scratch, hipStream_t s) {
+                        void *scratch, hipStream_t s, const void *x, const void *w_gate,
+                        int hidden) {
   if (dt == MOE_BF16)
     return launch_route_t<bf16_t>(reinterpret_cast<const bf16_t *>(logits), n_tokens, n_experts,
-                                  topk, local_offset, n_local, r, scratch, s);
+                                  topk, local_offset, n_local, r, scratch, s,
+                                  reinterpret_cast<const bf16_t *>(x),
+                                  reinterpret_cast<const bf16_t *>(w_gate), hidden);
   return launch_route_t<float>(reinterpret_cast<const float *>(logits), n_tokens, n_experts,
-                               topk, local_offset, n_local, r, scratch, s);
+                               topk, local_offset, n_local, r, scratch, s,
+                               reinterpret_cast<const float *>(x),
+                               reinterpret_cast<const float *>(w_gate), hidden);
 }
 
 }  // namespace moe

@@ -139,6 +139,17 @@ def routing_logits(n_tokens: int, n_experts: int, dtype: str = "bf16", seed: int
     return lg.to(DTYPES[dtype])
 
 
+def router_inputs(n_tokens: int, n_experts: int, hidden: int, dtype: str = "bf16",
+                  seed: int = 0, sigma: Optional[float] = None):
+    """Token rows ``x [N, H]`` ~ N(0, 1) and the router's gate weight
+    ``w_gate [E, H]`` ~ N(0, sigma) (default 1/sqrt(H), so the logits are about
+    N(0, 1) like ``routing_logits``), drawn in that order and rounded to dtype."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    x = torch.randn(n_tokens, hidden, generator=gen, dtype=torch.float32)
+    w = torch.randn(n_experts, hidden, generator=gen, dtype=torch.float32) * _std(sigma, hidden)
+    return x.to(DTYPES[dtype]), w.to(DTYPES[dtype])
+
+
 def pack_w13(gate: torch.Tensor, up: torch.Tensor, layout: str) -> torch.Tensor:
     """Lay gate/up rows out as ``[E, 2I, H]``: packed [gate; up] or interleaved."""
     if layout == "packed":

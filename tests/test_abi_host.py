@@ -192,3 +192,29 @@ def test_share_entry_points_argument_checks(lib):
     assert fwd_ep(13, 4) == N.MOE_ERR_SHAPE
     assert fwd_ep(-2, 4) == N.MOE_ERR_SHAPE
     assert fwd_ep(0, 4, k=17) == N.MOE_ERR_SHAPE
+
+
+def test_gate_entry_points_argument_checks(lib):
+    r = routing()
+
+    def gate(n=33, h=128, e=16, k=4, x=FAKE, wg=FAKE, lg=FAKE, dt=N.MOE_BF16, ws=FAKE):
+        return lib.moe_gate_route(x, wg, dt, n, h, e, k, lg, ctypes.byref(r), ws, 1 << 30, None)
+    assert gate(n=0, x=None, wg=None, lg=None, ws=None) == N.MOE_OK
+    assert gate(x=None) == N.MOE_ERR_NULL
+    assert gate(wg=None) == N.MOE_ERR_NULL
+    assert gate(lg=None) == N.MOE_ERR_NULL
+    assert gate(lg=MISALIGNED) == N.MOE_ERR_ALIGN
+    assert gate(h=100) == N.MOE_ERR_SHAPE                        # not a multiple of 8
+    assert gate(e=257) == N.MOE_ERR_SHAPE
+    assert gate(k=17) == N.MOE_ERR_SHAPE
+    assert gate(n=1 << 20, h=1 << 11) == N.MOE_ERR_SHAPE         # x over 2^31 bytes
+    assert gate(dt=7) == N.MOE_ERR_DTYPE
+    assert gate(n=4096, ws=None) == N.MOE_ERR_WORKSPACE
+
+    def gfwd(n=33, x=FAKE, act=N.MOE_ACT_SILU, layout=N.MOE_W13_PACKED, wsb=1 << 30):
+        return lib.moe_gate_forward(x, FAKE, N.MOE_BF16, n, 128, FAKE, FAKE, 8, 256, 2, act,
+                                    layout, None, FAKE, ctypes.byref(r), FAKE, FAKE, wsb, None)
+    assert gfwd(n=0) == N.MOE_OK
+    assert gfwd(x=None) == N.MOE_ERR_NULL
+    assert gfwd(act=N.MOE_ACT_RELU2, layout=N.MOE_W13_INTERLEAVED) == N.MOE_ERR_UNSUPPORTED
+    assert gfwd(wsb=256) == N.MOE_ERR_WORKSPACE
