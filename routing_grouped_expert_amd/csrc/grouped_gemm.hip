@@ -34,13 +34,12 @@
 #include <cmath>
 #include <type_traits>
 
+#include "lds_dma.h"
 #include "moe_common.h"
 
 namespace moe {
 namespace {
 
-constexpr uint32_t kOOB = 0x80000000u;  // buffer offset past every num_records used here
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 family
 
 // Epilogue kinds: GEMM1 applies the activation (gated without or with the
 // clamp, or ReLU^2); GEMM2 scales by the routing weight and writes the sorted
@@ -92,57 +91,6 @@ template <int RB> __device__ __forceinline__ int swz_key(int row) {
 }
 template <int RB> __device__ __forceinline__ int swz(int row, int chunk) {
   return row * RB + ((chunk ^ swz_key<RB>(row)) << 4);
-}
-
-// Workgroup barrier that also stops the scheduler from moving any instruction
-// (MFMAs included) across it, so phases stay where the code puts them.
-__device__ __forceinline__ void barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-
-// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and 15:14,
-// expcnt 6:4 left at 7, lgkmcnt 11:8 = 0).
-template <int N> __device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-
-// Wait until at most P * PER + (st ? NST : 0) vector-memory operations are
-// outstanding, for the largest P <= pend (pend <= PMAX).  PER is the number of
-// load instructions per slice and NST the number of stores one epilogue
-// issues; vmcnt counts loads and stores together and retires them in order.
-// Counts above the 6-bit field wait for 63 instead (a stricter wait).
-constexpr int vm_cap(int n) { return n > 63 ? 63 : n; }
-template <int PER, int NST, int P>
-__device__ __forceinline__ void wait_pending(int pend, bool st) {
-  if constexpr (P == 0) {
-    if (st) wait_vm<vm_cap(NST)>(); else wait_vm<0>();
-  } else {
-    if (pend >= P) {
-      if (st) wait_vm<vm_cap(P * PER + NST)>(); else wait_vm<vm_cap(P * PER)>();
-    } else {
-      wait_pending<PER, NST, P - 1>(pend, st);
-    }
-  }
-}
-
-// 16 bytes per lane from buffer `r` at byte offset `voff` into LDS at
-// lds + 16 * lane (lds must be the same for the whole wave).  Issued as inline
-// asm so the compiler does not track the LDS write: left to itself it waits for
-// every outstanding load before any LDS read, which would serialise the ring.
-// The waits for these loads are the explicit wait_pending<> calls.
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char *lds, uint32_t voff) {
-  const uint32_t m0 = (uint32_t)(uintptr_t)(void __attribute__((address_space(3))) *)lds;
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "buffer_load_dwordx4 %0, %1, 0 offen lds"
-      :
-      : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(m0))
-      : "memory", "m0");
 }
 
 // Activation of one (gate, up) pair.  Gated kinds evaluate the logistic

@@ -155,7 +155,8 @@ moe_status_t check_gate(const void *x, const void *w_gate, moe_dtype_t dt, int64
   if (hidden < 8 || hidden % 8 || hidden > (1 << 24) || e < 1 || e > moe::kMaxExperts || n < 0)
     return MOE_ERR_SHAPE;
   const int64_t lim = 0x7fffffff, es = (int64_t)dsize(dt);
-  if (n * hidden * es > lim || n * e * es > lim) return MOE_ERR_SHAPE;
+  if (n * hidden * es > lim || n * e * es > lim || (int64_t)e * hidden * es > lim)
+    return MOE_ERR_SHAPE;
   if (n == 0) return MOE_OK;
   return check_ptrs({x, w_gate, logits_out});
 }

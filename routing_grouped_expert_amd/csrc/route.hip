@@ -48,6 +48,7 @@
 // #45457 report ("implementation breakdown"), with the share given as the
 // (local_expert_offset, num_local_experts) pair of the kernel call in the PR
 // #47106 report ("key source snippets").
+#include "lds_dma.h"
 #include "moe_common.h"
 
 namespace moe {
@@ -395,8 +396,13 @@ constexpr int kGateRowBytes = 128;  // one K-slice of a row in LDS
 // Batches up to this size run the router GEMM in the one-workgroup routing
 // kernel's prologue; larger ones launch gate_gemm first.
 constexpr int kGateFusedTokens = 64;
-// LDS bytes of gate_logits<.., NT, ..>: NT token rows + up to 256 gate rows
-constexpr int gate_lds_bytes(int nt) { return (nt + kMaxExperts) * kGateRowBytes; }
+
+// Experts rounded up to the gate-row bucket the kernels are built for.
+inline int gate_bucket(int e) { return e <= 32 ? 32 : e <= 64 ? 64 : e <= 128 ? 128 : 256; }
+// Ring depth that fits `budget` LDS bytes (at most 8 stages).
+constexpr int gate_stages(int nt, int epb, int budget) {
+  return budget / ((nt + epb) * kGateRowBytes) < 8 ? budget / ((nt + epb) * kGateRowBytes) : 8;
+}
 
 // Byte offset of 16-byte chunk c of LDS row r: chunks are XOR-swizzled with
 // (r / 2) % 8, so the 16 lanes of a fragment read (16 consecutive rows, same
@@ -405,57 +411,66 @@ __device__ __forceinline__ int gate_swz(int r, int c) {
   return r * kGateRowBytes + ((c ^ ((r >> 1) & 7)) << 4);
 }
 
-// logits[t][e] for tokens t in [tok0, min(tok0 + NT, N)) and all E experts:
-// sum over h of x[t][h] * wg[e][h] in fp32, rounded once to T.  The token rows
-// and the gate rows go through LDS one 128-byte K-slice at a time (the next
-// slice's loads are in flight while the current one is multiplied); 32x32
-// output blocks (gate rows as the first MFMA operand, so a lane holds one token
-// and runs of 4 experts) are dealt to the waves.  Ends with every thread past
-// a barrier, its logits stored.
-template <typename T, int NT, int THREADS>
+// logits[t][e] for tokens t in [tok0, min(tok0 + NT, N)) and the E <= EPB
+// experts: sum over h of x[t][h] * wg[e][h] in fp32, rounded once to T.
+// Every K-slice of 128 bytes of the NT token rows and EPB gate rows (rows past
+// N or E read as zero) goes from memory straight into an S-stage LDS ring with
+// 16-byte DMA loads, issued S - 1 slices ahead by waves 0-3; every wave then
+// multiplies 32x32 output blocks on MFMA (gate rows as the first operand, so a
+// lane ends up holding one token and runs of 4 experts).  Uses S * (NT + EPB) *
+// 128 bytes of `lds` and ends with every thread past a barrier, the logits
+// stored.
+template <typename T, int NT, int THREADS, int EPB, int S>
 __device__ __forceinline__ void gate_logits(const T *__restrict__ x, const T *__restrict__ wg,
                                             int64_t N, int H, int E, int64_t tok0,
                                             T *__restrict__ logits, char *lds) {
   using Mm = GateMma<T>;
   constexpr int NW = THREADS / 64;
-  constexpr int MAXB = ((NT / 32) * (kMaxExperts / 32) + NW - 1) / NW;  // output blocks a wave
-  constexpr int U = ((NT + kMaxExperts) * 8 + THREADS - 1) / THREADS;  // chunk loads a thread
+  constexpr int RS = NT + EPB;                 // LDS rows of one stage
+  constexpr int STAGE = RS * kGateRowBytes;
+  constexpr int NWI = 4;                       // waves issuing the DMA loads
+  constexpr int PER = RS / 8 / NWI;            // 1 KB loads (8 rows) per issuing wave per slice
+  static_assert(RS % (8 * NWI) == 0 && NW >= NWI, "loads per issuing wave");
+  static_assert(S >= 2 && (S - 2) * PER < 64, "ring depth / vmcnt range");
+  // 32x32 output blocks over the whole NT x EPB tile (rows past N or E hold
+  // zeros and their results are not stored), dealt to the waves: block
+  // b = wave + j * NW is token block b % TBS, expert block b / TBS.  A fixed
+  // deal keeps the MFMA loop free of branches, so fragment reads overlap it.
+  constexpr int TBS = NT / 32, NBS = TBS * (EPB / 32);
+  constexpr int MAXB = (NBS + NW - 1) / NW;       // output blocks a wave
+  constexpr bool SAME_TB = NW % TBS == 0;         // one token block per wave
   constexpr int KSTEPS = kGateRowBytes / (Mm::KS * (int)sizeof(T));
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int live = (int)min<int64_t>(NT, N - tok0);
-  const int tbn = (live + 31) >> 5, ebn = (E + 31) >> 5;
-  const int xrows = tbn * 32, nchunks = (xrows + ebn * 32) * 8;
   const int rowb = H * (int)sizeof(T);  // bytes of one x / gate row (a multiple of 16)
   const int nslice = (rowb + kGateRowBytes - 1) / kGateRowBytes;
-  const char *xb = reinterpret_cast<const char *>(x);
-  const char *wb = reinterpret_cast<const char *>(wg);
-
-  u32x4_t pre[U];
-  auto fetch = [&](int sl) {
+  // buffer views: this chunk's token rows, and the gate weight
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<T *>(x) + tok0 * H, (short)0, live * rowb, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(wg), (short)0, E * rowb, kRsrcWord3);
+  // per load j of this wave: stage rows 8i .. 8i+7 for i = wave * PER + j; the
+  // lane fills physical chunk lane % 8 of row 8i + lane / 8 with the logical
+  // chunk that the swizzle puts there
+  uint32_t voff[PER], coff[PER];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int q = tid + u * THREADS;
-      const int r = q >> 3, kb = sl * kGateRowBytes + (q & 7) * 16;
-      pre[u] = u32x4_t{0u, 0u, 0u, 0u};
-      if (q < nchunks && kb < rowb) {
-        if (r < xrows) {
-          const int64_t t = tok0 + r;
-          if (t < N) pre[u] = *reinterpret_cast<const u32x4_t *>(xb + t * rowb + kb);
-        } else if (r - xrows < E) {
-          pre[u] = *reinterpret_cast<const u32x4_t *>(wb + (int64_t)(r - xrows) * rowb + kb);
-        }
-      }
-    }
-  };
-  auto stash = [&]() {
+  for (int j = 0; j < PER; ++j) {
+    const int r = (wave * PER + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    coff[j] = (uint32_t)c * 16;
+    const bool ok = r < NT ? r < live : r - NT < E;
+    voff[j] = ok ? (uint32_t)(r < NT ? r : r - NT) * (uint32_t)rowb + coff[j] : kOOB;
+  }
+  auto issue = [&](int z) {
+    const uint32_t kb = (uint32_t)z * kGateRowBytes;
+    const bool tail = (int)kb + kGateRowBytes > rowb;
+    char *base = lds + (z % S) * STAGE;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int q = tid + u * THREADS;
-      if (q < nchunks) {
-        const int r = q >> 3;
-        const int lr = r < xrows ? r : NT + (r - xrows);  // gate rows live after NT
-        *reinterpret_cast<u32x4_t *>(lds + gate_swz(lr, q & 7)) = pre[u];
-      }
+    for (int j = 0; j < PER; ++j) {
+      uint32_t off = voff[j] + kb;  // kOOB + kb stays out of range
+      if (tail && (int)(kb + coff[j]) >= rowb) off = kOOB;
+      dma16((wave * PER + j) * 8 < NT ? rx : rw, base + (wave * PER + j) * 1024, off);
     }
   };
 
@@ -464,35 +479,43 @@ __device__ __forceinline__ void gate_logits(const T *__restrict__ x, const T *__
   for (int j = 0; j < MAXB; ++j)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[j][i] = 0.f;
-  const int nb = tbn * ebn;
-  fetch(0);
-  for (int sl = 0; sl < nslice; ++sl) {
-    stash();
-    __syncthreads();
-    if (sl + 1 < nslice) fetch(sl + 1);
+  const bool busy = wave < NBS;  // waves past the block count only load and wait
+  if (wave < NWI) {
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int bo = (ks * Mm::KS + (lane >> 5) * Mm::EPL) * (int)sizeof(T);
+    for (int z = 0; z < S - 1; ++z)
+      if (z < nslice) issue(z);
+  }
+  for (int z = 0; z < nslice; ++z) {
+    if (wave < NWI) wait_pending<PER, 0, S - 2>(min(S - 2, nslice - 1 - z), false);
+    barrier();  // slice z is in LDS for every wave; slot (z - 1) % S is free
+    if (wave < NWI && z + S - 1 < nslice) issue(z + S - 1);
+    const char *st = lds + (z % S) * STAGE;
+    if (busy) {
 #pragma unroll
-      for (int j = 0; j < MAXB; ++j) {
-        const int b = wave + j * NW;
-        if (b < nb) {
-          const int tb = b % tbn, eb = b / tbn;
-          const int ra = NT + eb * 32 + (lane & 31), rx = tb * 32 + (lane & 31);
-          const typename Mm::Frag fa = Mm::ld(lds + gate_swz(ra, bo >> 4) + (bo & 15));
-          const typename Mm::Frag fx = Mm::ld(lds + gate_swz(rx, bo >> 4) + (bo & 15));
-          acc[j] = Mm::mma(fa, fx, acc[j]);
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int bo = (ks * Mm::KS + (lane >> 5) * Mm::EPL) * (int)sizeof(T);
+        typename Mm::Frag fa[MAXB], fx[MAXB];
+#pragma unroll
+        for (int j = 0; j < MAXB; ++j) {
+          const int b = min(wave + j * NW, NBS - 1);  // a wave's spare blocks repeat its last
+          const int ra = NT + (b / TBS) * 32 + (lane & 31);
+          fa[j] = Mm::ld(st + gate_swz(ra, bo >> 4) + (bo & 15));
+          if (!SAME_TB || j == 0) {
+            const int rt = (b % TBS) * 32 + (lane & 31);
+            fx[j] = Mm::ld(st + gate_swz(rt, bo >> 4) + (bo & 15));
+          }
         }
+#pragma unroll
+        for (int j = 0; j < MAXB; ++j) acc[j] = Mm::mma(fa[j], fx[SAME_TB ? 0 : j], acc[j]);
       }
     }
-    __syncthreads();
   }
   // lane: token tb*32 + lane%32; register r: expert eb*32 + 8(r/4) + 4(lane/32) + r%4
 #pragma unroll
   for (int j = 0; j < MAXB; ++j) {
     const int b = wave + j * NW;
-    if (b < nb) {
-      const int tb = b % tbn, eb = b / tbn;
+    if (b < NBS) {
+      const int tb = b % TBS, eb = b / TBS;
       const int64_t t = tok0 + tb * 32 + (lane & 31);
       if (t < N) {
 #pragma unroll
@@ -503,18 +526,20 @@ __device__ __forceinline__ void gate_logits(const T *__restrict__ x, const T *__
       }
     }
   }
-  __syncthreads();
+  __syncthreads();  // logits visible to the workgroup; the ring's LDS may be reused
 }
 
-// Router GEMM alone: one workgroup of 256 threads per 64 tokens.
-constexpr int kGateTokens = 64, kGateThreads = 256;
-template <typename T>
+// Router GEMM alone: one workgroup of 256 threads per NT tokens, all experts.
+constexpr int kGateThreads = 256;
+constexpr int kGateLdsBudget = 150 * 1024;
+template <typename T, int NT, int EPB>
 __global__ __launch_bounds__(kGateThreads) void gate_gemm(const T *__restrict__ x,
                                                           const T *__restrict__ wg, int64_t N,
                                                           int H, int E, T *__restrict__ logits) {
-  __shared__ __align__(16) char lds[gate_lds_bytes(kGateTokens)];
-  gate_logits<T, kGateTokens, kGateThreads>(x, wg, N, H, E, (int64_t)blockIdx.x * kGateTokens,
-                                            logits, lds);
+  constexpr int S = gate_stages(NT, EPB, kGateLdsBudget);
+  __shared__ __align__(16) char lds[S * (NT + EPB) * kGateRowBytes];
+  gate_logits<T, NT, kGateThreads, EPB, S>(x, wg, N, H, E, (int64_t)blockIdx.x * NT, logits,
+                                           lds);
 }
 
 // Batches of at most NT tokens: one workgroup, one launch.  Every per-entry
@@ -522,8 +547,11 @@ __global__ __launch_bounds__(kGateThreads) void gate_gemm(const T *__restrict__ 
 // GATE: the logits are first computed from x and the gate weight (router GEMM
 // prologue) and stored to `logits`, which the top-k phase then reads.
 // (The logits pointer carries no __restrict__: with GATE the same buffer is
-// written through logits_out first.)
-template <typename T, int THREADS, int C, typename Lds, bool GATE = false>
+// written through logits_out first.)  With GATE the GEMM's LDS ring and the
+// routing phases' LDS share one buffer: the ring is dead once the logits are
+// stored.
+constexpr int kFusedGateRing = 140 * 1024;
+template <typename T, int THREADS, int C, typename Lds, bool GATE = false, int EPB = 32>
 __global__ __launch_bounds__(THREADS) void route_fused(
     const T *logits, int64_t N, int E, int K, int lo, int nl, int logG, int vec,
     int32_t *__restrict__ topk_idx, T *__restrict__ topk_w, uint32_t *__restrict__ bitmatrix,
@@ -532,14 +560,16 @@ __global__ __launch_bounds__(THREADS) void route_fused(
     T *__restrict__ gate_scal, const T *__restrict__ x = nullptr, const T *__restrict__ wg = nullptr,
     int H = 0, T *logits_out = nullptr) {
   constexpr int NT = Lds::kTokens;
-  __shared__ Lds L;
+  constexpr int GS = gate_stages(kGateFusedTokens, EPB, kFusedGateRing);
+  constexpr int RING = GATE ? GS * (kGateFusedTokens + EPB) * kGateRowBytes : 0;
+  constexpr int RAW = RING > (int)sizeof(Lds) ? RING : (int)sizeof(Lds);
+  __shared__ __align__(16) char s_raw[RAW];
+  Lds &L = *reinterpret_cast<Lds *>(s_raw);
   __shared__ uint16_t s_rank[NT * Lds::kSlots];
   __shared__ int s_off[Lds::kExperts + 1];
   const int tid = threadIdx.x;
-  if constexpr (GATE) {  // N <= kGateFusedTokens
-    __shared__ __align__(16) char s_gemm[gate_lds_bytes(kGateFusedTokens)];
-    gate_logits<T, kGateFusedTokens, THREADS>(x, wg, N, H, E, 0, logits_out, s_gemm);
-  }
+  if constexpr (GATE)  // N <= kGateFusedTokens
+    gate_logits<T, kGateFusedTokens, THREADS, EPB, GS>(x, wg, N, H, E, 0, logits_out, s_raw);
   topk_chunk<T, THREADS, C>(logits, N, E, K, lo, nl, logG, vec, 0, topk_idx, topk_w, bitmatrix,
                             L);
   __syncthreads();
@@ -753,15 +783,38 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
   T *lw = const_cast<T *>(logits);
   if (x && N <= kGateFusedTokens) {  // router GEMM in the routing kernel's prologue
     // (batches this small take one logit chunk a lane: `wide` is false)
-    hipLaunchKernelGGL((route_fused<T, 1024, 1, ChunkLds<T, kFusedTokens>, true>), dim3(1),
-                       dim3(1024), 0, s, logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw,
-                       r->bitmatrix, r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs, x,
-                       wg, H, lw);
+    auto fused = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(1), dim3(1024), 0, s, logits, N, E, K, lo, nl, logG, vec,
+                         r->topk_idx, tw, r->bitmatrix, r->col_sum, r->offsets, r->col_sorted,
+                         r->row_sorted, gs, x, wg, H, lw);
+    };
+    using L = ChunkLds<T, kFusedTokens>;
+    switch (gate_bucket(E)) {
+      case 32: fused(route_fused<T, 1024, 1, L, true, 32>); break;
+      case 64: fused(route_fused<T, 1024, 1, L, true, 64>); break;
+      case 128: fused(route_fused<T, 1024, 1, L, true, 128>); break;
+      default: fused(route_fused<T, 1024, 1, L, true, 256>); break;
+    }
     return hipGetLastError();
   }
   if (x) {  // router GEMM as a kernel of its own, then the routing kernels
-    hipLaunchKernelGGL(gate_gemm<T>, dim3((unsigned)((N + kGateTokens - 1) / kGateTokens)),
-                       dim3(kGateThreads), 0, s, x, wg, N, H, E, lw);
+    // 32-token tiles spread a moderate batch over more compute units; 128-token
+    // tiles read the gate weight a quarter as often
+    const bool small = N <= 4096;
+    const unsigned g = (unsigned)((N + (small ? 31 : 127)) / (small ? 32 : 128));
+    auto gemm = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(g), dim3(kGateThreads), 0, s, x, wg, N, H, E, lw);
+    };
+    switch (gate_bucket(E) * (small ? 1 : -1)) {
+      case 32: gemm(gate_gemm<T, 32, 32>); break;
+      case 64: gemm(gate_gemm<T, 32, 64>); break;
+      case 128: gemm(gate_gemm<T, 32, 128>); break;
+      case 256: gemm(gate_gemm<T, 32, 256>); break;
+      case -32: gemm(gate_gemm<T, 128, 32>); break;
+      case -64: gemm(gate_gemm<T, 128, 64>); break;
+      case -128: gemm(gate_gemm<T, 128, 128>); break;
+      default: gemm(gate_gemm<T, 128, 256>); break;
+    }
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
