@@ -10,6 +10,8 @@ Python binding, and imports neither.
   offsets, stable expert-sorted gather/scatter indices, permuted gate weights).
 * :mod:`oracle.ffn` -- the expert FFN (SiLU-gated, SwiGLU-OAI, ReLU^2) run as the
   masked per-expert loop, the weighted combine, and the sorted-dispatch variant.
+* :mod:`oracle.ffn` also gives the layer with the routing weight on the input
+  rows (``moe_ffn_weighted_input``).
 * :mod:`oracle.routing` also gives the router logits from the gate weight
   (``gate_logits``, ``route_gate``).
 * both also give one GPU's expert-parallel share (``route_ep``,
@@ -23,11 +25,13 @@ to the pages) is marked "parity unpinned" where it is defined.
 from .routing import (RoutingRef, bitmatrix, gate_logits, histogram, offsets_from_hist,
                       remap_to_share, route, route_ep, route_gate, round_to_dtype, sorted_indices,
                       topk_select, topk_softmax)
-from .ffn import activation, moe_ffn, moe_ffn_share, moe_ffn_sorted, split_gate_up
+from .ffn import (activation, moe_ffn, moe_ffn_share, moe_ffn_sorted,
+                  moe_ffn_weighted_input, split_gate_up)
 
 __all__ = [
     "RoutingRef", "route", "topk_select", "topk_softmax", "bitmatrix", "histogram",
     "offsets_from_hist", "sorted_indices", "round_to_dtype", "remap_to_share", "route_ep",
     "gate_logits", "route_gate",
     "activation", "split_gate_up", "moe_ffn", "moe_ffn_sorted", "moe_ffn_share",
+    "moe_ffn_weighted_input",
 ]

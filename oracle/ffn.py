@@ -156,3 +156,28 @@ def moe_ffn_share(x, topk_idx, topk_w, w13, w2, act: str, local_offset: int,
     from .routing import remap_to_share
     loc = remap_to_share(topk_idx, local_offset, int(w13.shape[0]))
     return moe_ffn(x, loc, topk_w, w13, w2, act, layout, params, tokens=tokens)
+
+
+def moe_ffn_weighted_input(x, topk_idx, topk_w, w13, w2, act: str, dtype: str,
+                           layout: str = "packed", params: dict | None = None) -> np.ndarray:
+    """Layer output ``[N, H]`` (float64) with the routing weight applied to the
+    input rows (the ``apply_router_weight_on_input`` flag of the experts
+    ``apply`` in the vLLM PR #47106 report, section "key source snippets"):
+    masked per-expert loop as in ``moe_ffn``, but each routed row's input is
+    ``x[t] * w[t, j]`` rounded once to the layer ``dtype`` and the expert
+    output is added unweighted."""
+    from .routing import round_to_dtype
+    _check(act, layout, w13, w2)
+    xs = to_f64(x)
+    idx = np.asarray(topk_idx)
+    w = np.asarray(topk_w, dtype=np.float64)
+    out = np.zeros((xs.shape[0], w2.shape[1]), dtype=np.float64)
+    for e in range(w13.shape[0]):
+        mask = idx == e
+        if not mask.any():
+            continue
+        rows = np.flatnonzero(mask.any(axis=1))
+        wt = np.where(mask, w, 0.0).sum(axis=1)[rows]   # a token names e at most once
+        xin = round_to_dtype(xs[rows] * wt[:, None], dtype)
+        out[rows] += expert_ffn(xin, to_f64(w13[e]), to_f64(w2[e]), act, layout, params)
+    return out

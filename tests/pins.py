@@ -468,9 +468,47 @@ def pin_ffn_shares(seed=15):
     assert z.shape == x.shape and not z.any()
 
 
+def pin_ffn_weighted_input(seed=17):
+    """Routing weight on the input rows: a scalar token loop that scales and
+    rounds each slot's input row explicitly; the power-of-two closed form (for
+    ReLU^2, h(w x) = w^2 h(x) exactly when w is a power of two, so the result is
+    the output-weighted layer with weights w^2, bit for bit); top-1 with weight
+    1 is the plain layer."""
+    rng = np.random.default_rng(seed)
+    for act, layout, params, dt in [("silu", "packed", {}, "bf16"),
+                                    ("swiglu_oai", "interleaved",
+                                     {"alpha": 1.702, "beta": 1.0, "limit": 0.9}, "f32"),
+                                    ("relu2", "packed", {}, "bf16")]:
+        x, r, w13, w2 = _tiny_case(rng, act, layout, n=7, h=5, inter=4, e=3, k=2)
+        got = offn.moe_ffn_weighted_input(x, r.topk_idx, r.topk_w, w13, w2, act, dt, layout,
+                                          params)
+        n, k = r.topk_idx.shape
+        want = np.zeros_like(got)
+        for t in range(n):
+            for j in range(k):
+                xin = orout.round_to_dtype(x[t:t + 1] * float(r.topk_w[t, j]), dt)
+                one = np.ones((1, 1))
+                want[t] += brute_ffn(xin, r.topk_idx[t:t + 1, j:j + 1], one, w13, w2, act, layout,
+                                     params)[0]
+        assert np.allclose(got, want, rtol=1e-11, atol=1e-11), act
+    x, r, w13, w2 = _tiny_case(rng, "relu2", "packed", n=9, h=6, inter=5, e=4, k=2)
+    pw = 2.0 ** rng.integers(-3, 2, size=r.topk_w.shape)
+    a = offn.moe_ffn_weighted_input(x, r.topk_idx, pw, w13, w2, "relu2", "f32")
+    xr = orout.round_to_dtype(x, "f32")
+    b = offn.moe_ffn(xr, r.topk_idx, pw * pw, w13, w2, "relu2")
+    assert np.array_equal(a, b)
+    v = rng.normal(size=(9, 4))
+    r1 = orout.route(v, 1, "f32")
+    assert np.all(r1.topk_w == 1.0)
+    xb = orout.round_to_dtype(x, "bf16")
+    assert np.array_equal(
+        offn.moe_ffn_weighted_input(xb, r1.topk_idx, r1.topk_w, w13, w2, "relu2", "bf16"),
+        offn.moe_ffn(xb, r1.topk_idx, r1.topk_w, w13, w2, "relu2"))
+
+
 ROUTING_PINS = [pin_golden_routing, pin_topk_bruteforce, pin_topk_lexsort, pin_topk_special_cases,
                 pin_bf16_rounding, pin_weights_closed_forms, pin_metadata_invariants,
                 pin_empty_experts, pin_share_routing, pin_gate_logits]
 FFN_PINS = [pin_ffn_bruteforce, pin_ffn_masked_equals_sorted, pin_ffn_layout_invariance,
             pin_ffn_dense_special_case, pin_activation_closed_forms, pin_ffn_linearity,
-            pin_ffn_token_subset, pin_ffn_shares]
+            pin_ffn_token_subset, pin_ffn_shares, pin_ffn_weighted_input]

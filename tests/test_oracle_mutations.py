@@ -153,6 +153,27 @@ def gate_dropped_last_column(x, w, dtype):
     return _orig_gate(orout.to_f64(x)[:, :-1], orout.to_f64(w)[:, :-1], dtype)
 
 
+_orig_wi = offn.moe_ffn_weighted_input
+
+
+def weighted_input_unrounded(x, idx, w, w13, w2, act, dtype, layout="packed", params=None):
+    # the scaled input rows kept in float64 (the rounding to the layer dtype dropped)
+    xs, idx, w = orout.to_f64(x), np.asarray(idx), np.asarray(w, dtype=np.float64)
+    out = np.zeros((xs.shape[0], w2.shape[1]))
+    for e in range(w13.shape[0]):
+        mask = idx == e
+        if mask.any():
+            rows = np.flatnonzero(mask.any(axis=1))
+            wt = np.where(mask, w, 0.0).sum(axis=1)[rows]
+            out[rows] += offn.expert_ffn(xs[rows] * wt[:, None], orout.to_f64(w13[e]),
+                                         orout.to_f64(w2[e]), act, layout, params)
+    return out
+
+
+def weighted_input_on_output(x, idx, w, w13, w2, act, dtype, layout="packed", params=None):
+    return offn.moe_ffn(x, idx, w, w13, w2, act, layout, params)
+
+
 def remap_off_by_one(idx, lo, nl):
     r = _orig_remap(idx, lo, nl)
     return np.where(r >= 0, np.minimum(r + 1, nl - 1), -1).astype(np.int32)
@@ -192,6 +213,10 @@ MUTATIONS = [
     ("share ids not remapped (ffn)", orout, "remap_to_share", remap_none, "ffn"),
     ("share remap off by one (ffn)", orout, "remap_to_share", remap_off_by_one, "ffn"),
     ("gate logits not rounded", orout, "gate_logits", gate_not_rounded, "routing"),
+    ("weighted input not rounded", offn, "moe_ffn_weighted_input", weighted_input_unrounded,
+     "ffn"),
+    ("weight on output instead of input", offn, "moe_ffn_weighted_input",
+     weighted_input_on_output, "ffn"),
     ("gate rows swapped", orout, "gate_logits", gate_rows_swapped, "routing"),
     ("gate last hidden unit dropped", orout, "gate_logits", gate_dropped_last_column, "routing"),
 ]
