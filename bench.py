@@ -37,7 +37,8 @@ sys.path.insert(0, ROOT)
 from routing_grouped_expert_amd import (Routing, moe_workspace_bytes,  # noqa: E402
                                         prepare_experts_w13, prepare_experts_w2,
                                         prepare_forward, prepare_forward_ep,
-                                        prepare_gate_route, prepare_route, prepare_route_ep)
+                                        prepare_gate_forward, prepare_gate_route, prepare_route,
+                                        prepare_route_ep)
 from routing_grouped_expert_amd.synth import (act_params, layer_spec, make_layer,  # noqa: E402
                                               router_inputs, routing_logits)
 
@@ -328,6 +329,105 @@ def bench_gate_route(args, name: str):
     print(json.dumps(result), flush=True)
 
 
+def bench_decode_stack(args, name: str):
+    """decode<L>_n<N>: L chained layers shaped as gpt-oss-20b's MoE layers (32
+    experts, top-4, H = I = 2880, SwiGLU-OAI interleaved), N tokens, each layer
+    router GEMM + routing + experts (moe_gate_forward), its output the next
+    layer's input.  One step = the L layers; timed eager (L prepared calls) and
+    as one captured HIP graph replay, to show what capture saves on launches."""
+    import re
+    m = re.fullmatch(r"decode(\d+)_n(\d+)", name)
+    if not m:
+        raise SystemExit(f"unknown workload {name!r}")
+    L, n = int(m.group(1)), int(m.group(2))
+    e, k, h, i = 32, 4, 2880, 2880
+    prm = {"alpha": 1.702, "beta": 1.0, "limit": 7.0}
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    gen = torch.Generator(device=dev)
+
+    def draw(shape, std, seed):  # seeded on the GPU, one expert at a time, cast to bf16
+        gen.manual_seed(seed)
+        out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        for j in range(shape[0]):
+            out[j] = (torch.randn(shape[1:], generator=gen, device=dev) * std).to(torch.bfloat16)
+        return out
+
+    layers = [(draw((e, h), h ** -0.5, 3 * l), draw((e, 2 * i, h), 0.02, 3 * l + 1),
+               draw((e, h, i), 0.02, 3 * l + 2)) for l in range(L)]
+    x0, _ = router_inputs(n, e, h, "bf16", seed=0)
+    bufs = [x0.to(dev)] + [torch.empty(n, h, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    logits = torch.empty(n, e, dtype=torch.bfloat16, device=dev)
+    routing = Routing.empty(n, e, k, torch.bfloat16, dev)
+    ws = torch.empty(moe_workspace_bytes(n, e, k, h, i), dtype=torch.uint8, device=dev)
+
+    def prepared(stream):
+        return [prepare_gate_forward(bufs[l], wg, w13, w2, k, "swiglu_oai", "interleaved", prm,
+                                     out=bufs[l + 1], logits=logits, routing=routing,
+                                     workspace=ws, stream=stream)
+                for l, (wg, w13, w2) in enumerate(layers)]
+
+    stream = torch.cuda.current_stream(dev)
+    eager = prepared(stream)
+
+    def step():
+        for c in eager:
+            c()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ref = bufs[-1].clone()
+    st_eager = step_stats(step, args.steps, stream)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for c in prepared(side):
+            c()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        captured = prepared(torch.cuda.current_stream(dev))
+        for c in captured:
+            c()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(bufs[-1], ref))
+    st_graph = step_stats(g.replay, args.steps, stream)
+    # weights of the experts each layer's tokens touch, read once (counted in an
+    # untimed eager pass that reads every layer's histogram)
+    touched = []
+    for c in eager:
+        c()
+        touched.append(int((routing.col_sum > 0).sum()))
+    nbytes = sum(t * 3 * i * h * 2 + e * h * 2 + n * h * 2 * 2 for t in touched)
+    ms = st_graph["mean"]
+    ach = nbytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": round(n / (ms * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": st_graph["steps"], "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian token rows; weights drawn on the GPU from seeded "
+                "generators)",
+        "config": {"workload": f"{name}: {L} chained gpt-oss-20b-shaped MoE layers "
+                               f"(E=32 k=4 H=I=2880 swiglu_oai interleaved bf16), N={n}, "
+                               f"router GEMM + routing + experts per layer"},
+        "graph_us_per_step": round(ms * 1e3, 2),
+        "eager_us_per_step": round(st_eager["mean"] * 1e3, 2),
+        "graph_us_per_layer": round(ms * 1e3 / L, 2),
+        "eager_us_per_layer": round(st_eager["mean"] * 1e3 / L, 2),
+        "graph_replay_equals_eager": same,
+        "experts_touched_per_layer": touched,
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                     "kernel": "whole step (graph replay)", "traffic": None,
+                     "algorithmic_bytes": nbytes, "avg_launch_us": round(ms * 1e3, 2)},
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -356,6 +456,8 @@ def main():
         return bench_route_only(args, args.workload)
     if args.workload.startswith("gate_"):
         return bench_gate_route(args, args.workload)
+    if args.workload.startswith("decode"):
+        return bench_decode_stack(args, args.workload)
     spec = workload(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -179,6 +179,24 @@ moe_status_t moe_forward(const void *x, const void *logits, moe_dtype_t dtype,
                          const moe_routing_t *routing_out, void *out, void *workspace,
                          size_t ws_bytes, void *stream);
 
+/* ---- Routing weight on the input rows ---------------------------------------
+ * moe_experts_weighted_input: the experts apply() of the vLLM PR #47106 report
+ *   takes apply_router_weight_on_input ("key source snippets"); with it the
+ *   routing weight scales the expert's input instead of its output:
+ *     out[t] = sum over the token's slots j of W2[e] act(W13[e] xw),
+ *     xw = x[t] * gate, multiplied in fp32 and rounded once (nearest-even) to
+ *     `dtype`, the expert outputs summed in slot order with fp32 accumulation.
+ *   Arguments as moe_experts; the workspace must hold moe_workspace_bytes(...)
+ *   plus n_tokens * topk * hidden elements of `dtype` rounded up to 256 bytes
+ *   (the scaled input rows).  Any topk (the pages' kernels use it with 1). */
+moe_status_t moe_experts_weighted_input(const void *x, moe_dtype_t dtype, int64_t n_tokens,
+                                        int32_t hidden, const void *w13, const void *w2,
+                                        int32_t n_experts, int32_t inter, int32_t topk,
+                                        moe_act_t act, moe_w13_layout_t layout,
+                                        const moe_act_params_t *params,
+                                        const moe_routing_t *routing, void *out, void *workspace,
+                                        size_t ws_bytes, void *stream);
+
 /* ---- Router GEMM ahead of the routing ----------------------------------------
  * The router's gate matmul, logits = x . w_gate^T, is the step just before
  * the top-k; the vLLM PR #45457 report leaves it to its own kernel

@@ -40,7 +40,8 @@ __all__ = ["Routing", "MoeError", "Prepared", "moe_route", "moe_experts", "moe_e
            "prepare_experts_w13", "prepare_experts_w2", "prepare_forward",
            "moe_route_ep", "moe_experts_ep", "moe_forward_ep", "prepare_route_ep",
            "prepare_experts_ep", "prepare_forward_ep", "moe_gate_route", "moe_gate_forward",
-           "prepare_gate_route", "prepare_gate_forward",
+           "prepare_gate_route", "prepare_gate_forward", "moe_experts_weighted_input",
+           "prepare_experts_weighted_input",
            "moe_workspace_bytes", "moe_status_str", "ACTS", "LAYOUTS"]
 
 _DT = {torch.float32: N.MOE_F32, torch.bfloat16: N.MOE_BF16}
@@ -516,3 +517,38 @@ def moe_gate_forward(x: torch.Tensor, w_gate: torch.Tensor, w13: torch.Tensor, w
     return prepare_gate_forward(x, w_gate, w13, w2, topk, act, layout, params, out=out,
                                 logits=logits, routing=routing, workspace=workspace,
                                 stream=stream)()
+
+
+def prepare_experts_weighted_input(x, w13, w2, routing: Routing, act: str,
+                                   layout: str = "packed", params: Optional[dict] = None, *,
+                                   out=None, workspace=None, stream=None) -> Prepared:
+    dev = _dev(x, w13, w2)
+    _shapes(x, w13, w2, act, out)
+    n, hidden = x.shape
+    e, inter = w2.shape[0], w2.shape[2]
+    k = routing.topk
+    _check_routing(routing, n, e, k)
+    if out is None:
+        out = torch.empty_like(x)
+    # the scaled input rows xs [N*k, hidden] follow the experts' workspace
+    need = moe_workspace_bytes(n, max(e, k), k, hidden, inter, x.dtype) \
+        + (n * k * hidden * x.element_size() + 255) // 256 * 256
+    ws = _workspace(workspace, need, dev)
+    r = routing.as_c()
+    p = _params(params)
+    args = (x.data_ptr(), _dt(x), n, hidden, w13.data_ptr(), w2.data_ptr(), e, inter, k,
+            ACTS[act], LAYOUTS[layout], ctypes.byref(p) if p else None, ctypes.byref(r),
+            out.data_ptr(), ws.data_ptr(), _nbytes(ws), _stream(dev, stream))
+    return Prepared("moe_experts_weighted_input", args, (r, p, x, w13, w2, out, ws, routing), out)
+
+
+def moe_experts_weighted_input(x: torch.Tensor, w13: torch.Tensor, w2: torch.Tensor,
+                               routing: Routing, act: str, layout: str = "packed",
+                               params: Optional[dict] = None, *,
+                               out: Optional[torch.Tensor] = None,
+                               workspace: Optional[torch.Tensor] = None,
+                               stream=None) -> torch.Tensor:
+    """Expert FFN with the routing weight applied to each entry's input row
+    (rounded to the layer dtype) instead of its output (see moe.h)."""
+    return prepare_experts_weighted_input(x, w13, w2, routing, act, layout, params, out=out,
+                                          workspace=workspace, stream=stream)()

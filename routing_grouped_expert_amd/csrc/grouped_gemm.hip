@@ -325,8 +325,11 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
         const uint32_t arow = g.gather ? (uint32_t)(g.col_sorted[p] / g.topk) : (uint32_t)p;
         va[j] = arow * (uint32_t)kbytes + (((lane % CPR) ^ swz_key<RB>(r)) << 4);
         if (META && lane % CPR == 0) {
-          const float gs = g.gate_bf16 ? to_f32(reinterpret_cast<const bf16_t *>(g.gate_scal)[p])
-                                       : reinterpret_cast<const float *>(g.gate_scal)[p];
+          // no gate weights: the routing weight was applied to the input rows
+          const float gs = !g.gate_scal ? 1.f
+                           : g.gate_bf16
+                               ? to_f32(reinterpret_cast<const bf16_t *>(g.gate_scal)[p])
+                               : reinterpret_cast<const float *>(g.gate_scal)[p];
           i32x2_t m;
           m[0] = EPI == EPI_OUT ? g.col_sorted[p] : p;  // topk == 1: entry index == token
           m[1] = __float_as_int(gs);
@@ -616,11 +619,14 @@ hipError_t launch_t(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
 hipError_t launch_gemm1(const void *x, const void *w13, void *act_out, const int32_t *offsets,
                         const int32_t *col_sorted, moe_dtype_t dt, int64_t n_tokens, int topk,
                         int n_experts, int hidden, int inter, moe_act_t act,
-                        moe_w13_layout_t layout, ActParams p, hipStream_t s) {
+                        moe_w13_layout_t layout, ActParams p, hipStream_t s, bool sorted_rows) {
   const int64_t M = n_tokens * topk;
   const size_t es = dt == MOE_BF16 ? 2 : 4;
-  GemmArgs a{x, w13, act_out, offsets, col_sorted, nullptr, (uint32_t)(n_tokens * hidden * es),
-             (uint32_t)(M * inter * es), 0, n_experts, hidden, inter, topk, 1,
+  // A is x [N, hidden] read through the gather index, or (sorted_rows) rows
+  // already in sorted order [M, hidden]
+  const int64_t a_rows = sorted_rows ? M : n_tokens;
+  GemmArgs a{x, w13, act_out, offsets, col_sorted, nullptr, (uint32_t)(a_rows * hidden * es),
+             (uint32_t)(M * inter * es), 0, n_experts, hidden, inter, topk, sorted_rows ? 0 : 1,
              layout == MOE_W13_INTERLEAVED, act, p};
   const bool gated = act != MOE_ACT_RELU2;
   const bool clamp = std::isfinite(p.limit);  // an infinite limit clamps nothing

@@ -176,11 +176,12 @@ hipError_t run_w13(const void *x, moe_dtype_t dtype, int64_t n, int32_t hidden, 
 
 hipError_t run_w2(const void *a, moe_dtype_t dtype, int64_t n, int32_t hidden, const void *w2,
                   int32_t e, int32_t inter, int32_t k, const moe_routing_t *r, void *out, void *y,
-                  hipStream_t s, bool share = false) {
+                  hipStream_t s, bool share = false, bool unit_gate = false) {
   const bool direct = k == 1;  // one row per token: GEMM2 writes the output rows itself
   hipError_t err = moe::launch_gemm2(a, w2, direct ? out : y, r->offsets, r->col_sorted,
-                                     r->gate_scal, (moe_dtype_t)r->w_dtype, dtype, n, k, e,
-                                     hidden, inter, direct, s);
+                                     unit_gate ? nullptr : r->gate_scal,
+                                     (moe_dtype_t)r->w_dtype, dtype, n, k, e, hidden, inter,
+                                     direct, s);
   if (err != hipSuccess) return err;
   // an expert share leaves the rows of tokens routed elsewhere to be zeroed
   if (direct) return share ? moe::launch_zero_unrouted(r->row_sorted, out, dtype, n, hidden, s)
@@ -385,6 +386,38 @@ moe_status_t moe_gate_forward(const void *x, const void *w_gate, moe_dtype_t dty
     return MOE_ERR_HIP;
   return run_experts(x, dtype, n_tokens, hidden, w13, w2, n_experts, inter, topk, act, layout,
                      prm, routing_out, out, workspace, s);
+}
+
+moe_status_t moe_experts_weighted_input(const void *x, moe_dtype_t dtype, int64_t n_tokens,
+                                        int32_t hidden, const void *w13, const void *w2,
+                                        int32_t n_experts, int32_t inter, int32_t topk,
+                                        moe_act_t act, moe_w13_layout_t layout,
+                                        const moe_act_params_t *params,
+                                        const moe_routing_t *routing, void *out, void *workspace,
+                                        size_t ws_bytes, void *stream) {
+  ActParams prm;
+  moe_status_t st = check_expert_args(dtype, n_tokens, hidden, n_experts, inter, topk, act,
+                                      layout, params, routing, &prm);
+  if (st != MOE_OK || n_tokens == 0) return st;
+  if ((st = check_ptrs({x, w13, w2, out})) != MOE_OK) return st;
+  const size_t base = experts_ws_bytes(n_tokens, topk, hidden, inter, dtype);
+  const size_t xs_bytes = align256((size_t)n_tokens * topk * hidden * dsize(dtype));
+  if ((st = check_ws(workspace, ws_bytes, base + xs_bytes)) != MOE_OK) return st;
+  // workspace: a[M, inter], (topk > 1) y[M, hidden], then the scaled rows xs[M, hidden]
+  hipStream_t s = (hipStream_t)stream;
+  char *ws = reinterpret_cast<char *>(workspace);
+  void *a = ws;
+  void *y = ws + align256((size_t)n_tokens * topk * inter * dsize(dtype));
+  void *xs = ws + base;
+  if (moe::launch_scale_gather(x, routing->col_sorted, routing->gate_scal,
+                               (moe_dtype_t)routing->w_dtype, routing->offsets, n_experts, dtype,
+                               n_tokens, topk, hidden, xs, s) != hipSuccess ||
+      moe::launch_gemm1(xs, w13, a, routing->offsets, routing->col_sorted, dtype, n_tokens, topk,
+                        n_experts, hidden, inter, act, layout, prm, s, true) != hipSuccess ||
+      run_w2(a, dtype, n_tokens, hidden, w2, n_experts, inter, topk, routing, out, y, s, false,
+             true) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
 }
 
 const char *moe_status_str(moe_status_t status) {

@@ -61,9 +61,10 @@ struct ActParams {
 hipError_t launch_gemm1(const void *x, const void *w13, void *act_out, const int32_t *offsets,
                         const int32_t *col_sorted, moe_dtype_t dt, int64_t n_tokens, int topk,
                         int n_experts, int hidden, int inter, moe_act_t act,
-                        moe_w13_layout_t layout, ActParams p, hipStream_t s);
-// GEMM2: y = gate_scal[p] * (a[p] . W2[e]^T); stored to y_sorted[M, hidden], or
-// (topk == 1) straight to out[token(p)].
+                        moe_w13_layout_t layout, ActParams p, hipStream_t s,
+                        bool sorted_rows = false);
+// GEMM2: y = gate_scal[p] * (a[p] . W2[e]^T) (gate_scal NULL: weight 1); stored
+// to y_sorted[M, hidden], or (topk == 1) straight to out[token(p)].
 hipError_t launch_gemm2(const void *act_in, const void *w2, void *y, const int32_t *offsets,
                         const int32_t *col_sorted, const void *gate_scal, moe_dtype_t gate_dt,
                         moe_dtype_t dt, int64_t n_tokens, int topk, int n_experts, int hidden,
@@ -72,6 +73,13 @@ hipError_t launch_gemm2(const void *act_in, const void *w2, void *y, const int32
 // with row_sorted = -1 skipped.
 hipError_t launch_combine(const void *y_sorted, const int32_t *row_sorted, void *out,
                           moe_dtype_t dt, int64_t n_tokens, int topk, int hidden, hipStream_t s);
+// xs[p] = RNE(gate_scal[p] * x[col_sorted[p] / topk]) for the routed rows
+// p < offsets[n_experts]: the input rows of each entry, in sorted order and
+// scaled by the entry's routing weight.
+hipError_t launch_scale_gather(const void *x, const int32_t *col_sorted, const void *gate_scal,
+                               moe_dtype_t gate_dt, const int32_t *offsets, int n_experts,
+                               moe_dtype_t dt, int64_t n_tokens, int topk, int hidden, void *xs,
+                               hipStream_t s);
 // topk == 1: out[t] = 0 where row_sorted[t] = -1.
 hipError_t launch_zero_unrouted(const int32_t *row_sorted, void *out, moe_dtype_t dt,
                                 int64_t n_tokens, int hidden, hipStream_t s);
