@@ -278,7 +278,7 @@ def bench_gate_route(args, name: str):
     x, w = x_cpu.to(dev), w_cpu.to(dev)
     lg = torch.empty(n, e, dtype=torch.bfloat16, device=dev)
     routing = Routing.empty(n, e, k, torch.bfloat16, dev)
-    ws = torch.empty(max(1, moe_workspace_bytes(n, e, k)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(1, moe_workspace_bytes(n, e, k, h)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     p_gate = prepare_gate_route(x, w, k, logits=lg, routing=routing, workspace=ws, stream=stream)
     p_route = prepare_route(lg, k, routing=routing, workspace=ws, stream=stream)

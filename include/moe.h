@@ -122,7 +122,8 @@ typedef struct {
 } moe_routing_t;
 
 /* Bytes of device workspace sufficient for moe_route (pass hidden = inter = 0),
- * moe_experts and moe_forward with these sizes.  Returns 0 on invalid sizes. */
+ * moe_gate_route (pass hidden, inter = 0), moe_experts, moe_forward and
+ * moe_gate_forward (pass both) with these sizes.  Returns 0 on invalid sizes. */
 size_t moe_workspace_bytes(int64_t n_tokens, int32_t n_experts, int32_t topk,
                            int32_t hidden, int32_t inter, moe_dtype_t dtype);
 
@@ -207,9 +208,11 @@ moe_status_t moe_experts_weighted_input(const void *x, moe_dtype_t dtype, int64_
  *   receives logits[t][e] = sum_h x[t][h] * w_gate[e][h], accumulated in fp32
  *   and rounded once (nearest-even) to `dtype`; then everything moe_route
  *   computes from those logits goes to *out (out->w_dtype == dtype).  The same
- *   result as writing the logits and calling moe_route on them.  Workspace and
- *   limits as moe_route; hidden a positive multiple of 8; x and logits_out
- *   below 2^31 bytes.
+ *   result as writing the logits and calling moe_route on them.  Workspace:
+ *   moe_workspace_bytes(n_tokens, n_experts, topk, hidden, 0, dtype) (small
+ *   batches keep per-K-slice partial sums of the product there); limits as
+ *   moe_route; hidden a positive multiple of 8; x, w_gate and logits_out below
+ *   2^31 bytes.
  * moe_gate_forward: moe_gate_route then moe_experts, on one stream. */
 moe_status_t moe_gate_route(const void *x, const void *w_gate, moe_dtype_t dtype,
                             int64_t n_tokens, int32_t hidden, int32_t n_experts, int32_t topk,

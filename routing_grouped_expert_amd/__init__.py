@@ -467,7 +467,7 @@ def prepare_gate_route(x: torch.Tensor, w_gate: torch.Tensor, topk: int, *,
     if routing is None:
         routing = Routing.empty(n, e, topk, x.dtype, dev)
     _check_routing(routing, n, e, topk)
-    ws = _workspace(workspace, moe_workspace_bytes(n, e, topk, 0, 0, x.dtype), dev)
+    ws = _workspace(workspace, moe_workspace_bytes(n, e, topk, x.shape[1], 0, x.dtype), dev)
     r = routing.as_c()
     args = (x.data_ptr(), w_gate.data_ptr(), _dt(x), n, x.shape[1], e, topk, logits.data_ptr(),
             ctypes.byref(r), ws.data_ptr(), _nbytes(ws), _stream(dev, stream))

@@ -212,12 +212,14 @@ extern "C" {
 size_t moe_workspace_bytes(int64_t n_tokens, int32_t n_experts, int32_t topk, int32_t hidden,
                            int32_t inter, moe_dtype_t dtype) {
   if (check_sizes(n_tokens, n_experts, topk) != MOE_OK || !dtype_ok(dtype)) return 0;
-  size_t route = moe::route_scratch_bytes(n_tokens, n_experts, topk);
+  if (inter != 0 && check_ffn_sizes(hidden, inter) != MOE_OK) return 0;
+  if (inter == 0 && hidden != 0 && check_ffn_sizes(hidden, 8) != MOE_OK) return 0;
+  // routing scratch, plus the router GEMM's when hidden is given; the expert
+  // intermediates reuse the same bytes once the routing has run
+  const size_t route = moe::route_scratch_bytes(n_tokens, n_experts, topk) +
+                       (hidden ? moe::gate_scratch_bytes(n_tokens, n_experts, hidden, dtype) : 0);
   size_t ffn = 0;
-  if (hidden != 0 || inter != 0) {
-    if (check_ffn_sizes(hidden, inter) != MOE_OK) return 0;
-    ffn = experts_ws_bytes(n_tokens, topk, hidden, inter, dtype);
-  }
+  if (inter != 0) ffn = experts_ws_bytes(n_tokens, topk, hidden, inter, dtype);
   const size_t b = route > ffn ? route : ffn;
   return b ? b : 256;
 }
@@ -359,6 +361,9 @@ moe_status_t moe_gate_route(const void *x, const void *w_gate, moe_dtype_t dtype
   if (st != MOE_OK) return st;
   st = check_route(logits_out, dtype, n_tokens, n_experts, topk, out, workspace, ws_bytes);
   if (st != MOE_OK || n_tokens == 0) return st;
+  if (ws_bytes < moe::route_scratch_bytes(n_tokens, n_experts, topk) +
+                     moe::gate_scratch_bytes(n_tokens, n_experts, hidden, dtype))
+    return MOE_ERR_WORKSPACE;
   if (moe::launch_route(logits_out, dtype, n_tokens, n_experts, topk, 0, n_experts, out,
                         workspace, (hipStream_t)stream, x, w_gate, hidden) != hipSuccess)
     return MOE_ERR_HIP;
@@ -380,6 +385,9 @@ moe_status_t moe_gate_forward(const void *x, const void *w_gate, moe_dtype_t dty
   st = check_experts(x, dtype, n_tokens, hidden, w13, w2, n_experts, inter, topk, act, layout,
                      params, routing_out, out, workspace, ws_bytes, &prm);
   if (st != MOE_OK || n_tokens == 0) return st;
+  if (ws_bytes < moe::route_scratch_bytes(n_tokens, n_experts, topk) +
+                     moe::gate_scratch_bytes(n_tokens, n_experts, hidden, dtype))
+    return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   if (moe::launch_route(logits_out, dtype, n_tokens, n_experts, topk, 0, n_experts, routing_out,
                         workspace, s, x, w_gate, hidden) != hipSuccess)

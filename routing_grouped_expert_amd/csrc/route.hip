@@ -392,45 +392,59 @@ template <> struct GateMma<float> {
   }
 };
 
-constexpr int kGateRowBytes = 128;  // one K-slice of a row in LDS
-// Batches up to this size run the router GEMM in the one-workgroup routing
-// kernel's prologue; larger ones launch gate_gemm first.
+constexpr int kGateRowBytes = 256;  // one K-slice of a row in LDS (preferred)
+// Batches up to this size finish the router GEMM in the one-workgroup routing
+// kernel's prologue; larger ones launch gate_gemm first.  kGateSplitK: the
+// prologue adds up K-slice sums that gate_partial spread over many compute
+// units, instead of computing the whole product on one.
 constexpr int kGateFusedTokens = 64;
+constexpr bool kGateSplitK = true;
 
 // Experts rounded up to the gate-row bucket the kernels are built for.
 inline int gate_bucket(int e) { return e <= 32 ? 32 : e <= 64 ? 64 : e <= 128 ? 128 : 256; }
-// Ring depth that fits `budget` LDS bytes (at most 8 stages).
-constexpr int gate_stages(int nt, int epb, int budget) {
-  return budget / ((nt + epb) * kGateRowBytes) < 8 ? budget / ((nt + epb) * kGateRowBytes) : 8;
+// Ring depth that fits `budget` LDS bytes with rows of rb bytes (at most 8).
+constexpr int gate_stages(int nt, int epb, int budget, int rb) {
+  return budget / ((nt + epb) * rb) < 8 ? budget / ((nt + epb) * rb) : 8;
+}
+// Row bytes of a tile: the preferred slice unless two stages of it do not fit.
+constexpr int gate_row_bytes(int nt, int epb, int budget) {
+  return gate_stages(nt, epb, budget, kGateRowBytes) >= 2 ? kGateRowBytes : 128;
 }
 
-// Byte offset of 16-byte chunk c of LDS row r: chunks are XOR-swizzled with
-// (r / 2) % 8, so the 16 lanes of a fragment read (16 consecutive rows, same
-// chunk) land in different bank groups.
-__device__ __forceinline__ int gate_swz(int r, int c) {
-  return r * kGateRowBytes + ((c ^ ((r >> 1) & 7)) << 4);
+// Byte offset of 16-byte chunk c of LDS row r.  A ds_read_b128 serves 16
+// lanes at a time from 256 bytes of banks, i.e. from 256 / kGateRowBytes rows;
+// XOR-ing the chunk with (r / (256 / kGateRowBytes)) % (kGateRowBytes / 16)
+// puts the 16 lanes of a fragment read (16 consecutive rows, same chunk) in
+// different bank groups.
+template <int RB> __device__ __forceinline__ int gate_swz(int r, int c) {
+  return r * RB + ((c ^ ((r / (256 / RB)) % (RB / 16))) << 4);
 }
 
 // logits[t][e] for tokens t in [tok0, min(tok0 + NT, N)) and the E <= EPB
 // experts: sum over h of x[t][h] * wg[e][h] in fp32, rounded once to T.
-// Every K-slice of 128 bytes of the NT token rows and EPB gate rows (rows past
+// Every K-slice of RB bytes of the NT token rows and EPB gate rows (rows past
 // N or E read as zero) goes from memory straight into an S-stage LDS ring with
 // 16-byte DMA loads, issued S - 1 slices ahead by waves 0-3; every wave then
 // multiplies 32x32 output blocks on MFMA (gate rows as the first operand, so a
 // lane ends up holding one token and runs of 4 experts).  Uses S * (NT + EPB) *
-// 128 bytes of `lds` and ends with every thread past a barrier, the logits
-// stored.
-template <typename T, int NT, int THREADS, int EPB, int S>
+// RB bytes of `lds` and ends with every thread past a barrier, the logits
+// stored.  PART: only the K-slices [zb, ze) are summed and the fp32 sums are
+// stored to part[((t - tok0) * E + e) * pstride] instead.
+template <typename T, int NT, int THREADS, int EPB, int S, int RB, bool PART = false>
 __device__ __forceinline__ void gate_logits(const T *__restrict__ x, const T *__restrict__ wg,
                                             int64_t N, int H, int E, int64_t tok0,
-                                            T *__restrict__ logits, char *lds) {
+                                            T *__restrict__ logits, char *lds, int zb = 0,
+                                            int ze = -1, float *__restrict__ part = nullptr,
+                                            int pstride = 1) {
   using Mm = GateMma<T>;
   constexpr int NW = THREADS / 64;
   constexpr int RS = NT + EPB;                 // LDS rows of one stage
-  constexpr int STAGE = RS * kGateRowBytes;
+  constexpr int STAGE = RS * RB;
   constexpr int NWI = 4;                       // waves issuing the DMA loads
-  constexpr int PER = RS / 8 / NWI;            // 1 KB loads (8 rows) per issuing wave per slice
-  static_assert(RS % (8 * NWI) == 0 && NW >= NWI, "loads per issuing wave");
+  constexpr int CPR = RB / 16;                 // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;                // rows per 1 KB load
+  constexpr int PER = RS / RPI / NWI;          // 1 KB loads per issuing wave per slice
+  static_assert(RS % (RPI * NWI) == 0 && NT % RPI == 0 && NW >= NWI, "loads per issuing wave");
   static_assert(S >= 2 && (S - 2) * PER < 64, "ring depth / vmcnt range");
   // 32x32 output blocks over the whole NT x EPB tile (rows past N or E hold
   // zeros and their results are not stored), dealt to the waves: block
@@ -439,38 +453,39 @@ __device__ __forceinline__ void gate_logits(const T *__restrict__ x, const T *__
   constexpr int TBS = NT / 32, NBS = TBS * (EPB / 32);
   constexpr int MAXB = (NBS + NW - 1) / NW;       // output blocks a wave
   constexpr bool SAME_TB = NW % TBS == 0;         // one token block per wave
-  constexpr int KSTEPS = kGateRowBytes / (Mm::KS * (int)sizeof(T));
+  constexpr int KSTEPS = RB / (Mm::KS * (int)sizeof(T));
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int live = (int)min<int64_t>(NT, N - tok0);
   const int rowb = H * (int)sizeof(T);  // bytes of one x / gate row (a multiple of 16)
-  const int nslice = (rowb + kGateRowBytes - 1) / kGateRowBytes;
+  if (ze < 0) ze = (rowb + RB - 1) / RB;
+  const int nslice = ze - zb;  // slices of this call
   // buffer views: this chunk's token rows, and the gate weight
   const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<T *>(x) + tok0 * H, (short)0, live * rowb, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rw =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(wg), (short)0, E * rowb, kRsrcWord3);
-  // per load j of this wave: stage rows 8i .. 8i+7 for i = wave * PER + j; the
-  // lane fills physical chunk lane % 8 of row 8i + lane / 8 with the logical
-  // chunk that the swizzle puts there
+  // per load j of this wave: RPI stage rows from RPI * i for i = wave * PER + j;
+  // the lane fills physical chunk lane % CPR of row RPI * i + lane / CPR with
+  // the logical chunk that the swizzle puts there
   uint32_t voff[PER], coff[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int r = (wave * PER + j) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    const int r = (wave * PER + j) * RPI + lane / CPR;
+    const int c = (gate_swz<RB>(r, lane % CPR) - r * RB) >> 4;  // XOR is an involution
     coff[j] = (uint32_t)c * 16;
     const bool ok = r < NT ? r < live : r - NT < E;
     voff[j] = ok ? (uint32_t)(r < NT ? r : r - NT) * (uint32_t)rowb + coff[j] : kOOB;
   }
   auto issue = [&](int z) {
-    const uint32_t kb = (uint32_t)z * kGateRowBytes;
-    const bool tail = (int)kb + kGateRowBytes > rowb;
+    const uint32_t kb = (uint32_t)(zb + z) * RB;
+    const bool tail = (int)kb + RB > rowb;
     char *base = lds + (z % S) * STAGE;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
       uint32_t off = voff[j] + kb;  // kOOB + kb stays out of range
       if (tail && (int)(kb + coff[j]) >= rowb) off = kOOB;
-      dma16((wave * PER + j) * 8 < NT ? rx : rw, base + (wave * PER + j) * 1024, off);
+      dma16((wave * PER + j) * RPI < NT ? rx : rw, base + (wave * PER + j) * 1024, off);
     }
   };
 
@@ -499,10 +514,10 @@ __device__ __forceinline__ void gate_logits(const T *__restrict__ x, const T *__
         for (int j = 0; j < MAXB; ++j) {
           const int b = min(wave + j * NW, NBS - 1);  // a wave's spare blocks repeat its last
           const int ra = NT + (b / TBS) * 32 + (lane & 31);
-          fa[j] = Mm::ld(st + gate_swz(ra, bo >> 4) + (bo & 15));
+          fa[j] = Mm::ld(st + gate_swz<RB>(ra, bo >> 4) + (bo & 15));
           if (!SAME_TB || j == 0) {
             const int rt = (b % TBS) * 32 + (lane & 31);
-            fx[j] = Mm::ld(st + gate_swz(rt, bo >> 4) + (bo & 15));
+            fx[j] = Mm::ld(st + gate_swz<RB>(rt, bo >> 4) + (bo & 15));
           }
         }
 #pragma unroll
@@ -521,13 +536,29 @@ __device__ __forceinline__ void gate_logits(const T *__restrict__ x, const T *__
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int e = eb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (e < E) logits[t * E + e] = from_f32<T>(acc[j][r]);
+          if (e < E) {
+            if constexpr (PART)
+              part[((t - tok0) * E + e) * pstride] = acc[j][r];
+            else
+              logits[t * E + e] = from_f32<T>(acc[j][r]);
+          }
         }
       }
     }
   }
   __syncthreads();  // logits visible to the workgroup; the ring's LDS may be reused
 }
+
+// Router GEMM of a small batch (N <= kGateFusedTokens) split over K: workgroup
+// z sums K-slice z of every token and expert and stores the fp32 sums to
+// part[(t * E + e) * npad + z] (a logit's slices contiguous, npad a multiple of
+// 4); the routing kernel adds them up.  The gate weight is read by as many
+// compute units as it has slices instead of by one.
+constexpr int kGateMaxParts = 64;  // more K-slices than this: the one-workgroup GEMM
+template <typename T, int EPB>
+__global__ __launch_bounds__(256) void gate_partial(const T *__restrict__ x,
+                                                    const T *__restrict__ wg, int64_t N, int H,
+                                                    int E, float *__restrict__ part, int npad);
 
 // Router GEMM alone: one workgroup of 256 threads per NT tokens, all experts.
 constexpr int kGateThreads = 256;
@@ -536,10 +567,29 @@ template <typename T, int NT, int EPB>
 __global__ __launch_bounds__(kGateThreads) void gate_gemm(const T *__restrict__ x,
                                                           const T *__restrict__ wg, int64_t N,
                                                           int H, int E, T *__restrict__ logits) {
-  constexpr int S = gate_stages(NT, EPB, kGateLdsBudget);
-  __shared__ __align__(16) char lds[S * (NT + EPB) * kGateRowBytes];
-  gate_logits<T, NT, kGateThreads, EPB, S>(x, wg, N, H, E, (int64_t)blockIdx.x * NT, logits,
-                                           lds);
+  constexpr int RB = gate_row_bytes(NT, EPB, kGateLdsBudget);
+  constexpr int S = gate_stages(NT, EPB, kGateLdsBudget, RB);
+  __shared__ __align__(16) char lds[S * (NT + EPB) * RB];
+  gate_logits<T, NT, kGateThreads, EPB, S, RB>(x, wg, N, H, E, (int64_t)blockIdx.x * NT, logits,
+                                               lds);
+}
+
+// Row bytes of the split-K router GEMM's slices (one slice a workgroup), and
+// the number of slices of a row of rowb bytes.
+constexpr int gate_part_rb(int epb) { return gate_row_bytes(kGateFusedTokens, epb, kGateLdsBudget); }
+inline int gate_parts(int e, int rowb) {
+  const int rb = gate_part_rb(gate_bucket(e));
+  return (rowb + rb - 1) / rb;
+}
+template <typename T, int EPB>
+__global__ __launch_bounds__(256) void gate_partial(const T *__restrict__ x,
+                                                    const T *__restrict__ wg, int64_t N, int H,
+                                                    int E, float *__restrict__ part, int npad) {
+  constexpr int RB = gate_part_rb(EPB);
+  __shared__ __align__(16) char lds[2 * (kGateFusedTokens + EPB) * RB];
+  const int z = blockIdx.x;
+  gate_logits<T, kGateFusedTokens, kGateThreads, EPB, 2, RB, true>(
+      x, wg, N, H, E, 0, nullptr, lds, z, z + 1, part + z, npad);
 }
 
 // Batches of at most NT tokens: one workgroup, one launch.  Every per-entry
@@ -551,25 +601,49 @@ __global__ __launch_bounds__(kGateThreads) void gate_gemm(const T *__restrict__ 
 // routing phases' LDS share one buffer: the ring is dead once the logits are
 // stored.
 constexpr int kFusedGateRing = 140 * 1024;
-template <typename T, int THREADS, int C, typename Lds, bool GATE = false, int EPB = 32>
+// GATE: 0 logits given; 1 router GEMM in the prologue; 2 the prologue adds up
+// the K-slice partial sums of gate_partial (nparts slices) into the logits.
+template <typename T, int THREADS, int C, typename Lds, int GATE = 0, int EPB = 32>
 __global__ __launch_bounds__(THREADS) void route_fused(
     const T *logits, int64_t N, int E, int K, int lo, int nl, int logG, int vec,
     int32_t *__restrict__ topk_idx, T *__restrict__ topk_w, uint32_t *__restrict__ bitmatrix,
     int32_t *__restrict__ col_sum, int32_t *__restrict__ offsets,
     int32_t *__restrict__ col_sorted, int32_t *__restrict__ row_sorted,
     T *__restrict__ gate_scal, const T *__restrict__ x = nullptr, const T *__restrict__ wg = nullptr,
-    int H = 0, T *logits_out = nullptr) {
+    int H = 0, T *logits_out = nullptr, const float *__restrict__ part = nullptr,
+    int nparts = 0) {
   constexpr int NT = Lds::kTokens;
-  constexpr int GS = gate_stages(kGateFusedTokens, EPB, kFusedGateRing);
-  constexpr int RING = GATE ? GS * (kGateFusedTokens + EPB) * kGateRowBytes : 0;
+  constexpr int GRB = gate_row_bytes(kGateFusedTokens, EPB, kFusedGateRing);
+  constexpr int GS = gate_stages(kGateFusedTokens, EPB, kFusedGateRing, GRB);
+  constexpr int RING = GATE == 1 ? GS * (kGateFusedTokens + EPB) * GRB : 0;
   constexpr int RAW = RING > (int)sizeof(Lds) ? RING : (int)sizeof(Lds);
   __shared__ __align__(16) char s_raw[RAW];
   Lds &L = *reinterpret_cast<Lds *>(s_raw);
   __shared__ uint16_t s_rank[NT * Lds::kSlots];
   __shared__ int s_off[Lds::kExperts + 1];
   const int tid = threadIdx.x;
-  if constexpr (GATE)  // N <= kGateFusedTokens
-    gate_logits<T, kGateFusedTokens, THREADS, EPB, GS>(x, wg, N, H, E, 0, logits_out, s_raw);
+  if constexpr (GATE == 1)  // N <= kGateFusedTokens
+    gate_logits<T, kGateFusedTokens, THREADS, EPB, GS, GRB>(x, wg, N, H, E, 0, logits_out, s_raw);
+  if constexpr (GATE == 2) {  // slices summed in order, rounded once
+    // a logit's nparts sums are contiguous (stride npad, a multiple of 4): up to
+    // 16 travel in four independent 16-byte loads
+    const int ne = (int)N * E, npad = (nparts + 3) & ~3;
+    for (int i = tid; i < ne; i += THREADS) {
+      const f32x4_t *q = reinterpret_cast<const f32x4_t *>(part + (size_t)i * npad);
+      float acc = 0.f;
+      for (int z0 = 0; z0 < nparts; z0 += 16) {
+        f32x4_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          v[u] = z0 + 4 * u < nparts ? q[z0 / 4 + u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          if (z0 + u < nparts) acc += v[u / 4][u % 4];
+      }
+      logits_out[i] = from_f32<T>(acc);
+    }
+    __syncthreads();
+  }
   topk_chunk<T, THREADS, C>(logits, N, E, K, lo, nl, logG, vec, 0, topk_idx, topk_w, bitmatrix,
                             L);
   __syncthreads();
@@ -781,19 +855,42 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
   T *gs = reinterpret_cast<T *>(r->gate_scal);
   const RoutePath path = route_path(N, E, K);
   T *lw = const_cast<T *>(logits);
+  const int gate_np = x ? gate_parts(E, H * (int)sizeof(T)) : 0;
+  if (x && N <= kGateFusedTokens && kGateSplitK && gate_np <= kGateMaxParts) {
+    // split-K router GEMM into the scratch, then the routing kernel adds the
+    // slices up in its prologue (batches this small take one logit chunk a lane)
+    float *part = reinterpret_cast<float *>(scratch);
+    const int ep = gate_bucket(E), np = gate_np, npad = (np + 3) & ~3;
+    auto partial = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3((unsigned)np), dim3(256), 0, s, x, wg, N, H, E, part, npad);
+    };
+    switch (ep) {
+      case 32: partial(gate_partial<T, 32>); break;
+      case 64: partial(gate_partial<T, 64>); break;
+      case 128: partial(gate_partial<T, 128>); break;
+      default: partial(gate_partial<T, 256>); break;
+    }
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((route_fused<T, 1024, 1, ChunkLds<T, kFusedTokens>, 2>), dim3(1),
+                       dim3(1024), 0, s, logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw,
+                       r->bitmatrix, r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs, x,
+                       wg, H, lw, part, np);
+    return hipGetLastError();
+  }
   if (x && N <= kGateFusedTokens) {  // router GEMM in the routing kernel's prologue
     // (batches this small take one logit chunk a lane: `wide` is false)
     auto fused = [&](auto kern) {
       hipLaunchKernelGGL(kern, dim3(1), dim3(1024), 0, s, logits, N, E, K, lo, nl, logG, vec,
                          r->topk_idx, tw, r->bitmatrix, r->col_sum, r->offsets, r->col_sorted,
-                         r->row_sorted, gs, x, wg, H, lw);
+                         r->row_sorted, gs, x, wg, H, lw, nullptr, 0);
     };
     using L = ChunkLds<T, kFusedTokens>;
     switch (gate_bucket(E)) {
-      case 32: fused(route_fused<T, 1024, 1, L, true, 32>); break;
-      case 64: fused(route_fused<T, 1024, 1, L, true, 64>); break;
-      case 128: fused(route_fused<T, 1024, 1, L, true, 128>); break;
-      default: fused(route_fused<T, 1024, 1, L, true, 256>); break;
+      case 32: fused(route_fused<T, 1024, 1, L, 1, 32>); break;
+      case 64: fused(route_fused<T, 1024, 1, L, 1, 64>); break;
+      case 128: fused(route_fused<T, 1024, 1, L, 1, 128>); break;
+      default: fused(route_fused<T, 1024, 1, L, 1, 256>); break;
     }
     return hipGetLastError();
   }
@@ -848,6 +945,13 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
 }
 
 }  // namespace
+
+size_t gate_scratch_bytes(int64_t n_tokens, int n_experts, int hidden, moe_dtype_t dt) {
+  if (!kGateSplitK || n_tokens > kGateFusedTokens) return 0;
+  const int np = gate_parts(n_experts, hidden * (dt == MOE_BF16 ? 2 : 4));
+  if (np > kGateMaxParts) return 0;
+  return align256((size_t)((np + 3) & ~3) * n_tokens * n_experts * 4);
+}
 
 size_t route_scratch_bytes(int64_t n_tokens, int n_experts, int topk) {
   if (route_path(n_tokens, n_experts, topk) != kPathBlocks) return 0;

@@ -73,6 +73,8 @@ GATE_CASES = [
     (1000, 33, 1000, 3, "f32"),     # fp32, multi-block
     (4096, 8, 512, 1, "bf16"),      # small-model router
     (4096, 128, 2880, 4, "bf16"),   # gpt-oss-sized router
+    (2, 16, 8200, 2, "bf16"),       # more K-slices than the split-K path takes: full prologue
+    (40, 256, 4096, 8, "bf16"),     # split-K with the widest expert bucket
 ]
 
 
