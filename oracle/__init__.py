@@ -12,6 +12,8 @@ Python binding, and imports neither.
   masked per-expert loop, the weighted combine, and the sorted-dispatch variant.
 * :mod:`oracle.ffn` also gives the layer with the routing weight on the input
   rows (``moe_ffn_weighted_input``).
+* :mod:`oracle.quant` -- MXFP4 expert weights: E2M1 codes with one E8M0 scale
+  per 32 weights along K (quantise, dequantise).
 * :mod:`oracle.routing` also gives the router logits from the gate weight
   (``gate_logits``, ``route_gate``).
 * both also give one GPU's expert-parallel share (``route_ep``,
@@ -25,6 +27,7 @@ to the pages) is marked "parity unpinned" where it is defined.
 from .routing import (RoutingRef, bitmatrix, gate_logits, histogram, offsets_from_hist,
                       remap_to_share, route, route_ep, route_gate, round_to_dtype, sorted_indices,
                       topk_select, topk_softmax)
+from .quant import dequantize_mxfp4, e2m1_decode, e2m1_encode, quantize_mxfp4
 from .ffn import (activation, moe_ffn, moe_ffn_share, moe_ffn_sorted,
                   moe_ffn_weighted_input, split_gate_up)
 
@@ -33,5 +36,6 @@ __all__ = [
     "offsets_from_hist", "sorted_indices", "round_to_dtype", "remap_to_share", "route_ep",
     "gate_logits", "route_gate",
     "activation", "split_gate_up", "moe_ffn", "moe_ffn_sorted", "moe_ffn_share",
-    "moe_ffn_weighted_input",
+    "moe_ffn_weighted_input", "quantize_mxfp4", "dequantize_mxfp4", "e2m1_encode",
+    "e2m1_decode",
 ]

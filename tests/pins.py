@@ -17,6 +17,7 @@ import numpy as np
 import torch
 
 import oracle.ffn as offn
+import oracle.quant as oquant
 import oracle.routing as orout
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -512,3 +513,74 @@ ROUTING_PINS = [pin_golden_routing, pin_topk_bruteforce, pin_topk_lexsort, pin_t
 FFN_PINS = [pin_ffn_bruteforce, pin_ffn_masked_equals_sorted, pin_ffn_layout_invariance,
             pin_ffn_dense_special_case, pin_activation_closed_forms, pin_ffn_linearity,
             pin_ffn_token_subset, pin_ffn_shares, pin_ffn_weighted_input]
+
+
+# --------------------------------------------------------------------------
+# MXFP4 weight pins
+# --------------------------------------------------------------------------
+
+def _e2m1_value(code: int) -> float:
+    """FP4 E2M1 value from its bit fields: sign, 2 exponent bits (bias 1), 1
+    mantissa bit; exponent 0 is subnormal (m * 0.5)."""
+    sgn, e, m = code >> 3, (code >> 1) & 3, code & 1
+    mag = m * 0.5 if e == 0 else 2.0 ** (e - 1) * (1 + m / 2)
+    return -mag if sgn else mag
+
+
+def _e2m1_nearest(v: float) -> int:
+    """Brute force: the code nearest to v (magnitude capped at the largest value),
+    ties to the code with an even lowest bit, the sign of v kept."""
+    mags = [abs(_e2m1_value(m)) for m in range(8)]
+    a = min(abs(v), max(mags))
+    d = [abs(a - mg) for mg in mags]
+    cands = [m for m in range(8) if d[m] == min(d)]
+    m = cands[0] if len(cands) == 1 else [c for c in cands if c % 2 == 0][0]
+    return m | (8 if math.copysign(1.0, v) < 0 else 0)
+
+
+def pin_mxfp4_codes():
+    """Decoding matches the E2M1 bit-field formula for all 16 codes; encoding of
+    every multiple of 1/64 in [-10, 10] matches brute force (ties included)."""
+    for c in range(16):
+        assert float(oquant.e2m1_decode(np.uint8(c))) == _e2m1_value(c), c
+    vals = np.arange(-640, 641) / 64.0
+    got = oquant.e2m1_encode(vals)
+    for v, c in zip(vals, got):
+        assert int(c) == _e2m1_nearest(float(v)), (v, int(c), _e2m1_nearest(float(v)))
+
+
+def pin_mxfp4_blocks(seed=18):
+    """Block quantisation: the scale puts each block's largest magnitude in
+    [4, 8); every element is the brute-force nearest code at that scale, even
+    element in the low nibble; quantising the dequantised weights gives the same
+    bytes back; a block of representable values round-trips exactly; an all-zero
+    block gets scale byte 0 and zero codes."""
+    rng = np.random.default_rng(seed)
+    w = rng.normal(size=(6, 96)) * np.array([1e-3, 1.0, 50.0, 0.3, 7.0, 1e-30])[:, None]
+    w[0, :32] = 0.0
+    grid = np.array([_e2m1_value(c) for c in range(16)])
+    w[1, 32:64] = rng.choice(grid, size=32) * 2.0 ** -3
+    w[1, 32] = 6.0 * 2.0 ** -3                   # the block's max decides X = -3
+    q, s = oquant.quantize_mxfp4(w)
+    assert q.shape == (6, 48) and s.shape == (6, 3) and q.dtype == np.uint8
+    deq = oquant.dequantize_mxfp4(q, s)
+    for r in range(6):
+        for b in range(3):
+            blk = w[r, 32 * b:32 * b + 32]
+            x = int(s[r, b]) - 127
+            amax = np.abs(blk).max()
+            if amax == 0:
+                assert s[r, b] == 0 and not q[r, 16 * b:16 * b + 16].any()
+                continue
+            assert 4.0 <= amax / 2.0 ** x < 8.0, (r, b, x, amax)
+            for i in range(32):
+                c = _e2m1_nearest(blk[i] / 2.0 ** x)
+                byte = int(q[r, 16 * b + i // 2])
+                assert (byte >> (4 * (i % 2))) & 15 == c, (r, b, i)
+                assert deq[r, 32 * b + i] == _e2m1_value(c) * 2.0 ** x
+    q2, s2 = oquant.quantize_mxfp4(deq)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+    assert np.array_equal(deq[1, 32:64], w[1, 32:64])
+
+
+QUANT_PINS = [pin_mxfp4_codes, pin_mxfp4_blocks]

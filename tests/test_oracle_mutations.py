@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import oracle.ffn as offn
+import oracle.quant as oquant
 import oracle.routing as orout
 from tests import pins
 
@@ -174,6 +175,31 @@ def weighted_input_on_output(x, idx, w, w13, w2, act, dtype, layout="packed", pa
     return offn.moe_ffn(x, idx, w, w13, w2, act, layout, params)
 
 
+_orig_enc = oquant.e2m1_encode
+_orig_q = oquant.quantize_mxfp4
+
+
+def e2m1_ties_away(v):
+    # ties rounded away from zero instead of to the even code
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    d = np.abs(a[..., None] - oquant.E2M1)
+    best = 7 - np.argmin(d[..., ::-1], axis=-1)   # last minimum: the larger magnitude
+    best = np.where(a > 6.0, 7, best)
+    return (best.astype(np.uint8) | (np.signbit(v).astype(np.uint8) << 3)).astype(np.uint8)
+
+
+def mxfp4_scale_off_by_one(w):
+    # X = floor(log2 amax) - 1: the block's max lands in [2, 4)
+    q, s = _orig_q(np.asarray(w, dtype=np.float64) / 2.0)
+    return q, s + 1
+
+
+def mxfp4_nibbles_swapped(w):
+    q, s = _orig_q(w)
+    return ((q >> 4) | (q << 4)).astype(np.uint8), s
+
+
 def remap_off_by_one(idx, lo, nl):
     r = _orig_remap(idx, lo, nl)
     return np.where(r >= 0, np.minimum(r + 1, nl - 1), -1).astype(np.int32)
@@ -213,6 +239,10 @@ MUTATIONS = [
     ("share ids not remapped (ffn)", orout, "remap_to_share", remap_none, "ffn"),
     ("share remap off by one (ffn)", orout, "remap_to_share", remap_off_by_one, "ffn"),
     ("gate logits not rounded", orout, "gate_logits", gate_not_rounded, "routing"),
+    ("e2m1 ties away from zero", oquant, "e2m1_encode", e2m1_ties_away, "quant"),
+    ("mxfp4 scale exponent off by one", oquant, "quantize_mxfp4", mxfp4_scale_off_by_one,
+     "quant"),
+    ("mxfp4 nibble order swapped", oquant, "quantize_mxfp4", mxfp4_nibbles_swapped, "quant"),
     ("weighted input not rounded", offn, "moe_ffn_weighted_input", weighted_input_unrounded,
      "ffn"),
     ("weight on output instead of input", offn, "moe_ffn_weighted_input",
@@ -223,7 +253,8 @@ MUTATIONS = [
 
 
 def _some_pin_fails(group):
-    group_pins = pins.ROUTING_PINS if group == "routing" else pins.FFN_PINS
+    group_pins = {"routing": pins.ROUTING_PINS, "ffn": pins.FFN_PINS,
+                  "quant": pins.QUANT_PINS}[group]
     failed = []
     for pin in group_pins:
         try:
@@ -243,3 +274,4 @@ def test_mutation_is_caught(monkeypatch, name, mod, attr, fn, group):
 def test_unmutated_oracle_passes_all_pins():
     assert not _some_pin_fails("routing")
     assert not _some_pin_fails("ffn")
+    assert not _some_pin_fails("quant")
