@@ -38,7 +38,8 @@ from routing_grouped_expert_amd import (Routing, moe_workspace_bytes,  # noqa: E
                                         prepare_experts_w13, prepare_experts_w2,
                                         prepare_forward, prepare_forward_ep,
                                         prepare_gate_forward, prepare_gate_route, prepare_route,
-                                        prepare_route_ep)
+                                        prepare_route_ep, moe_quantize_mxfp4,
+                                        prepare_experts_mxfp4, prepare_forward_mxfp4)
 from routing_grouped_expert_amd.synth import (act_params, layer_spec, make_layer,  # noqa: E402
                                               router_inputs, routing_logits)
 
@@ -48,6 +49,8 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
 
 
 def workload(name: str):
+    if name.endswith("_mxfp4"):  # the same layer with MXFP4 expert weights
+        return workload(name[:-len("_mxfp4")]).with_(name=name)
     if name.startswith("gptoss_ep"):
         # one GPU of an expert-parallel group of G: the first E/G experts of the
         # gpt-oss-sized layer, every token routed over all E
@@ -90,6 +93,23 @@ def algorithmic(spec, col_sum):
     w2_f = 2 * m * h * i
     w2_b = et * h * i * s + m * i * s + m * h * s + (m * h * s + m * 4 + n * h * s if k > 1 else 0)
     return {"route": (0, route_b), "w13": (w13_f, w13_b), "w2": (w2_f, w2_b)}, et
+
+
+MXFP4_BYTES = 17 / 32  # bytes per weight: a 4-bit code plus a 1-byte scale per 32
+
+
+def algorithmic_mxfp4(spec, col_sum):
+    """Flops / bytes of one experts call (both grouped GEMMs) with MXFP4 weights:
+    the touched experts' codes and scales read once, activations read and
+    written once."""
+    n, h, i, k = spec.n_tokens, spec.hidden, spec.inter, spec.topk
+    m = int(col_sum.sum())
+    g = 2 if spec.act != "relu2" else 1
+    et = int((col_sum > 0).sum())
+    flops = 2 * m * g * i * h + 2 * m * h * i
+    nbytes = int(et * (g * i * h + h * i) * MXFP4_BYTES) + n * h * 2 + 2 * m * i * 2 + \
+        (2 * m * h * 2 + m * 4 + n * h * 2 if k > 1 else n * h * 2)
+    return flops, nbytes, et
 
 
 def roofline(spec, flops, nbytes, ms):
@@ -336,10 +356,10 @@ def bench_decode_stack(args, name: str):
     layer's input.  One step = the L layers; timed eager (L prepared calls) and
     as one captured HIP graph replay, to show what capture saves on launches."""
     import re
-    m = re.fullmatch(r"decode(\d+)_n(\d+)", name)
+    m = re.fullmatch(r"decode(\d+)_n(\d+)(_mxfp4)?", name)
     if not m:
         raise SystemExit(f"unknown workload {name!r}")
-    L, n = int(m.group(1)), int(m.group(2))
+    L, n, mx = int(m.group(1)), int(m.group(2)), m.group(3) is not None
     e, k, h, i = 32, 4, 2880, 2880
     prm = {"alpha": 1.702, "beta": 1.0, "limit": 7.0}
     dev = torch.device("cuda:0")
@@ -353,8 +373,14 @@ def bench_decode_stack(args, name: str):
             out[j] = (torch.randn(shape[1:], generator=gen, device=dev) * std).to(torch.bfloat16)
         return out
 
-    layers = [(draw((e, h), h ** -0.5, 3 * l), draw((e, 2 * i, h), 0.02, 3 * l + 1),
-               draw((e, h, i), 0.02, 3 * l + 2)) for l in range(L)]
+    layers = []
+    for l in range(L):
+        wg, w13, w2 = (draw((e, h), h ** -0.5, 3 * l), draw((e, 2 * i, h), 0.02, 3 * l + 1),
+                       draw((e, h, i), 0.02, 3 * l + 2))
+        if mx:  # MXFP4 expert weights (the router stays bf16)
+            w13, w2 = moe_quantize_mxfp4(w13), moe_quantize_mxfp4(w2)
+            torch.cuda.synchronize()
+        layers.append((wg, w13, w2))
     x0, _ = router_inputs(n, e, h, "bf16", seed=0)
     bufs = [x0.to(dev)] + [torch.empty(n, h, dtype=torch.bfloat16, device=dev) for _ in range(L)]
     logits = torch.empty(n, e, dtype=torch.bfloat16, device=dev)
@@ -362,10 +388,19 @@ def bench_decode_stack(args, name: str):
     ws = torch.empty(moe_workspace_bytes(n, e, k, h, i), dtype=torch.uint8, device=dev)
 
     def prepared(stream):
-        return [prepare_gate_forward(bufs[l], wg, w13, w2, k, "swiglu_oai", "interleaved", prm,
-                                     out=bufs[l + 1], logits=logits, routing=routing,
-                                     workspace=ws, stream=stream)
-                for l, (wg, w13, w2) in enumerate(layers)]
+        if not mx:
+            return [prepare_gate_forward(bufs[l], wg, w13, w2, k, "swiglu_oai", "interleaved",
+                                         prm, out=bufs[l + 1], logits=logits, routing=routing,
+                                         workspace=ws, stream=stream)
+                    for l, (wg, w13, w2) in enumerate(layers)]
+        calls = []
+        for l, (wg, (q13, s13), (q2, s2)) in enumerate(layers):
+            calls.append(prepare_gate_route(bufs[l], wg, k, logits=logits, routing=routing,
+                                            workspace=ws, stream=stream))
+            calls.append(prepare_experts_mxfp4(bufs[l], q13, s13, q2, s2, routing, "swiglu_oai",
+                                               "interleaved", prm, out=bufs[l + 1],
+                                               workspace=ws, stream=stream))
+        return calls
 
     stream = torch.cuda.current_stream(dev)
     eager = prepared(stream)
@@ -398,10 +433,12 @@ def bench_decode_stack(args, name: str):
     # weights of the experts each layer's tokens touch, read once (counted in an
     # untimed eager pass that reads every layer's histogram)
     touched = []
-    for c in eager:
+    for j, c in enumerate(eager):
         c()
-        touched.append(int((routing.col_sum > 0).sum()))
-    nbytes = sum(t * 3 * i * h * 2 + e * h * 2 + n * h * 2 * 2 for t in touched)
+        if not mx or j % 2 == 0:
+            touched.append(int((routing.col_sum > 0).sum()))
+    wb = MXFP4_BYTES if mx else 2  # bytes per expert weight
+    nbytes = sum(int(t * 3 * i * h * wb) + e * h * 2 + n * h * 2 * 2 for t in touched)
     ms = st_graph["mean"]
     ach = nbytes / (ms * 1e-3) / 1e9
     result = {
@@ -412,7 +449,8 @@ def bench_decode_stack(args, name: str):
         "data": "synthetic (seeded Gaussian token rows; weights drawn on the GPU from seeded "
                 "generators)",
         "config": {"workload": f"{name}: {L} chained gpt-oss-20b-shaped MoE layers "
-                               f"(E=32 k=4 H=I=2880 swiglu_oai interleaved bf16), N={n}, "
+                               f"(E=32 k=4 H=I=2880 swiglu_oai interleaved bf16"
+                               f"{', MXFP4 expert weights' if mx else ''}), N={n}, "
                                f"router GEMM + routing + experts per layer"},
         "graph_us_per_step": round(ms * 1e3, 2),
         "eager_us_per_step": round(st_eager["mean"] * 1e3, 2),
@@ -459,11 +497,16 @@ def main():
     if args.workload.startswith("decode"):
         return bench_decode_stack(args, args.workload)
     spec = workload(args.workload)
+    mx = spec.name.endswith("_mxfp4")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     layer = make_layer(spec)
     x, lg = layer.x.to(dev), layer.logits.to(dev)
     w13, w2 = layer.w13.to(dev), layer.w2.to(dev)
+    if mx:  # quantised once, outside the timed region, as a model load would
+        wq = moe_quantize_mxfp4(w13) + moe_quantize_mxfp4(w2)
+        del w13, w2
+        torch.cuda.synchronize()
     n, e, k = spec.n_tokens, spec.n_experts, spec.topk
     share = spec.n_local is not None
     dt = x.dtype
@@ -473,7 +516,13 @@ def main():
     ws = torch.empty(moe_workspace_bytes(n, e, k, spec.hidden, spec.inter, dt), dtype=torch.uint8,
                      device=dev)
     stream = torch.cuda.current_stream(dev)
-    if share:
+    if mx:
+        p_route = prepare_route(lg, k, routing=routing, workspace=ws, stream=stream)
+        p_fwd = prepare_forward_mxfp4(x, lg, *wq, k, spec.act, spec.layout, act_params(spec),
+                                      out=out, routing=routing, workspace=ws, stream=stream)
+        p_exp = prepare_experts_mxfp4(x, *wq, routing, spec.act, spec.layout, act_params(spec),
+                                      out=out, workspace=ws, stream=stream)
+    elif share:
         p_route = prepare_route_ep(lg, k, spec.local_offset, spec.n_local, routing=routing,
                                    workspace=ws, stream=stream)
         p_fwd = prepare_forward_ep(x, lg, w13, w2, k, spec.local_offset, spec.act, spec.layout,
@@ -485,9 +534,10 @@ def main():
                                 out=out, routing=routing, workspace=ws, stream=stream)
     # the halves run the same kernels as the full call (k > 1 for every share
     # workload, so the combine skips the slots routed to other GPUs)
-    p_w13 = prepare_experts_w13(x, w13, routing, spec.act, spec.layout, act_params(spec),
-                                act_out=act, stream=stream)
-    p_w2 = prepare_experts_w2(act, w2, routing, out=out, workspace=ws, stream=stream)
+    if not mx:
+        p_w13 = prepare_experts_w13(x, w13, routing, spec.act, spec.layout, act_params(spec),
+                                    act_out=act, stream=stream)
+        p_w2 = prepare_experts_w2(act, w2, routing, out=out, workspace=ws, stream=stream)
 
     K, W = args.steps, args.warmup
 
@@ -510,20 +560,31 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = st["mean"]
     # stages (the routing metadata of the last step stays valid for w13 / w2)
-    stage_ms = {name: timed(fn, K) for name, fn in (("route", p_route), ("w13", p_w13),
-                                                   ("w2", p_w2))}
+    stages = (("route", p_route), ("experts", p_exp)) if mx else \
+        (("route", p_route), ("w13", p_w13), ("w2", p_w2))
+    stage_ms = {name: timed(fn, K) for name, fn in stages}
     cold_step, cold_route = cold_stats([p_fwd, p_route], 20, stream, dev)
     col_sum = routing.col_sum.cpu()
-    work, et = algorithmic(spec, col_sum)
-    # the w13 grouped GEMM is one kernel and the largest of the layer (it has
-    # n_sets x the flops of the w2 GEMM); its back-to-back launches are timed
-    dom = "w13"
-    f, b = work[dom]
-    roof = roofline(spec, f, b, stage_ms[dom])
-    roof.update({"kernel": "grouped_gemm (w13 + activation)",
-                 "traffic": stored_traffic(spec.name, dom),
-                 "algorithmic_bytes": b, "algorithmic_flops": f,
-                 "avg_launch_us": round(stage_ms[dom] * 1e3, 2)})
+    if mx:
+        # MXFP4 workloads: both grouped GEMMs of one experts call, weight bytes
+        # at 17/32 byte a weight
+        f, b, et = algorithmic_mxfp4(spec, col_sum)
+        roof = roofline(spec, f, b, stage_ms["experts"])
+        roof.update({"kernel": "grouped_gemm w13 + w2 (MXFP4 weights, one experts call)",
+                     "traffic": None, "algorithmic_bytes": b, "algorithmic_flops": f,
+                     "avg_launch_us": round(stage_ms["experts"] * 1e3, 2)})
+    else:
+        work, et = algorithmic(spec, col_sum)
+        # the w13 grouped GEMM is one kernel and the largest of the layer (it
+        # has n_sets x the flops of the w2 GEMM); its back-to-back launches are
+        # timed
+        dom = "w13"
+        f, b = work[dom]
+        roof = roofline(spec, f, b, stage_ms[dom])
+        roof.update({"kernel": "grouped_gemm (w13 + activation)",
+                     "traffic": stored_traffic(spec.name, dom),
+                     "algorithmic_bytes": b, "algorithmic_flops": f,
+                     "avg_launch_us": round(stage_ms[dom] * 1e3, 2)})
     result = {
         "metric": METRIC,
         "value": round(n / (ms_step * 1e-3), 1),
@@ -546,7 +607,7 @@ def main():
         "wall_ms_per_step": round(wall / K * 1e3, 4),
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not mx:
         result["cpu_baseline"] = cpu_baseline(spec, layer, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 

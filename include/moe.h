@@ -274,6 +274,49 @@ moe_status_t moe_forward_ep(const void *x, const void *logits, moe_dtype_t dtype
                             const moe_act_params_t *params, const moe_routing_t *routing_out,
                             void *out, void *workspace, size_t ws_bytes, void *stream);
 
+/* ---- MXFP4 expert weights ------------------------------------------------------
+ * The gpt-oss experts of the vLLM PR #45457 report run with MXFP4 weights and
+ * bf16 activations (the MXFP4 experts forward of "key source snippets"); the
+ * pages name the format only.  Format (public OCP microscaling definition):
+ * every 32 consecutive weights along K share a scale 2^X stored as the byte
+ * X + 127, X = floor(log2 max|w|) - 2 (-127 for an all-zero block); each weight
+ * is an FP4 E2M1 code (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; bit 3 the sign)
+ * for the nearest value of w * 2^-X, ties to the code with an even lowest bit,
+ * saturating at 6.  Codes pack two to a byte, the even element in the low
+ * nibble; scales are block-major per expert.
+ *
+ * moe_quantize_mxfp4: w [n_experts, rows, k] (dtype) -> q [n_experts, rows,
+ *   k / 2] bytes and scales [n_experts, k / 32, rows] bytes.  k a multiple of
+ *   32; w and q 16-byte aligned.  Deterministic, bit-exact. */
+moe_status_t moe_quantize_mxfp4(const void *w, moe_dtype_t dtype, int32_t n_experts,
+                                int32_t rows, int32_t k, void *q, void *scales, void *stream);
+
+/* moe_experts_mxfp4 / moe_forward_mxfp4: moe_experts / moe_forward with MXFP4
+ *   expert weights from moe_quantize_mxfp4: w13_q [E, w13 rows, hidden / 2] and
+ *   w13_s [E, hidden / 32, w13 rows] (w13 rows = 2 * inter gated, in the same
+ *   packed or interleaved order as a bf16 w13; inter for ReLU^2), w2_q
+ *   [E, hidden, inter / 2] and w2_s [E, inter / 32, hidden].  The layer is bf16
+ *   (dtype MOE_BF16, else MOE_ERR_UNSUPPORTED); hidden and inter multiples of
+ *   32.  Each weight is its code's value times its block's scale, exactly
+ *   representable in bf16, so the result is that of moe_experts on the
+ *   dequantised bf16 weights (bit-identical when both run the same tiles;
+ *   these run the 32-row and one-wave tiles at every batch size).  Workspace
+ *   and other arguments as moe_experts / moe_forward. */
+moe_status_t moe_experts_mxfp4(const void *x, moe_dtype_t dtype, int64_t n_tokens,
+                               int32_t hidden, const void *w13_q, const void *w13_s,
+                               const void *w2_q, const void *w2_s, int32_t n_experts,
+                               int32_t inter, int32_t topk, moe_act_t act,
+                               moe_w13_layout_t layout, const moe_act_params_t *params,
+                               const moe_routing_t *routing, void *out, void *workspace,
+                               size_t ws_bytes, void *stream);
+moe_status_t moe_forward_mxfp4(const void *x, const void *logits, moe_dtype_t dtype,
+                               int64_t n_tokens, int32_t hidden, const void *w13_q,
+                               const void *w13_s, const void *w2_q, const void *w2_s,
+                               int32_t n_experts, int32_t inter, int32_t topk, moe_act_t act,
+                               moe_w13_layout_t layout, const moe_act_params_t *params,
+                               const moe_routing_t *routing_out, void *out, void *workspace,
+                               size_t ws_bytes, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *moe_status_str(moe_status_t status);
 

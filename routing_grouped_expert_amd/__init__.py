@@ -41,7 +41,8 @@ __all__ = ["Routing", "MoeError", "Prepared", "moe_route", "moe_experts", "moe_e
            "moe_route_ep", "moe_experts_ep", "moe_forward_ep", "prepare_route_ep",
            "prepare_experts_ep", "prepare_forward_ep", "moe_gate_route", "moe_gate_forward",
            "prepare_gate_route", "prepare_gate_forward", "moe_experts_weighted_input",
-           "prepare_experts_weighted_input",
+           "prepare_experts_weighted_input", "moe_quantize_mxfp4", "moe_experts_mxfp4",
+           "moe_forward_mxfp4", "prepare_experts_mxfp4", "prepare_forward_mxfp4",
            "moe_workspace_bytes", "moe_status_str", "ACTS", "LAYOUTS"]
 
 _DT = {torch.float32: N.MOE_F32, torch.bfloat16: N.MOE_BF16}
@@ -552,3 +553,110 @@ def moe_experts_weighted_input(x: torch.Tensor, w13: torch.Tensor, w2: torch.Ten
     (rounded to the layer dtype) instead of its output (see moe.h)."""
     return prepare_experts_weighted_input(x, w13, w2, routing, act, layout, params, out=out,
                                           workspace=workspace, stream=stream)()
+
+
+def moe_quantize_mxfp4(w: torch.Tensor, *, stream=None):
+    """MXFP4 expert weights from ``w [E, rows, K]`` (K a multiple of 32): returns
+    ``(q [E, rows, K/2] uint8, scales [E, K/32, rows] uint8)`` (see moe.h)."""
+    dev = _dev(w)
+    if w.dim() != 3:
+        raise ValueError("expected w [E, rows, K]")
+    e, rows, k = w.shape
+    q = torch.empty(e, rows, k // 2, dtype=torch.uint8, device=dev)
+    sc = torch.empty(e, k // 32, rows, dtype=torch.uint8, device=dev)
+    _check(N.load().moe_quantize_mxfp4(w.data_ptr(), _dt(w), e, rows, k, q.data_ptr(),
+                                       sc.data_ptr(), _stream(dev, stream)), "moe_quantize_mxfp4")
+    return q, sc
+
+
+def _mxfp4_shapes(x, w13_q, w13_s, w2_q, w2_s, act):
+    """Codes and scales as moe_quantize_mxfp4 lays them out; returns (E, inter)."""
+    if x.dtype != torch.bfloat16:
+        raise TypeError("MXFP4 weights run a bf16 layer")
+    for t in (w13_q, w13_s, w2_q, w2_s):
+        if t.dtype != torch.uint8 or t.dim() != 3:
+            raise TypeError("MXFP4 codes and scales are 3-D uint8 tensors")
+    n, h = x.shape
+    e, hh, half_i = w2_q.shape
+    inter = 2 * half_i
+    rows = inter if act == "relu2" else 2 * inter
+    want = {"w13_q": (e, rows, h // 2), "w13_s": (e, h // 32, rows),
+            "w2_q": (e, h, inter // 2), "w2_s": (e, inter // 32, h)}
+    got = {"w13_q": w13_q, "w13_s": w13_s, "w2_q": w2_q, "w2_s": w2_s}
+    if hh != h or h % 32 or inter % 32:
+        raise ValueError("hidden and inter must be multiples of 32 and match x")
+    for k, shp in want.items():
+        if tuple(got[k].shape) != shp:
+            raise ValueError(f"{k} must be {shp}, got {tuple(got[k].shape)}")
+    return e, inter
+
+
+def prepare_experts_mxfp4(x, w13_q, w13_s, w2_q, w2_s, routing: Routing, act: str,
+                          layout: str = "packed", params: Optional[dict] = None, *, out=None,
+                          workspace=None, stream=None) -> Prepared:
+    dev = _dev(x, w13_q, w13_s, w2_q, w2_s)
+    if act not in ACTS:
+        raise ValueError(f"unknown activation {act!r}")
+    e, inter = _mxfp4_shapes(x, w13_q, w13_s, w2_q, w2_s, act)
+    n, hidden = x.shape
+    k = routing.topk
+    _check_routing(routing, n, e, k)
+    if out is None:
+        out = torch.empty_like(x)
+    ws = _workspace(workspace, moe_workspace_bytes(n, max(e, k), k, hidden, inter, x.dtype), dev)
+    r = routing.as_c()
+    p = _params(params)
+    args = (x.data_ptr(), _dt(x), n, hidden, w13_q.data_ptr(), w13_s.data_ptr(), w2_q.data_ptr(),
+            w2_s.data_ptr(), e, inter, k, ACTS[act], LAYOUTS[layout],
+            ctypes.byref(p) if p else None, ctypes.byref(r), out.data_ptr(), ws.data_ptr(),
+            _nbytes(ws), _stream(dev, stream))
+    return Prepared("moe_experts_mxfp4", args,
+                    (r, p, x, w13_q, w13_s, w2_q, w2_s, out, ws, routing), out)
+
+
+def moe_experts_mxfp4(x: torch.Tensor, w13_q: torch.Tensor, w13_s: torch.Tensor,
+                      w2_q: torch.Tensor, w2_s: torch.Tensor, routing: Routing, act: str,
+                      layout: str = "packed", params: Optional[dict] = None, *,
+                      out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """moe_experts with MXFP4 expert weights (codes and scales from
+    moe_quantize_mxfp4); bf16 layer (see moe.h)."""
+    return prepare_experts_mxfp4(x, w13_q, w13_s, w2_q, w2_s, routing, act, layout, params,
+                                 out=out, workspace=workspace, stream=stream)()
+
+
+def prepare_forward_mxfp4(x, logits, w13_q, w13_s, w2_q, w2_s, topk: int, act: str,
+                          layout: str = "packed", params: Optional[dict] = None, *, out=None,
+                          routing=None, workspace=None, stream=None) -> Prepared:
+    dev = _dev(x, logits, w13_q, w13_s, w2_q, w2_s)
+    if act not in ACTS:
+        raise ValueError(f"unknown activation {act!r}")
+    e, inter = _mxfp4_shapes(x, w13_q, w13_s, w2_q, w2_s, act)
+    n, hidden = x.shape
+    if logits.dtype != x.dtype or tuple(logits.shape) != (n, e):
+        raise ValueError("logits must be [N, E] in the layer dtype")
+    if routing is None:
+        routing = Routing.empty(n, e, topk, x.dtype, dev)
+    _check_routing(routing, n, e, topk)
+    if out is None:
+        out = torch.empty_like(x)
+    ws = _workspace(workspace, moe_workspace_bytes(n, e, topk, hidden, inter, x.dtype), dev)
+    r = routing.as_c()
+    p = _params(params)
+    args = (x.data_ptr(), logits.data_ptr(), _dt(x), n, hidden, w13_q.data_ptr(),
+            w13_s.data_ptr(), w2_q.data_ptr(), w2_s.data_ptr(), e, inter, topk, ACTS[act],
+            LAYOUTS[layout], ctypes.byref(p) if p else None, ctypes.byref(r), out.data_ptr(),
+            ws.data_ptr(), _nbytes(ws), _stream(dev, stream))
+    return Prepared("moe_forward_mxfp4", args,
+                    (r, p, x, logits, w13_q, w13_s, w2_q, w2_s, out, ws, routing),
+                    (out, routing))
+
+
+def moe_forward_mxfp4(x: torch.Tensor, logits: torch.Tensor, w13_q: torch.Tensor,
+                      w13_s: torch.Tensor, w2_q: torch.Tensor, w2_s: torch.Tensor, topk: int,
+                      act: str, layout: str = "packed", params: Optional[dict] = None, *,
+                      out: Optional[torch.Tensor] = None, routing: Optional[Routing] = None,
+                      workspace: Optional[torch.Tensor] = None, stream=None):
+    """Routing then the MXFP4-weight experts on one stream; returns ``(out, routing)``."""
+    return prepare_forward_mxfp4(x, logits, w13_q, w13_s, w2_q, w2_s, topk, act, layout, params,
+                                 out=out, routing=routing, workspace=workspace, stream=stream)()

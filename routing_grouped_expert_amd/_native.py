@@ -59,6 +59,13 @@ SIGNATURES = {
     "moe_experts_weighted_input": (c_i32, [c_vp, c_i32, c_i64, c_i32, c_vp, c_vp, c_i32, c_i32,
                                            c_i32, c_i32, c_i32, _P_PARAMS, _P_ROUTING, c_vp,
                                            c_vp, c_sz, c_vp]),
+    "moe_quantize_mxfp4": (c_i32, [c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
+    "moe_experts_mxfp4": (c_i32, [c_vp, c_i32, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32, c_i32,
+                                  c_i32, c_i32, c_i32, _P_PARAMS, _P_ROUTING, c_vp, c_vp, c_sz,
+                                  c_vp]),
+    "moe_forward_mxfp4": (c_i32, [c_vp, c_vp, c_i32, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_i32,
+                                  c_i32, c_i32, c_i32, c_i32, _P_PARAMS, _P_ROUTING, c_vp, c_vp,
+                                  c_sz, c_vp]),
     "moe_status_str": (ctypes.c_char_p, [c_i32]),
 }
 

@@ -57,6 +57,9 @@ struct GemmArgs {
   uint32_t c_bytes;              // bytes of C
   int gate_bf16, E, K, Nout, topk, gather, interleaved, act;
   ActParams prm;
+  // MXFP4 weights: W holds E2M1 codes [E, NSETS * Nout, K / 2] and wscale the
+  // E8M0 scales [E, K / 32, NSETS * Nout] (nullptr: W is in the A dtype)
+  const uint8_t *wscale;
 };
 
 template <typename T> struct Mma;
@@ -91,6 +94,19 @@ template <int RB> __device__ __forceinline__ int swz_key(int row) {
 }
 template <int RB> __device__ __forceinline__ int swz(int row, int chunk) {
   return row * RB + ((chunk ^ swz_key<RB>(row)) << 4);
+}
+
+// 8 E2M1 codes (element i in nibble i of `word`) times the scale `sc`, as the
+// bf16 fragment of 8 consecutive K elements.  The hardware conversion takes
+// byte b and yields its low nibble's value first.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t word, float sc) {
+  u32x4_t w;
+  w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 0));
+  w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 1));
+  w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 2));
+  w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 3));
+  return __builtin_bit_cast(bf16x8_t, w);
 }
 
 // Activation of one (gate, up) pair.  Gated kinds evaluate the logistic
@@ -194,7 +210,16 @@ __device__ __forceinline__ TileInfo tile_info(int L, const int *s_ts, const int 
 // sub-tile and each group of four registers four consecutive output columns.
 // The epilogue then writes 8-byte (bf16) or 16-byte (fp32) pieces of a row,
 // and needs one output-row index and one routing weight per lane.
-template <typename T, int NSETS, int EPI, int BM, int BN, int WM, int WN, int S, int RB>
+//
+// WQ (MXFP4 weights, one-phase tiles, bf16 activations): a stage holds the A
+// rows, each weight row's E2M1 codes for the slice (RB / 4 bytes: the same K
+// range) and the slice's E8M0 scales, tile rows in weight-row order per K-block
+// (4-byte loads: the rows of a tile are one or, packed and gated, two
+// contiguous runs of the block-major scale array).  A weight fragment is one
+// 4-byte read of 8 codes and one scale byte, turned into 8 bf16 values with
+// the hardware's scaled FP4 conversion (exact: a code times a power of two).
+template <typename T, int NSETS, int EPI, int BM, int BN, int WM, int WN, int S, int RB,
+          bool WQ = false>
 __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
   using Mm = Mma<T>;
   using Frag = typename Mm::Frag;
@@ -208,10 +233,21 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
   constexpr int JB = NB / RPI / NW;
   constexpr int TM = BM / WM / 32;         // 32x32 sub-tiles per wave
   constexpr int TN = BN / WN / 32;
-  constexpr int STAGE = (BM + NB) * RB;
+  constexpr int QRB = RB / 4;              // WQ: code bytes of a weight row's slice
+  constexpr int QCPR = QRB / 16;           // WQ: 16-byte chunks of those
+  constexpr int QRPI = 64 / (QCPR > 0 ? QCPR : 1);  // WQ: code rows per 1 KB load
+  constexpr int JBQ = WQ ? NB / QRPI / NW : 0;      // WQ: code loads per wave per slice
+  constexpr int SBK = BK / 32;             // WQ: scale blocks per slice
+  constexpr int BQ = WQ ? NB * QRB : NB * RB;       // B bytes of a stage
+  constexpr int SCL = WQ ? NW * 256 : 0;   // WQ: scale bytes of a stage (one 4-byte load a lane)
+  constexpr int STAGE = BM * RB + BQ + SCL;
+  constexpr int PER = WQ ? JA + JBQ + 1 : JA + JB;  // load instructions per wave per slice
   constexpr int NST = TM * TN * 4;         // stores per wave per epilogue
   constexpr bool META = EPI == EPI_Y || EPI == EPI_OUT;
   constexpr bool PP = NW == 8;             // ping-pong schedule
+  static_assert(!WQ || (!PP && std::is_same<T, bf16_t>::value && QCPR >= 1 &&
+                        JBQ * QRPI * NW == NB && SBK * NB <= SCL && NB % 4 == 0),
+                "MXFP4 weights: one-phase bf16 tiles");
   // a tile's metadata is written when its first slice is issued (S - 1
   // slices ahead) and read by its epilogue; NSL slots keep the epilogue of
   // tile i clear of the set-up of tile i + NSL
@@ -221,7 +257,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
                 "tile rows vs waves");
   static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "wave tiles");
   static_assert(BK % Mm::KS == 0, "slice vs instruction K");
-  static_assert(S >= 2 && (S - 2) * (JA + JB) < 64, "stages / vmcnt range");
+  static_assert(S >= 2 && (S - 2) * PER < 64, "stages / vmcnt range");
   static_assert((EPI == EPI_RELU2 || EPI == EPI_Y || EPI == EPI_OUT) == (NSETS == 1),
                 "gated epilogues take two weight sets");
 
@@ -287,7 +323,9 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
       const_cast<void *>(g.A), (short)0, (int)g.a_bytes, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rc =
       __builtin_amdgcn_make_buffer_rsrc(g.C, (short)0, (int)g.c_bytes, kRsrcWord3);
-  const uint32_t w_bytes = (uint32_t)NSETS * Nout * kbytes;
+  const int wkbytes = WQ ? K / 2 : kbytes;  // bytes of one weight row
+  const uint32_t w_bytes = (uint32_t)NSETS * Nout * wkbytes;
+  const int nrows = NSETS * Nout;           // weight rows of one expert
   const int wm = wave % WM, wn = wave / WM;
   const float nal = -g.prm.alpha * 1.44269504088896341f;
 
@@ -295,8 +333,9 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
   // loads go out before its gather indices are read (the inline-asm loads are
   // compiler memory barriers, so the index loads stay behind them), and the
   // first weight slices travel while the indices make their round trip.
-  uint32_t va[JA], vb[JB];
-  __amdgpu_buffer_rsrc_t rb = ra;
+  uint32_t va[JA], vb[WQ ? JBQ : JB];
+  __amdgpu_buffer_rsrc_t rb = ra, rs = ra;
+  uint32_t vs = kOOB;  // WQ: this lane's scale offset at K-block 0 (4 rows)
   TileInfo cur;
   auto setup_b = [&](int i) {
     cur = tile_info<BM, BN>(first + i * gx, s_ts, s_off, E, n_nt);
@@ -304,14 +343,44 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
     rb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char *>(reinterpret_cast<const char *>(g.W)) + (size_t)cur.e * w_bytes,
         (short)0, (int)w_bytes, kRsrcWord3);
+    if constexpr (WQ) {
 #pragma unroll
-    for (int j = 0; j < JB; ++j) {
-      const int r = (wave * JB + j) * RPI + lrow;
-      const int set = r / BN, n = cur.n0 + r % BN;
-      vb[j] = kOOB;
-      if (n < Nout) {
-        const int grow = NSETS == 1 ? n : (g.interleaved ? 2 * n + set : set * Nout + n);
-        vb[j] = (uint32_t)grow * (uint32_t)kbytes + (((lane % CPR) ^ swz_key<RB>(r)) << 4);
+      for (int j = 0; j < JBQ; ++j) {
+        const int r = (wave * JBQ + j) * QRPI + lane / QCPR;
+        const int set = r / BN, n = cur.n0 + r % BN;
+        vb[j] = kOOB;
+        if (n < Nout) {
+          const int grow = NSETS == 1 ? n : (g.interleaved ? 2 * n + set : set * Nout + n);
+          vb[j] = (uint32_t)grow * (uint32_t)wkbytes + (((lane % QCPR) ^ swz_key<QRB>(r)) << 4);
+        }
+      }
+      // scales: stage byte o = 4 * (wave * 64 + lane) is K-block o / NB of the
+      // slice, tile row o % NB in weight-row order (packed: the gate run, then
+      // the up run; interleaved and plain: one run from the tile's first row)
+      const uint32_t sbytes = (uint32_t)(K / 32) * (uint32_t)nrows;
+      rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t *>(g.wscale) + (size_t)cur.e * sbytes, (short)0, (int)sbytes,
+          kRsrcWord3);
+      const int o = 4 * (wave * 64 + lane), blk = o / NB, rem = o % NB;
+      int wrow, n;
+      if (NSETS == 2 && !g.interleaved) {
+        n = cur.n0 + rem % BN;
+        wrow = (rem / BN) * Nout + n;
+      } else {
+        wrow = (NSETS == 2 ? 2 * cur.n0 : cur.n0) + rem;
+        n = NSETS == 2 ? wrow / 2 : wrow;
+      }
+      vs = (blk < SBK && n < Nout) ? (uint32_t)blk * (uint32_t)nrows + (uint32_t)wrow : kOOB;
+    } else {
+#pragma unroll
+      for (int j = 0; j < JB; ++j) {
+        const int r = (wave * JB + j) * RPI + lrow;
+        const int set = r / BN, n = cur.n0 + r % BN;
+        vb[j] = kOOB;
+        if (n < Nout) {
+          const int grow = NSETS == 1 ? n : (g.interleaved ? 2 * n + set : set * Nout + n);
+          vb[j] = (uint32_t)grow * (uint32_t)kbytes + (((lane % CPR) ^ swz_key<RB>(r)) << 4);
+        }
       }
     }
   };
@@ -347,14 +416,33 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
     // are K * sizeof(T) bytes, a multiple of 16, so the tail is chunk-aligned.
     const bool tail = (int)kb + RB > kbytes;
     if (kt == 0) setup_b(i);
+    if constexpr (WQ) {
+      const uint32_t qb = (uint32_t)kt * QRB;
 #pragma unroll
-    for (int j = 0; j < JB; ++j) {
-      uint32_t off = vb[j] + kb;
-      if (tail) {
-        const int coff = ((lane % CPR) ^ swz_key<RB>((wave * JB + j) * RPI + lrow)) << 4;
-        off = (int)kb + coff < kbytes ? off : kOOB;
+      for (int j = 0; j < JBQ; ++j) {
+        uint32_t off = vb[j] + qb;
+        if (tail) {
+          const int r = (wave * JBQ + j) * QRPI + lane / QCPR;
+          const int coff = ((lane % QCPR) ^ swz_key<QRB>(r)) << 4;
+          off = (int)qb + coff < wkbytes ? off : kOOB;
+        }
+        dma16(rb, base + BM * RB + (wave * JBQ + j) * 1024, off);
       }
-      dma16(rb, base + BM * RB + (wave * JB + j) * 1024, off);
+      // the slice's K-blocks kt * SBK + blk; blocks past K read as zero scales
+      const int o = 4 * (wave * 64 + lane);
+      const bool sin = kt * SBK + o / NB < K / 32;
+      dma4(rs, base + BM * RB + BQ + wave * 256,
+           sin ? vs + (uint32_t)(kt * SBK) * (uint32_t)nrows : kOOB);
+    } else {
+#pragma unroll
+      for (int j = 0; j < JB; ++j) {
+        uint32_t off = vb[j] + kb;
+        if (tail) {
+          const int coff = ((lane % CPR) ^ swz_key<RB>((wave * JB + j) * RPI + lrow)) << 4;
+          off = (int)kb + coff < kbytes ? off : kOOB;
+        }
+        dma16(rb, base + BM * RB + (wave * JB + j) * 1024, off);
+      }
     }
     if (kt == 0) setup_a(i);
 #pragma unroll
@@ -377,7 +465,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
   // slice w's loads (an epilogue at slice z0 follows the loads of slices up to
   // z0 + S - 1).  Waits on ds operations too.
   auto wait_slice = [&](int w) {
-    wait_pending<JA + JB, NST, S - 2>(min(S - 2, nz - 1 - w), w <= st_until);
+    wait_pending<PER, NST, S - 2>(min(S - 2, nz - 1 - w), w <= st_until);
   };
   auto frag_addr = [&](int ks, int row) {  // byte in a slice of k-step ks, operand row
     const int byte = (ks * Mm::KS + (lane >> 5) * Mm::EPL) * (int)sizeof(T);
@@ -501,9 +589,21 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int s = 0; s < NSETS; ++s)
-            fb[buf][j][s] =
-                Mm::ld(lb + frag_addr(ks, s * BN + wn * (BN / WN) + j * 32 + (lane & 31)));
+          for (int s = 0; s < NSETS; ++s) {
+            const int r = s * BN + wn * (BN / WN) + j * 32 + (lane & 31);
+            if constexpr (WQ) {
+              // 8 codes (K elements 16 ks + 8 (lane / 32) ..) and their block's scale
+              const int qoff = ks * 8 + (lane >> 5) * 4;
+              const uint32_t word =
+                  *reinterpret_cast<const uint32_t *>(lb + swz<QRB>(r, qoff >> 4) + (qoff & 15));
+              const int sidx = (NSETS == 2 && g.interleaved) ? 2 * (r % BN) + r / BN : r;
+              const uint32_t sb = reinterpret_cast<const uint8_t *>(lb + BQ)[(ks / 2) * NB + sidx];
+              const float sc = __uint_as_float(sb << 23);
+              fb[buf][j][s] = fp4x8_to_bf16(word, sc);
+            } else {
+              fb[buf][j][s] = Mm::ld(lb + frag_addr(ks, r));
+            }
+          }
       };
       load_frags(0, 0);
 #pragma unroll
@@ -550,10 +650,18 @@ using PlainS = Cfg<32, 128, 1, 4, 4, 128>;  // 4 waves, 32 x 32 each
 // three workgroups a CU.
 using GatedT = Cfg<32, 32, 1, 1, 2, 256>;   // 1 wave, 32 x (32 + 32)
 using PlainT = Cfg<32, 32, 1, 1, 2, 256>;   // 1 wave, 32 x 32
+// MXFP4 weights: the same tile shapes; deeper rings (4/6 and 6/8 stages) were
+// measured slower (LDS per workgroup costs occupancy) on the gpt-oss-sized
+// layer at 1, 33 and 512 tokens
+using GatedSQ = Cfg<32, 128, 1, 4, 4, 128>;
+using PlainSQ = Cfg<32, 128, 1, 4, 4, 128>;
+using GatedTQ = Cfg<32, 32, 1, 1, 2, 256>;
+using PlainTQ = Cfg<32, 32, 1, 1, 2, 256>;
 
-template <typename C, int NSETS> constexpr int lds_bytes() {
-  return C::S * (C::BM + NSETS * C::BN) * C::RB + 2 * (kMaxExperts + 1) * 4 +
-         (C::S + 1) * (16 + C::BM * 8);
+template <typename C, int NSETS, bool WQ = false> constexpr int lds_bytes() {
+  return C::S * (C::BM * C::RB + NSETS * C::BN * (WQ ? C::RB / 4 : C::RB) +
+                 (WQ ? C::WM * C::WN * 256 : 0)) +
+         2 * (kMaxExperts + 1) * 4 + (C::S + 1) * (16 + C::BM * 8);
 }
 
 // Upper bound on the tiles of one launch: floor(M / BM) + min(E, M) m-tiles.
@@ -561,16 +669,16 @@ inline int64_t est_tiles(int64_t M, int E, int Nout, int BM, int BN) {
   return (M / BM + (M < E ? M : E)) * ((Nout + BN - 1) / BN);
 }
 
-template <typename T, int NSETS, int EPI, typename C>
+template <typename T, int NSETS, int EPI, typename C, bool WQ = false>
 hipError_t launch_cfg(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
-  constexpr int LDS = lds_bytes<C, NSETS>();
+  constexpr int LDS = lds_bytes<C, NSETS, WQ>();
   constexpr int per_cu = (160 * 1024) / LDS > 0 ? (160 * 1024) / LDS : 1;
   const int64_t tiles = est_tiles(M, E, a.Nout, C::BM, C::BN);
   int64_t grid = (int64_t)device_cus() * (per_cu < 2 ? per_cu : 2);
   if (grid > tiles) grid = tiles;
   grid = (grid + 7) / 8 * 8;  // whole XCD rounds; surplus workgroups get no tiles
   static_assert(LDS <= 160 * 1024, "LDS budget");
-  hipLaunchKernelGGL((grouped_gemm<T, NSETS, EPI, C::BM, C::BN, C::WM, C::WN, C::S, C::RB>),
+  hipLaunchKernelGGL((grouped_gemm<T, NSETS, EPI, C::BM, C::BN, C::WM, C::WN, C::S, C::RB, WQ>),
                      dim3((unsigned)grid), dim3(64 * C::WM * C::WN), 0, s, a);
   return hipGetLastError();
 }
@@ -598,12 +706,26 @@ inline double launch_cost(int64_t tiles, int64_t cus, int BM, int BN, double sur
 // 128-row tiles, so it takes the 256-row tile; above that, whichever tile the
 // cost model favours (the 128-row tile wins where 256-row tiles would leave a
 // second, mostly empty round, e.g. at 256 rows per expert).
+// MXFP4 weights run on the one-phase tiles only (the 32-row and one-wave
+// tiles, which is what weight-streaming batches take anyway).
+template <typename T, int NSETS, int EPI>
+hipError_t launch_wq(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
+  using Sm = typename std::conditional<NSETS == 2, GatedSQ, PlainSQ>::type;
+  using Tn = typename std::conditional<NSETS == 2, GatedTQ, PlainTQ>::type;
+  if (expected_tiles(M, E, a.Nout, Sm::BM, Sm::BN) < device_cus())
+    return launch_cfg<T, NSETS, EPI, Tn, true>(a, M, E, s);
+  return launch_cfg<T, NSETS, EPI, Sm, true>(a, M, E, s);
+}
+
 template <typename T, int NSETS, int EPI>
 hipError_t launch_t(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
   using L = typename std::conditional<NSETS == 2, GatedL, PlainL>::type;
   using Md = typename std::conditional<NSETS == 2, GatedM, PlainM>::type;
   using Sm = typename std::conditional<NSETS == 2, GatedS, PlainS>::type;
   using Tn = typename std::conditional<NSETS == 2, GatedT, PlainT>::type;
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (a.wscale) return launch_wq<T, NSETS, EPI>(a, M, E, s);
+  }
   const int64_t cus = device_cus();
   const int64_t tm = expected_tiles(M, E, a.Nout, Md::BM, Md::BN);
   if (M < 48 * (int64_t)E || tm < cus / 2) {
@@ -623,7 +745,8 @@ hipError_t launch_t(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
 hipError_t launch_gemm1(const void *x, const void *w13, void *act_out, const int32_t *offsets,
                         const int32_t *col_sorted, moe_dtype_t dt, int64_t n_tokens, int topk,
                         int n_experts, int hidden, int inter, moe_act_t act,
-                        moe_w13_layout_t layout, ActParams p, hipStream_t s, bool sorted_rows) {
+                        moe_w13_layout_t layout, ActParams p, hipStream_t s, bool sorted_rows,
+                        const uint8_t *w13_scale) {
   const int64_t M = n_tokens * topk;
   const size_t es = dt == MOE_BF16 ? 2 : 4;
   // A is x [N, hidden] read through the gather index, or (sorted_rows) rows
@@ -631,7 +754,7 @@ hipError_t launch_gemm1(const void *x, const void *w13, void *act_out, const int
   const int64_t a_rows = sorted_rows ? M : n_tokens;
   GemmArgs a{x, w13, act_out, offsets, col_sorted, nullptr, (uint32_t)(a_rows * hidden * es),
              (uint32_t)(M * inter * es), 0, n_experts, hidden, inter, topk, sorted_rows ? 0 : 1,
-             layout == MOE_W13_INTERLEAVED, act, p};
+             layout == MOE_W13_INTERLEAVED, act, p, w13_scale};
   const bool gated = act != MOE_ACT_RELU2;
   const bool clamp = std::isfinite(p.limit);  // an infinite limit clamps nothing
   if (dt == MOE_BF16)
@@ -646,13 +769,13 @@ hipError_t launch_gemm1(const void *x, const void *w13, void *act_out, const int
 hipError_t launch_gemm2(const void *act_in, const void *w2, void *y, const int32_t *offsets,
                         const int32_t *col_sorted, const void *gate_scal, moe_dtype_t gate_dt,
                         moe_dtype_t dt, int64_t n_tokens, int topk, int n_experts, int hidden,
-                        int inter, bool direct_out, hipStream_t s) {
+                        int inter, bool direct_out, hipStream_t s, const uint8_t *w2_scale) {
   const int64_t M = n_tokens * topk;
   const size_t es = dt == MOE_BF16 ? 2 : 4;
   const int64_t c_rows = direct_out ? n_tokens : M;
   GemmArgs a{act_in, w2, y, offsets, col_sorted, gate_scal, (uint32_t)(M * inter * es),
              (uint32_t)(c_rows * hidden * es), gate_dt == MOE_BF16, n_experts, inter, hidden,
-             topk, 0, 0, 0, ActParams{1.f, 0.f, 0.f}};
+             topk, 0, 0, 0, ActParams{1.f, 0.f, 0.f}, w2_scale};
   if (dt == MOE_BF16)
     return direct_out ? launch_t<bf16_t, 1, EPI_OUT>(a, M, n_experts, s)
                       : launch_t<bf16_t, 1, EPI_Y>(a, M, n_experts, s);

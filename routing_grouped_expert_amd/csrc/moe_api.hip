@@ -169,19 +169,22 @@ moe_status_t check_share(int32_t e, int32_t lo, int32_t nl) {
 
 hipError_t run_w13(const void *x, moe_dtype_t dtype, int64_t n, int32_t hidden, const void *w13,
                    int32_t e, int32_t inter, int32_t k, moe_act_t act, moe_w13_layout_t layout,
-                   const ActParams &prm, const moe_routing_t *r, void *a, hipStream_t s) {
+                   const ActParams &prm, const moe_routing_t *r, void *a, hipStream_t s,
+                   const void *w13_scale = nullptr) {
   return moe::launch_gemm1(x, w13, a, r->offsets, r->col_sorted, dtype, n, k, e, hidden, inter,
-                           act, layout, prm, s);
+                           act, layout, prm, s, false,
+                           reinterpret_cast<const uint8_t *>(w13_scale));
 }
 
 hipError_t run_w2(const void *a, moe_dtype_t dtype, int64_t n, int32_t hidden, const void *w2,
                   int32_t e, int32_t inter, int32_t k, const moe_routing_t *r, void *out, void *y,
-                  hipStream_t s, bool share = false, bool unit_gate = false) {
+                  hipStream_t s, bool share = false, bool unit_gate = false,
+                  const void *w2_scale = nullptr) {
   const bool direct = k == 1;  // one row per token: GEMM2 writes the output rows itself
   hipError_t err = moe::launch_gemm2(a, w2, direct ? out : y, r->offsets, r->col_sorted,
                                      unit_gate ? nullptr : r->gate_scal,
                                      (moe_dtype_t)r->w_dtype, dtype, n, k, e, hidden, inter,
-                                     direct, s);
+                                     direct, s, reinterpret_cast<const uint8_t *>(w2_scale));
   if (err != hipSuccess) return err;
   // an expert share leaves the rows of tokens routed elsewhere to be zeroed
   if (direct) return share ? moe::launch_zero_unrouted(r->row_sorted, out, dtype, n, hidden, s)
@@ -193,14 +196,17 @@ moe_status_t run_experts(const void *x, moe_dtype_t dtype, int64_t n, int32_t hi
                          const void *w13, const void *w2, int32_t e, int32_t inter, int32_t k,
                          moe_act_t act, moe_w13_layout_t layout, const ActParams &prm,
                          const moe_routing_t *r, void *out, void *ws, hipStream_t s,
-                         bool share = false) {
+                         bool share = false, const void *w13_scale = nullptr,
+                         const void *w2_scale = nullptr) {
   // workspace: activation rows a[M, inter], then (topk > 1) weighted rows y[M, hidden]
   char *base = reinterpret_cast<char *>(ws);
   void *a = base;
   void *y = base + align256((size_t)n * k * inter * dsize(dtype));
-  if (run_w13(x, dtype, n, hidden, w13, e, inter, k, act, layout, prm, r, a, s) != hipSuccess)
+  if (run_w13(x, dtype, n, hidden, w13, e, inter, k, act, layout, prm, r, a, s, w13_scale) !=
+      hipSuccess)
     return MOE_ERR_HIP;
-  if (run_w2(a, dtype, n, hidden, w2, e, inter, k, r, out, y, s, share) != hipSuccess)
+  if (run_w2(a, dtype, n, hidden, w2, e, inter, k, r, out, y, s, share, false, w2_scale) !=
+      hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
 }
@@ -426,6 +432,74 @@ moe_status_t moe_experts_weighted_input(const void *x, moe_dtype_t dtype, int64_
              true) != hipSuccess)
     return MOE_ERR_HIP;
   return MOE_OK;
+}
+
+moe_status_t moe_quantize_mxfp4(const void *w, moe_dtype_t dtype, int32_t n_experts,
+                                int32_t rows, int32_t k, void *q, void *scales, void *stream) {
+  if (!dtype_ok(dtype)) return MOE_ERR_DTYPE;
+  if (n_experts < 1 || rows < 1 || k < 32 || k % 32 || k > (1 << 24)) return MOE_ERR_SHAPE;
+  if ((int64_t)n_experts * rows * k * (int64_t)dsize(dtype) > 0x7fffffffLL * 8)
+    return MOE_ERR_SHAPE;
+  moe_status_t st = check_ptrs({w, q});
+  if (st != MOE_OK) return st;
+  if (!scales) return MOE_ERR_NULL;
+  return moe::launch_quantize_mxfp4(w, dtype, n_experts, rows, k, q, scales,
+                                    (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+namespace {
+// MXFP4 weights: bf16 layer, K of both GEMMs (hidden, inter) a multiple of 32,
+// codes and scales present and 16-byte aligned.
+moe_status_t check_mxfp4(moe_dtype_t dtype, int32_t hidden, int32_t inter, const void *w13_s,
+                         const void *w2_s) {
+  if (dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (hidden % 32 || inter % 32) return MOE_ERR_SHAPE;
+  return check_ptrs({w13_s, w2_s});
+}
+}  // namespace
+
+moe_status_t moe_experts_mxfp4(const void *x, moe_dtype_t dtype, int64_t n_tokens,
+                               int32_t hidden, const void *w13_q, const void *w13_s,
+                               const void *w2_q, const void *w2_s, int32_t n_experts,
+                               int32_t inter, int32_t topk, moe_act_t act,
+                               moe_w13_layout_t layout, const moe_act_params_t *params,
+                               const moe_routing_t *routing, void *out, void *workspace,
+                               size_t ws_bytes, void *stream) {
+  ActParams prm;
+  moe_status_t st = check_experts(x, dtype, n_tokens, hidden, w13_q, w2_q, n_experts, inter,
+                                  topk, act, layout, params, routing, out, workspace, ws_bytes,
+                                  &prm);
+  if (st != MOE_OK) return st;
+  if ((st = check_mxfp4(dtype, hidden, inter, w13_s, w2_s)) != MOE_OK || n_tokens == 0)
+    return st;
+  return run_experts(x, dtype, n_tokens, hidden, w13_q, w2_q, n_experts, inter, topk, act, layout,
+                     prm, routing, out, workspace, (hipStream_t)stream, false, w13_s, w2_s);
+}
+
+moe_status_t moe_forward_mxfp4(const void *x, const void *logits, moe_dtype_t dtype,
+                               int64_t n_tokens, int32_t hidden, const void *w13_q,
+                               const void *w13_s, const void *w2_q, const void *w2_s,
+                               int32_t n_experts, int32_t inter, int32_t topk, moe_act_t act,
+                               moe_w13_layout_t layout, const moe_act_params_t *params,
+                               const moe_routing_t *routing_out, void *out, void *workspace,
+                               size_t ws_bytes, void *stream) {
+  ActParams prm;
+  moe_status_t st = check_route(logits, dtype, n_tokens, n_experts, topk, routing_out, workspace,
+                                ws_bytes);
+  if (st != MOE_OK) return st;
+  st = check_experts(x, dtype, n_tokens, hidden, w13_q, w2_q, n_experts, inter, topk, act,
+                     layout, params, routing_out, out, workspace, ws_bytes, &prm);
+  if (st != MOE_OK) return st;
+  if ((st = check_mxfp4(dtype, hidden, inter, w13_s, w2_s)) != MOE_OK || n_tokens == 0)
+    return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (moe::launch_route(logits, dtype, n_tokens, n_experts, topk, 0, n_experts, routing_out,
+                        workspace, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return run_experts(x, dtype, n_tokens, hidden, w13_q, w2_q, n_experts, inter, topk, act, layout,
+                     prm, routing_out, out, workspace, s, false, w13_s, w2_s);
 }
 
 const char *moe_status_str(moe_status_t status) {

@@ -61,17 +61,20 @@ struct ActParams {
 };
 
 // GEMM1: a[M, inter] = act(xs[M, hidden] . W13[e]^T) for every expert segment.
+// With w13_scale (bf16 only) W13 holds MXFP4 codes [E, rows, hidden / 2] and
+// w13_scale the scales [E, hidden / 32, rows]; GEMM2 likewise with w2_scale.
 hipError_t launch_gemm1(const void *x, const void *w13, void *act_out, const int32_t *offsets,
                         const int32_t *col_sorted, moe_dtype_t dt, int64_t n_tokens, int topk,
                         int n_experts, int hidden, int inter, moe_act_t act,
                         moe_w13_layout_t layout, ActParams p, hipStream_t s,
-                        bool sorted_rows = false);
+                        bool sorted_rows = false, const uint8_t *w13_scale = nullptr);
 // GEMM2: y = gate_scal[p] * (a[p] . W2[e]^T) (gate_scal NULL: weight 1); stored
 // to y_sorted[M, hidden], or (topk == 1) straight to out[token(p)].
 hipError_t launch_gemm2(const void *act_in, const void *w2, void *y, const int32_t *offsets,
                         const int32_t *col_sorted, const void *gate_scal, moe_dtype_t gate_dt,
                         moe_dtype_t dt, int64_t n_tokens, int topk, int n_experts, int hidden,
-                        int inter, bool direct_out, hipStream_t s);
+                        int inter, bool direct_out, hipStream_t s,
+                        const uint8_t *w2_scale = nullptr);
 // out[t] = sum_j y_sorted[row_sorted[t*topk + j]] (fp32, slot order), slots
 // with row_sorted = -1 skipped.
 hipError_t launch_combine(const void *y_sorted, const int32_t *row_sorted, void *out,
@@ -83,6 +86,9 @@ hipError_t launch_scale_gather(const void *x, const int32_t *col_sorted, const v
                                moe_dtype_t gate_dt, const int32_t *offsets, int n_experts,
                                moe_dtype_t dt, int64_t n_tokens, int topk, int hidden, void *xs,
                                hipStream_t s);
+// MXFP4: w [E, rows, k] -> codes q [E, rows, k/2], scales [E, k/32, rows].
+hipError_t launch_quantize_mxfp4(const void *w, moe_dtype_t dt, int n_experts, int rows, int k,
+                                 void *q, void *scales, hipStream_t s);
 // topk == 1: out[t] = 0 where row_sorted[t] = -1.
 hipError_t launch_zero_unrouted(const int32_t *row_sorted, void *out, moe_dtype_t dt,
                                 int64_t n_tokens, int hidden, hipStream_t s);
