@@ -345,19 +345,18 @@ __device__ __forceinline__ void rank_chunk(int E, int nlive, Lds &L) {
     }
   }
   __syncthreads();
-  // exclusive prefix over the chunk's groups, one wave per expert and one
-  // lane per group (a shuffle scan)
-  static_assert(TW <= 64, "one lane per 64-token group");
-  for (int e = wave; e < E; e += NWV) {
-    const int c = lane < TW ? L.cnt[lane][e] : 0;
-    int incl = c;
+  // exclusive prefix over the chunk's (at most four) groups: one thread per
+  // expert walks them in order
+  static_assert(TW <= 4, "a short serial prefix over the groups");
+  for (int e = tid; e < E; e += THREADS) {
+    int run = 0;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
+    for (int g = 0; g < TW; ++g) {
+      const int c = L.cnt[g][e];
+      L.cnt[g][e] = run;
+      run += c;
     }
-    if (lane < TW) L.cnt[lane][e] = incl - c;
-    if (lane == 63) L.tot[e] = incl;
+    L.tot[e] = run;
   }
   __syncthreads();
 }
@@ -829,6 +828,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // workgroup for up to 4096 tokens of a few experts was measured slower than
 // the two kernels: 16.8 against 11.1 us at N = 4096, E = 8.)
 constexpr int kFusedTokens = 256;
+// Batches of at most 64 tokens (decode) use a one-group chunk: the rank phase
+// then spreads the experts over all 16 waves of the workgroup.
+constexpr int kSmallTokens = 64;
+static_assert(kGateFusedTokens <= kSmallTokens, "the router-GEMM prologue paths use the small chunk");
 enum RoutePath { kPathFused, kPathBlocks };
 inline RoutePath route_path(int64_t N, int E, int K) {
   (void)E;
@@ -872,7 +875,7 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
     }
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((route_fused<T, 1024, 1, ChunkLds<T, kFusedTokens>, 2>), dim3(1),
+    hipLaunchKernelGGL((route_fused<T, 1024, 1, ChunkLds<T, kSmallTokens>, 2>), dim3(1),
                        dim3(1024), 0, s, logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw,
                        r->bitmatrix, r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs, x,
                        wg, H, lw, part, np);
@@ -885,7 +888,7 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
                          r->topk_idx, tw, r->bitmatrix, r->col_sum, r->offsets, r->col_sorted,
                          r->row_sorted, gs, x, wg, H, lw, nullptr, 0);
     };
-    using L = ChunkLds<T, kFusedTokens>;
+    using L = ChunkLds<T, kSmallTokens>;
     switch (gate_bucket(E)) {
       case 32: fused(route_fused<T, 1024, 1, L, 1, 32>); break;
       case 64: fused(route_fused<T, 1024, 1, L, 1, 64>); break;
@@ -916,7 +919,11 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
     if (err != hipSuccess) return err;
   }
   if (path == kPathFused) {
-    if (wide)
+    if (N <= kSmallTokens)  // (`wide` needs N > 64)
+      hipLaunchKernelGGL((route_fused<T, 1024, 1, ChunkLds<T, kSmallTokens>>), dim3(1), dim3(1024),
+                         0, s, logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw, r->bitmatrix,
+                         r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs);
+    else if (wide)
       hipLaunchKernelGGL((route_fused<T, 1024, 2, ChunkLds<T, kFusedTokens>>), dim3(1), dim3(1024),
                          0, s, logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw, r->bitmatrix,
                          r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs);
