@@ -34,33 +34,12 @@
 #include <cmath>
 #include <type_traits>
 
+#include "gemm_common.h"
 #include "lds_dma.h"
-#include "moe_common.h"
 
 namespace moe {
 namespace {
 
-
-// Epilogue kinds: GEMM1 applies the activation (gated without or with the
-// clamp, or ReLU^2); GEMM2 scales by the routing weight and writes the sorted
-// row (EPI_Y) or, with one expert per token, the token's output row (EPI_OUT).
-enum { EPI_GATED = 0, EPI_Y = 1, EPI_OUT = 2, EPI_GATED_CLAMP = 3, EPI_RELU2 = 4 };
-
-struct GemmArgs {
-  const void *A;                 // GEMM1: x [N, K]; GEMM2: a [M, K]
-  const void *W;                 // [E, NSETS * Nout, K]
-  void *C;                       // output rows
-  const int32_t *offsets;        // [E + 1]
-  const int32_t *col_sorted;     // [M]
-  const void *gate_scal;         // [M] (GEMM2)
-  uint32_t a_bytes;              // bytes of A (buffer range)
-  uint32_t c_bytes;              // bytes of C
-  int gate_bf16, E, K, Nout, topk, gather, interleaved, act;
-  ActParams prm;
-  // MXFP4 weights: W holds E2M1 codes [E, NSETS * Nout, K / 2] and wscale the
-  // E8M0 scales [E, K / 32, NSETS * Nout] (nullptr: W is in the A dtype)
-  const uint8_t *wscale;
-};
 
 template <typename T> struct Mma;
 template <> struct Mma<bf16_t> {
@@ -94,38 +73,6 @@ template <int RB> __device__ __forceinline__ int swz_key(int row) {
 }
 template <int RB> __device__ __forceinline__ int swz(int row, int chunk) {
   return row * RB + ((chunk ^ swz_key<RB>(row)) << 4);
-}
-
-// 8 E2M1 codes (element i in nibble i of `word`) times the scale `sc`, as the
-// bf16 fragment of 8 consecutive K elements.  The hardware conversion takes
-// byte b and yields its low nibble's value first.
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ bf16x8_t fp4x8_to_bf16(uint32_t word, float sc) {
-  u32x4_t w;
-  w[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 0));
-  w[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 1));
-  w[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 2));
-  w[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 3));
-  return __builtin_bit_cast(bf16x8_t, w);
-}
-
-// Activation of one (gate, up) pair.  Gated kinds evaluate the logistic
-// function as 1 / (1 + 2^(nal * g)) with nal = -alpha * log2(e), using the
-// hardware exp2 and reciprocal (about 1 ulp each); the clamp variant first
-// limits the gate from above and the up value to [-limit, limit].
-template <int EPI>
-__device__ __forceinline__ float act_val(float g, float u, float nal, const ActParams &p) {
-  if constexpr (EPI == EPI_RELU2) {
-    const float r = fmaxf(g, 0.f);
-    return r * r;
-  } else {
-    if constexpr (EPI == EPI_GATED_CLAMP) {
-      g = fminf(g, p.limit);
-      u = fminf(fmaxf(u, -p.limit), p.limit);
-    }
-    const float e = __builtin_amdgcn_exp2f(nal * g);
-    return g * __builtin_amdgcn_rcpf(1.f + e) * (u + p.beta);
-  }
 }
 
 // Four consecutive output elements of one row.
@@ -757,6 +704,9 @@ hipError_t launch_gemm1(const void *x, const void *w13, void *act_out, const int
              layout == MOE_W13_INTERLEAVED, act, p, w13_scale};
   const bool gated = act != MOE_ACT_RELU2;
   const bool clamp = std::isfinite(p.limit);  // an infinite limit clamps nothing
+  if (gemv_fits(dt, n_tokens, hidden, inter))
+    return launch_gemv(a, gated ? 2 : 1, !gated ? EPI_RELU2 : clamp ? EPI_GATED_CLAMP : EPI_GATED,
+                       n_tokens, M, s);
   if (dt == MOE_BF16)
     return !gated  ? launch_t<bf16_t, 1, EPI_RELU2>(a, M, n_experts, s)
            : clamp ? launch_t<bf16_t, 2, EPI_GATED_CLAMP>(a, M, n_experts, s)
@@ -776,6 +726,8 @@ hipError_t launch_gemm2(const void *act_in, const void *w2, void *y, const int32
   GemmArgs a{act_in, w2, y, offsets, col_sorted, gate_scal, (uint32_t)(M * inter * es),
              (uint32_t)(c_rows * hidden * es), gate_dt == MOE_BF16, n_experts, inter, hidden,
              topk, 0, 0, 0, ActParams{1.f, 0.f, 0.f}, w2_scale};
+  if (gemv_fits(dt, n_tokens, inter, hidden))
+    return launch_gemv(a, 1, direct_out ? EPI_OUT : EPI_Y, n_tokens, M, s);
   if (dt == MOE_BF16)
     return direct_out ? launch_t<bf16_t, 1, EPI_OUT>(a, M, n_experts, s)
                       : launch_t<bf16_t, 1, EPI_Y>(a, M, n_experts, s);

@@ -72,6 +72,13 @@ MX = [
     ("top1", 300, 128, 128, 8, 1, "silu", "packed", {"limit": 3.0}),
     ("ktail", 64, 160, 96, 4, 3, "silu", "interleaved", {}),
     ("many-rows", 2048, 128, 128, 4, 2, "silu", "packed", {}),
+    # decode-sized batches (matrix-vector kernel); the packed ones read the
+    # scales of two row runs
+    ("n1-oai-packed", 1, 256, 192, 16, 4, "swiglu_oai", "packed",
+     {"alpha": 1.702, "beta": 1.0, "limit": 7.0}),
+    ("n3-silu-interleaved", 3, 160, 96, 4, 3, "silu", "interleaved", {}),
+    ("n8-relu2-top1", 8, 96, 160, 4, 1, "relu2", "packed", {}),
+    ("n8-all-rows-k4096", 8, 4096, 128, 2, 2, "silu", "packed", {}),
 ]
 
 
