@@ -5,7 +5,7 @@
 // activation, or w2 with the routing weight), the one the minimind issue #835
 // page ("Summary") and the vLLM PR #47106 report (activation kinds, w13
 // layouts) describe.  With at most a handful of tokens the layer is a weight
-// stream: every weight is read once and used by one to eight rows, so the
+// stream: every weight is read once and used by a few rows, so the
 // kernel is shaped for bytes in flight, not for matrix-core reuse.
 //
 // Design (this file's own):
@@ -350,9 +350,12 @@ hipError_t launch_epi(const GemmArgs &a, int64_t M, int cb, hipStream_t s) {
 
 }  // namespace
 
-bool gemv_fits(moe_dtype_t dt, int64_t n_tokens, int K, int Nout) {
-  return dt == MOE_BF16 && n_tokens <= kGemvMaxTokens && K % 8 == 0 && K <= 4096 &&
-         Nout % 8 == 0;
+bool gemv_fits(moe_dtype_t dt, int64_t n_tokens, int topk, int n_experts, int K, int Nout,
+               bool mxfp4) {
+  if (dt != MOE_BF16 || n_tokens > kGemvMaxTokens || K % 8 != 0 || K > 4096 || Nout % 8 != 0)
+    return false;
+  const int64_t m = n_tokens * topk;
+  return mxfp4 ? 2 * m <= 3 * (int64_t)n_experts : m <= 3 * (int64_t)n_experts;
 }
 
 hipError_t launch_gemv(const GemmArgs &a, int nsets, int epi, int64_t n_tokens, int64_t M,

@@ -1,5 +1,5 @@
-"""Decode-sized layers (at most 8 tokens, bf16), which run the expert GEMMs as
-grouped matrix-vector products, against the CPU oracle.
+"""Decode-sized layers (at most 32 tokens, bf16, few rows per expert), which run
+the expert GEMMs as grouped matrix-vector products, against the CPU oracle.
 
 The cases cover every epilogue (gated with and without the clamp, ReLU^2, the
 routing weight into sorted rows and, with one expert per token, straight into
@@ -32,11 +32,18 @@ CASES = [
     ("n5-relu2-top1", 5, 520, 1032, 5, 1, "relu2", "packed", {}),
     ("n8-silu-top1", 8, 64, 64, 3, 1, "silu", "interleaved", {"limit": 0.5}),
     ("n7-relu2-k2", 7, 96, 160, 7, 2, "relu2", "packed", {}),
-    # k = E: every expert holds all 8 rows; K = 4096 stages 6 rows at a time
-    ("n8-all-rows-k4096", 8, 4096, 256, 2, 2, "silu", "interleaved", {}),
-    ("n8-all-rows-i4096", 8, 256, 4096, 2, 2, "swiglu_oai", "packed",
-     {"alpha": 1.702, "beta": 1.0, "limit": 7.0}),
     ("n4-ragged-cols", 4, 1032, 520, 9, 2, "silu", "packed", {}),
+    ("n24-k2", 24, 256, 384, 16, 2, "silu", "packed", {}),
+    ("n32-top1", 32, 136, 200, 16, 1, "relu2", "packed", {}),
+]
+
+# Skewed logits send nearly every token to one expert: that expert holds more
+# rows than one LDS group (K = 4096 stages 6 rows at a time, smaller K 8).
+SKEWED = [
+    ("skew-n32-k4096", 32, 4096, 256, 16, 1, "silu", "interleaved", {}),
+    ("skew-n32-i4096", 32, 256, 4096, 24, 2, "swiglu_oai", "packed",
+     {"alpha": 1.702, "beta": 1.0, "limit": 7.0}),
+    ("skew-n20-small", 20, 128, 136, 24, 3, "silu", "packed", {}),
 ]
 
 
@@ -49,7 +56,17 @@ def test_decode_layer(case):
     run_layer(spec)
 
 
-@pytest.mark.parametrize("n", [1, 8])
+@pytest.mark.parametrize("case", SKEWED, ids=[c[0] for c in SKEWED])
+def test_decode_skewed(case):
+    name, n, h, i, e, k, act, layout, params = case
+    spec = LayerSpec(name, n_tokens=n, hidden=h, inter=i, n_experts=e, topk=k, dtype="bf16",
+                     act=act, layout=layout, alpha=params.get("alpha"), beta=params.get("beta"),
+                     limit=params.get("limit"), zipf_s=6.0, seed=5 * n + h)
+    _, routing, _ = run_layer(spec)
+    assert int(routing.col_sum.max()) > 8, "the skew should overfill one LDS group"
+
+
+@pytest.mark.parametrize("n", [1, 8, 32])
 def test_decode_gptoss(n):
     run_layer(layer_spec("gptoss", n_tokens=n, name=f"gptoss_n{n}"))
 
@@ -63,7 +80,7 @@ def test_decode_deterministic():
 
 @pytest.mark.parametrize("lo,nl", [(0, 5), (9, 7)])
 def test_decode_share(lo, nl):
-    run_share(_share_spec("gptoss", lo, nl, n_tokens=6, hidden=256, inter=384, n_experts=16))
+    run_share(_share_spec("gptoss", lo, nl, n_tokens=2, hidden=256, inter=384, n_experts=16))
 
 
 def test_decode_weighted_input():

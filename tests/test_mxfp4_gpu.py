@@ -76,10 +76,20 @@ MX = [
     # scales of two row runs
     ("n1-oai-packed", 1, 256, 192, 16, 4, "swiglu_oai", "packed",
      {"alpha": 1.702, "beta": 1.0, "limit": 7.0}),
-    ("n3-silu-interleaved", 3, 160, 96, 4, 3, "silu", "interleaved", {}),
-    ("n8-relu2-top1", 8, 96, 160, 4, 1, "relu2", "packed", {}),
-    ("n8-all-rows-k4096", 8, 4096, 128, 2, 2, "silu", "packed", {}),
+    ("n3-silu-interleaved", 3, 160, 96, 8, 3, "silu", "interleaved", {}),
+    ("n8-relu2-top1", 8, 96, 160, 8, 1, "relu2", "packed", {}),
+    ("n24-skew-k4096", 24, 4096, 128, 32, 1, "silu", "packed", {"zipf_s": 6.0}),
 ]
+
+
+def _same_kernels(n, k, e):
+    """True when the MXFP4 and the bf16 layer take the same GEMM kernels (then
+    the results are the same bits): both the matrix-vector kernel (at most 32
+    tokens, n * k <= 1.5 E for MXFP4 and <= 3 E for bf16), or both the one-wave /
+    32-row MFMA tiles (n * k < 48 E, outside the matrix-vector range)."""
+    m = n * k
+    gv_mx, gv_16 = n <= 32 and 2 * m <= 3 * e, n <= 32 and m <= 3 * e
+    return (gv_mx and gv_16) or (not gv_mx and not gv_16 and m < 48 * e)
 
 
 @pytest.mark.parametrize("case", MX, ids=[c[0] for c in MX])
@@ -87,7 +97,7 @@ def test_mxfp4_layer(case):
     name, n, h, i, e, k, act, layout, params = case
     spec = LayerSpec(name, n_tokens=n, hidden=h, inter=i, n_experts=e, topk=k, dtype="bf16",
                      act=act, layout=layout, alpha=params.get("alpha"), beta=params.get("beta"),
-                     limit=params.get("limit"), seed=n + 3 * h)
+                     limit=params.get("limit"), zipf_s=params.get("zipf_s"), seed=n + 3 * h)
     print(f"[mxfp4] {spec}", flush=True)
     layer = make_layer(spec)
     w = _quantised(layer)
@@ -100,7 +110,7 @@ def test_mxfp4_layer(case):
     ref = oracle.moe_ffn(layer.x, ref_r.topk_idx, ref_r.topk_w, d13, d2, act, layout,
                          act_params(spec))
     print(f"[mxfp4] {name}: {assert_output_close(out, ref, name)}", flush=True)
-    if n * k < 48 * e:  # the bf16 path takes the same tiles: same bits
+    if _same_kernels(n, k, e):
         deq13 = torch.stack([torch.from_numpy(d13[j]) for j in range(e)]).to(torch.bfloat16)
         deq2 = torch.stack([torch.from_numpy(d2[j]) for j in range(e)]).to(torch.bfloat16)
         ref16 = moe_experts(x, deq13.to(DEV), deq2.to(DEV), routing, act, layout,
