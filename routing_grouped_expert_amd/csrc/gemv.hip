@@ -15,9 +15,9 @@
 //  * A wave owns RPW weight rows (the gate and up rows of its columns, or the
 //    plain rows) and loads all of them, whole, into registers before anything
 //    else: lane l holds the K elements 8 (l + 64 t) .. + 7 of every row, t < T.
-//    That is ~23 KB a wave in flight at K = 2880 (bf16: 4 rows, 16-byte loads;
-//    MXFP4: 16 rows of E2M1 codes, 4-byte loads), so a few waves a CU cover
-//    HBM latency.
+//    That is ~23 KB a wave in flight at K = 2880 with bf16 weights (4 rows,
+//    16-byte loads) and ~12 KB with MXFP4 weights (8 rows of E2M1 codes,
+//    4-byte loads), so a few waves a CU cover HBM latency.
 //  * The A rows of the expert (the gathered token rows, or the sorted
 //    activation rows) are staged in LDS, cb at a time; each lane reads the
 //    16-byte pieces matching its weight pieces.  Products accumulate in fp32
@@ -29,9 +29,9 @@
 //    partner's copy of that half, until a lane holds the gate and up sums of
 //    one output column (or the one sum of a plain column); the remaining lane
 //    bits are summed out.  Then one lane per column runs the epilogue.
-//  * MXFP4 scales: the 4 lanes that share a K-block load the 16 scale bytes of
-//    the wave's rows as four dwords and broadcast them inside the quad with
-//    DPP, so no lane loads single bytes.
+//  * MXFP4 scales: the 4 lanes that share a K-block load the 8 scale bytes of
+//    the wave's rows as dwords and broadcast them inside the quad with DPP, so
+//    no lane loads single bytes.
 #include "gemm_common.h"
 #include "lds_dma.h"
 
@@ -39,6 +39,12 @@ namespace moe {
 namespace {
 
 constexpr int kGemvWaves = 4;
+// weight rows a wave streams.  FP4 rows are a quarter of the bytes, but 16
+// of them a wave (as many bytes in flight as 4 bf16 rows) measured 20 % slower
+// than 8 at one token: the per-row decode and dot products, not the loads,
+// bound those waves, and 8 rows give twice the workgroups.
+constexpr int kRowsBf16 = 4, kRowsFp4 = 8;
+template <bool WQ> constexpr int rows_per_wave() { return WQ ? kRowsFp4 : kRowsBf16; }
 constexpr int kGemvLdsBudget = 48 * 1024;  // LDS for staged A rows
 
 // acc + a.lo * b.lo + a.hi * b.hi on packed bf16 pairs (v_dot2_f32_bf16)
@@ -91,7 +97,7 @@ template <int CTRL> __device__ __forceinline__ uint32_t dpp_b(uint32_t v) {
 template <int NSETS, int EPI, bool WQ, int T>
 __global__ __launch_bounds__(64 * kGemvWaves) void grouped_gemv(GemmArgs g, int cb) {
   constexpr int NW = kGemvWaves;
-  constexpr int RPW = WQ ? 16 : 4;   // weight rows per wave
+  constexpr int RPW = rows_per_wave<WQ>();  // weight rows per wave
   constexpr int RC = RPW / NSETS;    // output columns per wave
   constexpr int CW = WQ ? 1 : 4;     // dwords per lane per 8-element piece
   constexpr bool META = EPI == EPI_Y || EPI == EPI_OUT;
@@ -190,17 +196,18 @@ __global__ __launch_bounds__(64 * kGemvWaves) void grouped_gemv(GemmArgs g, int 
       }
     }
   // MXFP4 scales: quad lane j = lane % 4 loads the 4 bytes of the wave's local
-  // rows 4j .. 4j + 3 at K-block (lane + 64 t) / 4.  Local row order: column-
-  // major pairs (interleaved and plain) or the gate run then the up run
-  // (packed); either way 4 consecutive local rows are 4 consecutive weight
-  // rows, 4-byte aligned (Nout and n0 are multiples of 8).
+  // rows 4j' .. 4j' + 3, j' = j % (RPW / 4), at K-block (lane + 64 t) / 4.
+  // Local row order: column-major pairs (interleaved and plain) or the gate
+  // run then the up run (packed); either way 4 consecutive local rows are 4
+  // consecutive weight rows, 4-byte aligned (Nout and n0 are multiples of 4).
   uint32_t scw[WQ ? T : 1], scq[WQ ? T : 1][4];
   const bool packed = NSETS == 2 && !g.interleaved;
   if constexpr (WQ) {
     const uint32_t sbytes = (uint32_t)(K / 32) * (uint32_t)nrows;
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(g.wscale) + (size_t)e * sbytes, (short)0, (int)sbytes, kRsrcWord3);
-    const int l0 = 4 * (lane & 3);
+    static_assert(RPW == 8 || RPW == 16, "four-row scale dwords, one or two a quad lane");
+    const int l0 = 4 * ((lane & 3) % (RPW / 4));
     const int i0 = packed ? l0 % RC : l0 / NSETS, s0 = packed ? l0 / RC : l0 % NSETS;
     const uint32_t mr = (uint32_t)memrow(i0, s0);
     const bool col_ok = n0 + i0 < Nout;
@@ -322,7 +329,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void grouped_gemv(GemmArgs g, int 
 
 template <int NSETS, int EPI, bool WQ>
 hipError_t launch_sets(const GemmArgs &a, int64_t M, int cb, hipStream_t s) {
-  constexpr int RC = (WQ ? 16 : 4) / NSETS;
+  constexpr int RC = rows_per_wave<WQ>() / NSETS;
   const unsigned gx = (unsigned)((a.Nout + RC * kGemvWaves - 1) / (RC * kGemvWaves));
   const unsigned gy = (unsigned)(M < a.E ? M : a.E);
   const int nj = (cb * (a.K / 8) + 64 * kGemvWaves - 1) / (64 * kGemvWaves);
