@@ -163,6 +163,17 @@ def cpu_baseline(spec, layer, budget_s: float):
                       f"routing + masked per-expert FFN loop), {reps} passes in {dt:.1f} s"}
 
 
+def expert_kernel(spec, mxfp4: bool) -> str:
+    """Which kernel family runs the expert GEMMs of this layer: the library takes
+    the matrix-vector kernel for decode-sized bf16 batches (at most 32 tokens,
+    N * topk <= 3 E, or <= 1.5 E with MXFP4 weights; K <= 4096) and the MFMA
+    tiles otherwise.  Used for labels only."""
+    n, m, e = spec.n_tokens, spec.n_tokens * spec.topk, spec.n_local or spec.n_experts
+    fits = spec.dtype == "bf16" and n <= 32 and max(spec.hidden, spec.inter) <= 4096 and \
+        (2 * m <= 3 * e if mxfp4 else m <= 3 * e)
+    return "grouped_gemv" if fits else "grouped_gemm"
+
+
 def stored_traffic(workload_name: str, stage: str):
     """HBM bytes per launch of a stage's kernel from the committed rocprofv3
     counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter
@@ -570,7 +581,8 @@ def main():
         # at 17/32 byte a weight
         f, b, et = algorithmic_mxfp4(spec, col_sum)
         roof = roofline(spec, f, b, stage_ms["experts"])
-        roof.update({"kernel": "grouped_gemm w13 + w2 (MXFP4 weights, one experts call)",
+        roof.update({"kernel": f"{expert_kernel(spec, True)} w13 + w2 (MXFP4 weights, one "
+                               "experts call)",
                      "traffic": None, "algorithmic_bytes": b, "algorithmic_flops": f,
                      "avg_launch_us": round(stage_ms["experts"] * 1e3, 2)})
     else:
@@ -581,7 +593,7 @@ def main():
         dom = "w13"
         f, b = work[dom]
         roof = roofline(spec, f, b, stage_ms[dom])
-        roof.update({"kernel": "grouped_gemm (w13 + activation)",
+        roof.update({"kernel": f"{expert_kernel(spec, False)} (w13 + activation)",
                      "traffic": stored_traffic(spec.name, dom),
                      "algorithmic_bytes": b, "algorithmic_flops": f,
                      "avg_launch_us": round(stage_ms[dom] * 1e3, 2)})

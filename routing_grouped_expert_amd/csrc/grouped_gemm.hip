@@ -158,7 +158,7 @@ __device__ __forceinline__ TileInfo tile_info(int L, const int *s_ts, const int 
 // The epilogue then writes 8-byte (bf16) or 16-byte (fp32) pieces of a row,
 // and needs one output-row index and one routing weight per lane.
 //
-// WQ (MXFP4 weights, one-phase tiles, bf16 activations): a stage holds the A
+// WQ (MXFP4 weights, bf16 activations): a stage holds the A
 // rows, each weight row's E2M1 codes for the slice (RB / 4 bytes: the same K
 // range) and the slice's E8M0 scales, tile rows in weight-row order per K-block
 // (4-byte loads: the rows of a tile are one or, packed and gated, two
@@ -192,9 +192,9 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
   constexpr int NST = TM * TN * 4;         // stores per wave per epilogue
   constexpr bool META = EPI == EPI_Y || EPI == EPI_OUT;
   constexpr bool PP = NW == 8;             // ping-pong schedule
-  static_assert(!WQ || (!PP && std::is_same<T, bf16_t>::value && QCPR >= 1 &&
+  static_assert(!WQ || (std::is_same<T, bf16_t>::value && QCPR >= 1 && JBQ >= 1 &&
                         JBQ * QRPI * NW == NB && SBK * NB <= SCL && NB % 4 == 0),
-                "MXFP4 weights: one-phase bf16 tiles");
+                "MXFP4 weights: bf16 tiles whose code rows fill whole wave loads");
   // a tile's metadata is written when its first slice is issued (S - 1
   // slices ahead) and read by its epilogue; NSL slots keep the epilogue of
   // tile i clear of the set-up of tile i + NSL
@@ -418,6 +418,20 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
     const int byte = (ks * Mm::KS + (lane >> 5) * Mm::EPL) * (int)sizeof(T);
     return swz<RB>(row, byte >> 4) + (byte & 15);
   };
+  // B fragment of k-step ks, tile row r: 8 bf16 weights, or (WQ) 8 codes (K
+  // elements 16 ks + 8 (lane / 32) ..) times their block's scale
+  auto bfrag = [&](const char *lb, int ks, int r) -> Frag {
+    if constexpr (WQ) {
+      const int qoff = ks * 8 + (lane >> 5) * 4;
+      const uint32_t word =
+          *reinterpret_cast<const uint32_t *>(lb + swz<QRB>(r, qoff >> 4) + (qoff & 15));
+      const int sidx = (NSETS == 2 && g.interleaved) ? 2 * (r % BN) + r / BN : r;
+      const uint32_t sb = reinterpret_cast<const uint8_t *>(lb + BQ)[(ks / 2) * NB + sidx];
+      return fp4x8_to_bf16(word, __uint_as_float(sb << 23));
+    } else {
+      return Mm::ld(lb + frag_addr(ks, r));
+    }
+  };
   auto zero_acc = [&]() {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -494,8 +508,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
         for (int j = 0; j < TN; ++j)
 #pragma unroll
           for (int s = 0; s < NSETS; ++s)
-            fb[ks][j][s] =
-                Mm::ld(lb + frag_addr(ks, s * BN + wn * (BN / WN) + j * 32 + (lane & 31)));
+            fb[ks][j][s] = bfrag(lb, ks, s * BN + wn * (BN / WN) + j * 32 + (lane & 31));
       }
       if (grp && z + 1 < nz) wait_slice(z + 1);
       barrier();
@@ -536,21 +549,8 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int s = 0; s < NSETS; ++s) {
-            const int r = s * BN + wn * (BN / WN) + j * 32 + (lane & 31);
-            if constexpr (WQ) {
-              // 8 codes (K elements 16 ks + 8 (lane / 32) ..) and their block's scale
-              const int qoff = ks * 8 + (lane >> 5) * 4;
-              const uint32_t word =
-                  *reinterpret_cast<const uint32_t *>(lb + swz<QRB>(r, qoff >> 4) + (qoff & 15));
-              const int sidx = (NSETS == 2 && g.interleaved) ? 2 * (r % BN) + r / BN : r;
-              const uint32_t sb = reinterpret_cast<const uint8_t *>(lb + BQ)[(ks / 2) * NB + sidx];
-              const float sc = __uint_as_float(sb << 23);
-              fb[buf][j][s] = fp4x8_to_bf16(word, sc);
-            } else {
-              fb[buf][j][s] = Mm::ld(lb + frag_addr(ks, r));
-            }
-          }
+          for (int s = 0; s < NSETS; ++s)
+            fb[buf][j][s] = bfrag(lb, ks, s * BN + wn * (BN / WN) + j * 32 + (lane & 31));
       };
       load_frags(0, 0);
 #pragma unroll
@@ -600,6 +600,10 @@ using PlainT = Cfg<32, 32, 1, 1, 2, 256>;   // 1 wave, 32 x 32
 // MXFP4 weights: the same tile shapes; deeper rings (4/6 and 6/8 stages) were
 // measured slower (LDS per workgroup costs occupancy) on the gpt-oss-sized
 // layer at 1, 33 and 512 tokens
+// prefill-sized batches: the 8-wave ping-pong tiles (the plain one 256
+// columns wide, so its code rows fill whole 1 KB wave loads)
+using GatedMQ = Cfg<128, 128, 2, 4, 3, 128>;
+using PlainMQ = Cfg<128, 256, 2, 4, 3, 128>;
 using GatedSQ = Cfg<32, 128, 1, 4, 4, 128>;
 using PlainSQ = Cfg<32, 128, 1, 4, 4, 128>;
 using GatedTQ = Cfg<32, 32, 1, 1, 2, 256>;
@@ -653,15 +657,22 @@ inline double launch_cost(int64_t tiles, int64_t cus, int BM, int BN, double sur
 // 128-row tiles, so it takes the 256-row tile; above that, whichever tile the
 // cost model favours (the 128-row tile wins where 256-row tiles would leave a
 // second, mostly empty round, e.g. at 256 rows per expert).
-// MXFP4 weights run on the one-phase tiles only (the 32-row and one-wave
-// tiles, which is what weight-streaming batches take anyway).
+// MXFP4 weights take the same thresholds with their own tiles: the 32-row
+// and one-wave tiles for weight-streaming batches, the 128-row ping-pong tiles
+// above (no 256-row tile: its 64-byte row slices hold 16 code bytes a row,
+// too few to fill the wave loads).
 template <typename T, int NSETS, int EPI>
 hipError_t launch_wq(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
+  using Md = typename std::conditional<NSETS == 2, GatedMQ, PlainMQ>::type;
   using Sm = typename std::conditional<NSETS == 2, GatedSQ, PlainSQ>::type;
   using Tn = typename std::conditional<NSETS == 2, GatedTQ, PlainTQ>::type;
-  if (expected_tiles(M, E, a.Nout, Sm::BM, Sm::BN) < device_cus())
-    return launch_cfg<T, NSETS, EPI, Tn, true>(a, M, E, s);
-  return launch_cfg<T, NSETS, EPI, Sm, true>(a, M, E, s);
+  const int64_t cus = device_cus();
+  if (M < 48 * (int64_t)E || expected_tiles(M, E, a.Nout, Md::BM, Md::BN) < cus / 2) {
+    if (expected_tiles(M, E, a.Nout, Sm::BM, Sm::BN) < cus)
+      return launch_cfg<T, NSETS, EPI, Tn, true>(a, M, E, s);
+    return launch_cfg<T, NSETS, EPI, Sm, true>(a, M, E, s);
+  }
+  return launch_cfg<T, NSETS, EPI, Md, true>(a, M, E, s);
 }
 
 template <typename T, int NSETS, int EPI>

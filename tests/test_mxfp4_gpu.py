@@ -79,6 +79,11 @@ MX = [
     ("n3-silu-interleaved", 3, 160, 96, 8, 3, "silu", "interleaved", {}),
     ("n8-relu2-top1", 8, 96, 160, 8, 1, "relu2", "packed", {}),
     ("n24-skew-k4096", 24, 4096, 128, 32, 1, "silu", "packed", {"zipf_s": 6.0}),
+    # prefill-sized: the 128-row ping-pong tiles for both GEMMs
+    ("mq-oai-interleaved", 2500, 1024, 512, 4, 2, "swiglu_oai", "interleaved",
+     {"alpha": 1.702, "beta": 1.0, "limit": 7.0}),
+    ("mq-silu-packed-ktail", 2600, 1024, 416, 4, 2, "silu", "packed", {}),
+    ("mq-relu2-top1", 5000, 1024, 512, 4, 1, "relu2", "packed", {}),
 ]
 
 
@@ -120,7 +125,7 @@ def test_mxfp4_layer(case):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("n", [1, 33, 512])
+@pytest.mark.parametrize("n", [1, 33, 512, 4096])
 def test_mxfp4_gptoss(n):
     spec = layer_spec("gptoss", n_tokens=n, name=f"gptoss_n{n}_mxfp4")
     print(f"[mxfp4] {spec}", flush=True)
