@@ -652,11 +652,14 @@ inline double launch_cost(int64_t tiles, int64_t cus, int BM, int BN, double sur
 // waste), and so do launches too small to give half the CUs a 128-row tile;
 // when even the 32 x 128 tiles number fewer than the CUs, the 32 x 32
 // one-wave tile spreads the weight stream over more CUs.
-// Up to one 256-row tile per expert on average, the layer streams each
-// expert's weights about once with 256-row tiles and about 1.5 times with
-// 128-row tiles, so it takes the 256-row tile; above that, whichever tile the
-// cost model favours (the 128-row tile wins where 256-row tiles would leave a
-// second, mostly empty round, e.g. at 256 rows per expert).
+// Plain (w2) layers with up to one 256-row tile per expert on average stream
+// each expert's weights about once with 256-row tiles and about 1.5 times with
+// 128-row tiles, so they take the 256-row tile -- when those tiles still cover
+// the CUs (gpt-oss-sized w2 at 128 rows per expert).  Everything else takes
+// whichever tile the cost model favours: the gated 256 x 128 tile at 64-128
+// rows per expert is half empty and measured 6-14 % slower than the 128-row
+// tile (gpt-oss-sized layer, 2048 and 4096 tokens), and 64 plain 256-row tiles
+// leave most CUs idle (minimind-sized w2 at E = 32: 22 % slower).
 // MXFP4 weights take the same thresholds with their own tiles: the 32-row
 // and one-wave tiles for weight-streaming batches, the 128-row ping-pong tiles
 // above (no 256-row tile: its 64-byte row slices hold 16 code bytes a row,
@@ -691,7 +694,8 @@ hipError_t launch_t(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
       return launch_cfg<T, NSETS, EPI, Tn>(a, M, E, s);
     return launch_cfg<T, NSETS, EPI, Sm>(a, M, E, s);
   }
-  if (M < (int64_t)L::BM * E) return launch_cfg<T, NSETS, EPI, L>(a, M, E, s);
+  if (NSETS == 1 && M < (int64_t)L::BM * E && expected_tiles(M, E, a.Nout, L::BM, L::BN) >= cus)
+    return launch_cfg<T, NSETS, EPI, L>(a, M, E, s);
   const double cl = launch_cost(expected_tiles(M, E, a.Nout, L::BM, L::BN), cus, L::BM, L::BN, 0.0);
   const double cm = launch_cost(tm, cus, Md::BM, Md::BN, 0.15);
   if (cl <= cm) return launch_cfg<T, NSETS, EPI, L>(a, M, E, s);
