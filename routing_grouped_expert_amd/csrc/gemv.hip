@@ -121,12 +121,7 @@ __global__ __launch_bounds__(64 * kGemvWaves) void grouped_gemv(GemmArgs g, int 
       c[q] = lane * 4 + q < E ? o[q + 1] - o[q] : 0;
       n += c[q] > 0;
     }
-    int incl = n;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int v = __shfl_up(incl, d);
-      if (lane >= d) incl += v;
-    }
+    const int incl = wave_inclusive_sum(n);
     const int want = (int)blockIdx.y;
     int before = incl - n;
 #pragma unroll

@@ -231,12 +231,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
       v[q] = (e < E) ? (o1 - o0 + BM - 1) / BM : 0;
       s += v[q];
     }
-    int incl = s;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
-    }
+    const int incl = wave_inclusive_sum(s);
     int run = incl - s;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {

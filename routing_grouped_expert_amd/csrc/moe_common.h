@@ -35,6 +35,21 @@ template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float f) { return
 
 __device__ __forceinline__ int popc64(unsigned long long x) { return __popcll(x); }
 
+// Inclusive prefix sum over the 64 lanes of a wave, all in DPP (no LDS round
+// trips): shifts by 1, 2, 4 and 8 inside each 16-lane row (lanes shifted in
+// from outside the row add 0), then the last lane of rows 0 and 2 is added to
+// rows 1 and 3 (row_bcast:15) and the last lane of row 1 to rows 2 and 3
+// (row_bcast:31).  Needs every lane of the wave active.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
 }  // namespace moe
 
 // Host-side launchers (one per kernel family).  Each returns hipSuccess or the

@@ -158,12 +158,7 @@ __device__ void block_exclusive_scan(const int *in, int *out, int E) {
       v[q] = (e < E) ? in[e] : 0;
       s += v[q];
     }
-    int incl = s;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
-    }
+    const int incl = wave_inclusive_sum(s);
     int run = incl - s;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
