@@ -27,6 +27,7 @@ struct GemmArgs {
   // MXFP4 weights: W holds E2M1 codes [E, NSETS * Nout, K / 2] and wscale the
   // E8M0 scales [E, K / 32, NSETS * Nout] (nullptr: W is in the A dtype)
   const uint8_t *wscale;
+  const int32_t *row_sorted;     // [N * topk] (w2 with the combine folded in)
 };
 
 // 8 E2M1 codes (element i in nibble i of `word`) times the scale `sc`, as the

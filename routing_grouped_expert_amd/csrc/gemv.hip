@@ -322,6 +322,186 @@ __global__ __launch_bounds__(64 * kGemvWaves) void grouped_gemv(GemmArgs g, int 
   }
 }
 
+// GEMM2 with the combine folded in, for decode-sized layers with topk > 1:
+// workgroup (blockIdx.x, t) computes output columns [blockIdx.x * 4 * CPW,
+// + 4 * CPW) of token t.  Wave w streams, for each of the token's slots j, the
+// CPW weight rows of its columns from the slot's expert (slots in batches of
+// SB, all rows of a batch in flight at once), takes the dot products with the
+// slot's activation row (staged in LDS), and the lane sums of all SB * CPW
+// (slot, column) values go through one halving reduction.  Its addition tree
+// is the same for every value, so each y = RNE(gate_scal * sum) has the bits
+// the w2 kernel would store in y_sorted; the y of one column are then added
+// in slot order in fp32 and rounded once, as the combine kernel does.
+template <bool WQ, int T>
+__global__ __launch_bounds__(64 * kGemvWaves) void gemv_w2_combine(GemmArgs g) {
+  constexpr int NW = kGemvWaves;
+  constexpr int CPW = WQ ? 2 : 1;  // output columns a wave
+  constexpr int SB = 4;            // slots a batch
+  constexpr int CW = WQ ? 1 : 4;   // dwords per lane per 8-element piece
+  constexpr int V = SB * CPW;      // values a lane reduces per batch
+  extern __shared__ __attribute__((aligned(16))) char s_a[];  // SB activation rows
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ int s_p[kMaxTopk], s_e[kMaxTopk];
+  __shared__ float s_gs[kMaxTopk];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int E = g.E, K = g.K, Nout = g.Nout, k = g.topk;
+  const int t = (int)blockIdx.y;
+
+  // ---- the token's slots: sorted row, expert (from offsets), routing weight
+  for (int i = tid; i <= E; i += 64 * NW) s_off[i] = g.offsets[i];
+  if (tid < k) {
+    const int p = g.row_sorted[(size_t)t * k + tid];
+    s_p[tid] = p;
+    s_gs[tid] = p < 0 ? 0.f
+                : !g.gate_scal ? 1.f
+                : g.gate_bf16 ? to_f32(reinterpret_cast<const bf16_t *>(g.gate_scal)[p])
+                              : reinterpret_cast<const float *>(g.gate_scal)[p];
+  }
+  __syncthreads();
+  if (tid < k) {
+    const int p = s_p[tid];
+    int e = -1;
+    if (p >= 0) {  // the expert whose segment holds p: last e with offsets[e] <= p
+      int lo = 0, hi = E - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_off[mid] <= p) lo = mid; else hi = mid - 1;
+      }
+      e = lo;
+    }
+    s_e[tid] = e;
+  }
+  __syncthreads();
+
+  const int col0 = ((int)blockIdx.x * NW + wave) * CPW;
+  const int nch = K / 8;
+  const int rowb = WQ ? K / 2 : 2 * K;
+  const uint32_t wbytes = (uint32_t)Nout * (uint32_t)rowb;
+  const uint32_t sbytes = (uint32_t)(K / 32) * (uint32_t)Nout;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void *>(g.A), (short)0, (int)g.a_bytes, kRsrcWord3);
+  const int arow_b = 2 * K;
+  const int nj = (SB * nch + 64 * NW - 1) / (64 * NW);  // DMA instructions a wave per batch
+  // lane holding value v after the halving reduction: one lane bit per step
+  auto value_lane = [](int v) {
+    int l = 0, m = 32;
+    for (int n = V; n > 1; n /= 2, m >>= 1)
+      if (v & (n / 2)) { l += m; v -= n / 2; }
+    return l;
+  };
+  float out_acc[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) out_acc[c] = 0.f;
+
+  for (int j0 = 0; j0 < k; j0 += SB) {
+    if (j0 > 0) __syncthreads();  // every wave is done with the previous batch's rows
+    // weights of the batch's slots, all in flight
+    uint32_t w[SB][CPW][T][CW];
+    uint32_t sc[WQ ? SB : 1][T];
+#pragma unroll
+    for (int jj = 0; jj < SB; ++jj) {
+      const int e = j0 + jj < k ? __builtin_amdgcn_readfirstlane(s_e[j0 + jj]) : -1;
+      const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char *>(reinterpret_cast<const char *>(g.W)) + (size_t)(e < 0 ? 0 : e) * wbytes,
+          (short)0, (int)wbytes, kRsrcWord3);
+#pragma unroll
+      for (int c = 0; c < CPW; ++c)
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+          const int ch = lane + 64 * tt;
+          const uint32_t off = (e >= 0 && col0 + c < Nout && ch < nch)
+                                   ? (uint32_t)(col0 + c) * (uint32_t)rowb + (uint32_t)ch * (4 * CW)
+                                   : kOOB;
+          if constexpr (WQ) {
+            w[jj][c][tt][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rw, (int)off, 0, 0);
+          } else {
+            const u32x4_t v = __builtin_bit_cast(
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, 0));
+#pragma unroll
+            for (int d = 0; d < 4; ++d) w[jj][c][tt][d] = v[d];
+          }
+        }
+      if constexpr (WQ) {
+        // the scale bytes of the wave's two columns at K-block (lane + 64 tt) / 4
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t *>(g.wscale) + (size_t)(e < 0 ? 0 : e) * sbytes, (short)0,
+            (int)sbytes, kRsrcWord3);
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+          const int kb = (lane + 64 * tt) >> 2;
+          const uint32_t off = (e >= 0 && col0 < Nout && kb < K / 32)
+                                   ? (uint32_t)kb * (uint32_t)Nout + (uint32_t)col0
+                                   : kOOB;
+          sc[jj][tt] = (uint32_t)(uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rs, (int)off, 0, 0);
+        }
+      }
+    }
+    // the batch's activation rows (DMA behind the weight loads)
+    for (int j = 0; j < nj; ++j) {
+      const int q = (j * NW + wave) * 64 + lane;
+      const int r = q / nch, ch = q - r * nch;
+      const int p = r < SB && j0 + r < k ? s_p[j0 + r] : -1;
+      const uint32_t off = p >= 0 ? (uint32_t)p * (uint32_t)arow_b + (uint32_t)ch * 16 : kOOB;
+      dma16(ra, s_a + (j * NW + wave) * 1024, off);
+    }
+    wait_vm<0>();
+    barrier();
+    float acc[V];  // value index jj * CPW + c
+#pragma unroll
+    for (int jj = 0; jj < SB; ++jj) {
+      u32x4_t a[T];
+#pragma unroll
+      for (int tt = 0; tt < T; ++tt) {
+        a[tt] = *reinterpret_cast<const u32x4_t *>(s_a + jj * arow_b + (lane + 64 * tt) * 16);
+        if (lane + 64 * tt >= nch) a[tt] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int c = 0; c < CPW; ++c) {
+        float sum = 0.f;
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) {
+          uint32_t wv[4];
+          if constexpr (WQ) {
+            const float scl = __uint_as_float(((sc[jj][tt] >> (8 * c)) & 0xffu) << 23);
+            const u32x4_t d = __builtin_bit_cast(u32x4_t, fp4x8_to_bf16(w[jj][c][tt][0], scl));
+#pragma unroll
+            for (int q = 0; q < 4; ++q) wv[q] = d[q];
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) wv[q] = w[jj][c][tt][q];
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sum = dot2(wv[q], a[tt][q], sum);
+        }
+        acc[jj * CPW + c] = sum;
+      }
+    }
+    wave_sum<V, 1>(acc, lane);
+    // y of each (slot, column), added in slot order
+#pragma unroll
+    for (int jj = 0; jj < SB; ++jj) {
+      const int j = j0 + jj;
+      if (j < k && s_p[j] >= 0) {
+        const float gs = s_gs[j];
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+          const float y = __int_as_float(
+              __builtin_amdgcn_readlane(__float_as_int(acc[0]), value_lane(jj * CPW + c)));
+          out_acc[c] += to_f32(bf16_rne(y * gs));
+        }
+      }
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+      if (col0 + c < Nout)
+        reinterpret_cast<bf16_t *>(g.C)[(size_t)t * Nout + col0 + c] = bf16_rne(out_acc[c]);
+  }
+}
+
 template <int NSETS, int EPI, bool WQ>
 hipError_t launch_sets(const GemmArgs &a, int64_t M, int cb, hipStream_t s) {
   constexpr int RC = rows_per_wave<WQ>() / NSETS;
@@ -358,6 +538,44 @@ bool gemv_fits(moe_dtype_t dt, int64_t n_tokens, int topk, int n_experts, int K,
     return false;
   const int64_t m = n_tokens * topk;
   return mxfp4 ? 2 * m <= 3 * (int64_t)n_experts : m <= 3 * (int64_t)n_experts;
+}
+
+bool gemm2_combine_fits(moe_dtype_t dt, int64_t n_tokens, int topk, int n_experts, int hidden,
+                        int inter, bool mxfp4) {
+  // about one row per expert (each token reads its slots' weight rows itself);
+  // bf16 weights only: with MXFP4 weights the fused kernel measured no faster
+  // than the matrix-vector w2 plus the combine (one token, gpt-oss-sized layer)
+  return !mxfp4 && topk > 1 && n_tokens * topk <= n_experts && hidden % 2 == 0 &&
+         gemv_fits(dt, n_tokens, topk, n_experts, inter, hidden, mxfp4);
+}
+
+hipError_t launch_gemm2_combine(const void *act_in, const void *w2, void *out,
+                                const int32_t *offsets, const int32_t *row_sorted,
+                                const void *gate_scal, moe_dtype_t gate_dt, int64_t n_tokens,
+                                int topk, int n_experts, int hidden, int inter, hipStream_t s,
+                                const uint8_t *w2_scale) {
+  if (n_tokens <= 0) return hipSuccess;
+  const int64_t M = n_tokens * topk;
+  GemmArgs a{act_in, w2, out, offsets, nullptr, gate_scal, (uint32_t)(M * inter * 2),
+             (uint32_t)(n_tokens * hidden * 2), gate_dt == MOE_BF16, n_experts, inter, hidden,
+             topk, 0, 0, 0, ActParams{1.f, 0.f, 0.f}, w2_scale, row_sorted};
+  const bool wq = w2_scale != nullptr;
+  const int cpw = wq ? 2 : 1;
+  const unsigned gx = (unsigned)((hidden + cpw * kGemvWaves - 1) / (cpw * kGemvWaves));
+  const int nj = (4 * (inter / 8) + 64 * kGemvWaves - 1) / (64 * kGemvWaves);
+  const size_t lds = (size_t)(nj + 1) * kGemvWaves * 1024;  // + slack, as in grouped_gemv
+  const dim3 grid(gx, (unsigned)n_tokens), block(64 * kGemvWaves);
+  const int t = (inter + 511) / 512;
+  if (wq) {
+    if (t <= 4) hipLaunchKernelGGL((gemv_w2_combine<true, 4>), grid, block, lds, s, a);
+    else if (t <= 6) hipLaunchKernelGGL((gemv_w2_combine<true, 6>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((gemv_w2_combine<true, 8>), grid, block, lds, s, a);
+  } else {
+    if (t <= 4) hipLaunchKernelGGL((gemv_w2_combine<false, 4>), grid, block, lds, s, a);
+    else if (t <= 6) hipLaunchKernelGGL((gemv_w2_combine<false, 6>), grid, block, lds, s, a);
+    else hipLaunchKernelGGL((gemv_w2_combine<false, 8>), grid, block, lds, s, a);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_gemv(const GemmArgs &a, int nsets, int epi, int64_t n_tokens, int64_t M,

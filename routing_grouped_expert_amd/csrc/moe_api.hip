@@ -181,6 +181,11 @@ hipError_t run_w2(const void *a, moe_dtype_t dtype, int64_t n, int32_t hidden, c
                   hipStream_t s, bool share = false, bool unit_gate = false,
                   const void *w2_scale = nullptr) {
   const bool direct = k == 1;  // one row per token: GEMM2 writes the output rows itself
+  if (!direct && moe::gemm2_combine_fits(dtype, n, k, e, hidden, inter, w2_scale != nullptr))
+    return moe::launch_gemm2_combine(a, w2, out, r->offsets, r->row_sorted,
+                                     unit_gate ? nullptr : r->gate_scal, (moe_dtype_t)r->w_dtype,
+                                     n, k, e, hidden, inter, s,
+                                     reinterpret_cast<const uint8_t *>(w2_scale));
   hipError_t err = moe::launch_gemm2(a, w2, direct ? out : y, r->offsets, r->col_sorted,
                                      unit_gate ? nullptr : r->gate_scal,
                                      (moe_dtype_t)r->w_dtype, dtype, n, k, e, hidden, inter,

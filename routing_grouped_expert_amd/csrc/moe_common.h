@@ -90,6 +90,18 @@ hipError_t launch_gemm2(const void *act_in, const void *w2, void *y, const int32
                         moe_dtype_t dt, int64_t n_tokens, int topk, int n_experts, int hidden,
                         int inter, bool direct_out, hipStream_t s,
                         const uint8_t *w2_scale = nullptr);
+// Decode-sized layers with topk > 1 and about one row per expert: GEMM2 and
+// the combine in one kernel (true when launch_gemm2_combine takes the shape).
+bool gemm2_combine_fits(moe_dtype_t dt, int64_t n_tokens, int topk, int n_experts, int hidden,
+                        int inter, bool mxfp4);
+// out[t] = RNE(sum_j RNE(gate_scal[p] * (a[p] . W2[e(p)]^T))), p = row_sorted[t*topk + j]
+// in slot order (slots with p = -1 skipped): the same bits as launch_gemm2 into
+// y_sorted followed by launch_combine.
+hipError_t launch_gemm2_combine(const void *act_in, const void *w2, void *out,
+                                const int32_t *offsets, const int32_t *row_sorted,
+                                const void *gate_scal, moe_dtype_t gate_dt, int64_t n_tokens,
+                                int topk, int n_experts, int hidden, int inter, hipStream_t s,
+                                const uint8_t *w2_scale = nullptr);
 // out[t] = sum_j y_sorted[row_sorted[t*topk + j]] (fp32, slot order), slots
 // with row_sorted = -1 skipped.
 hipError_t launch_combine(const void *y_sorted, const int32_t *row_sorted, void *out,

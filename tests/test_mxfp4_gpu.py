@@ -94,6 +94,9 @@ def _same_kernels(n, k, e):
     32-row MFMA tiles (n * k < 48 E, outside the matrix-vector range)."""
     m = n * k
     gv_mx, gv_16 = n <= 32 and 2 * m <= 3 * e, n <= 32 and m <= 3 * e
+    # (at k > 1 and m <= E the bf16 layer folds the combine into its w2 kernel
+    # and the MXFP4 layer does not: the fused kernel is built to give the same
+    # bits, which this comparison then checks)
     return (gv_mx and gv_16) or (not gv_mx and not gv_16 and m < 48 * e)
 
 
