@@ -178,20 +178,25 @@ def stored_traffic(workload_name: str, stage: str):
     """HBM bytes per launch of a stage's kernel from the committed rocprofv3
     counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter
     reads for a copy kernel of known size), or None when there is none or when
-    the kernel source has changed since the counters were taken."""
+    the kernel's source file has changed since the counters were taken."""
     import hashlib
     import re
     path = os.path.join(ROOT, "profiles", "gemm_counters.md")
-    src = os.path.join(ROOT, "routing_grouped_expert_amd", "csrc", "grouped_gemm.hip")
     try:
         text = open(path).read()
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
     except OSError:
         return None
-    for m in re.finditer(r"traffic: workload=(\S+) stage=(\S+) src_sha256=(\S+) "
+    for m in re.finditer(r"traffic: workload=(\S+) stage=(\S+) src=(\S+) src_sha256=(\S+) "
                          r"fetch_bytes=(\d+) write_bytes=(\d+)", text):
-        if m.group(1) == workload_name and m.group(2) == stage and m.group(3) == sha:
-            return int(m.group(4)) + int(m.group(5))
+        if m.group(1) != workload_name or m.group(2) != stage:
+            continue
+        src = os.path.join(ROOT, "routing_grouped_expert_amd", "csrc", m.group(3))
+        try:
+            sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        except OSError:
+            return None
+        if m.group(4) == sha:
+            return int(m.group(5)) + int(m.group(6))
     return None
 
 
