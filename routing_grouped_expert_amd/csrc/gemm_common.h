@@ -67,8 +67,9 @@ __device__ __forceinline__ float act_val(float g, float u, float nal, const ActP
 // few rows per expert on average -- N * topk <= 3 E with bf16 weights, <= 1.5 E
 // with MXFP4 weights, whose FP4 decode is repeated for every row.  Above
 // that the MFMA tiles are faster (measured on gpt-oss-sized layers, E = 32
-// and 128).  True when that kernel takes a launch of this shape.
-constexpr int kGemvMaxTokens = 32;
+// and 128, up to 96 tokens).  True when that kernel takes a launch of this
+// shape.
+constexpr int kGemvMaxTokens = 128;
 bool gemv_fits(moe_dtype_t dt, int64_t n_tokens, int topk, int n_experts, int K, int Nout,
                bool mxfp4);
 // nsets: weight sets per output column (2 gated, 1 plain); epi: the epilogue

@@ -89,11 +89,11 @@ MX = [
 
 def _same_kernels(n, k, e):
     """True when the MXFP4 and the bf16 layer take the same GEMM kernels (then
-    the results are the same bits): both the matrix-vector kernel (at most 32
+    the results are the same bits): both the matrix-vector kernel (at most 128
     tokens, n * k <= 1.5 E for MXFP4 and <= 3 E for bf16), or both the one-wave /
     32-row MFMA tiles (n * k < 48 E, outside the matrix-vector range)."""
     m = n * k
-    gv_mx, gv_16 = n <= 32 and 2 * m <= 3 * e, n <= 32 and m <= 3 * e
+    gv_mx, gv_16 = n <= 128 and 2 * m <= 3 * e, n <= 128 and m <= 3 * e
     # (at k > 1 and m <= E the bf16 layer folds the combine into its w2 kernel
     # and the MXFP4 layer does not: the fused kernel is built to give the same
     # bits, which this comparison then checks)
