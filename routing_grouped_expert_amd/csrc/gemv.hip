@@ -17,7 +17,8 @@
 //    else: lane l holds the K elements 8 (l + 64 t) .. + 7 of every row, t < T.
 //    That is ~23 KB a wave in flight at K = 2880 with bf16 weights (4 rows,
 //    16-byte loads) and ~12 KB with MXFP4 weights (8 rows of E2M1 codes,
-//    4-byte loads), so a few waves a CU cover HBM latency.
+//    4-byte loads), so a few waves a CU cover HBM latency.  The weight loads
+//    are non-temporal: each weight is read once.
 //  * The A rows of the expert (the gathered token rows, or the sorted
 //    activation rows) are staged in LDS, cb at a time; each lane reads the
 //    16-byte pieces matching its weight pieces.  Products accumulate in fp32
@@ -39,6 +40,11 @@ namespace moe {
 namespace {
 
 constexpr int kGemvWaves = 4;
+// Cache policy of the weight loads: non-temporal (nt).  Every weight is read
+// once a layer, so keeping it out of the caches' retention leaves them to the
+// activation rows and routing data: measured 10-11 % faster at 8-33 tokens of
+// a gpt-oss-sized layer and 6 % on a 24-layer decode stack (cold weights).
+constexpr int kWeightCpol = 2;
 // weight rows a wave streams.  FP4 rows are a quarter of the bytes, but 16
 // of them a wave (as many bytes in flight as 4 bf16 rows) measured 20 % slower
 // than 8 at one token: the per-row decode and dot products, not the loads,
@@ -181,10 +187,10 @@ __global__ __launch_bounds__(64 * kGemvWaves) void grouped_gemv(GemmArgs g, int 
         const int ch = lane + 64 * t;
         const uint32_t off = (col_ok && ch < nch) ? rbase + (uint32_t)ch * (4 * CW) : kOOB;
         if constexpr (WQ) {
-          w[i][s][t][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rw, (int)off, 0, 0);
+          w[i][s][t][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rw, (int)off, 0, kWeightCpol);
         } else {
           const u32x4_t v =
-              __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, 0));
+              __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, kWeightCpol));
 #pragma unroll
           for (int d = 0; d < 4; ++d) w[i][s][t][d] = v[d];
         }
@@ -415,10 +421,10 @@ __global__ __launch_bounds__(64 * kGemvWaves) void gemv_w2_combine(GemmArgs g) {
                                    ? (uint32_t)(col0 + c) * (uint32_t)rowb + (uint32_t)ch * (4 * CW)
                                    : kOOB;
           if constexpr (WQ) {
-            w[jj][c][tt][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rw, (int)off, 0, 0);
+            w[jj][c][tt][0] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(rw, (int)off, 0, kWeightCpol);
           } else {
             const u32x4_t v = __builtin_bit_cast(
-                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, 0));
+                u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rw, (int)off, 0, kWeightCpol));
 #pragma unroll
             for (int d = 0; d < 4; ++d) w[jj][c][tt][d] = v[d];
           }

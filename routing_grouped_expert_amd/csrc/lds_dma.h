@@ -63,6 +63,17 @@ static __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char *lds
       : "memory", "m0");
 }
 
+// dma16 with the non-temporal cache policy, for operands streamed once.
+static __device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t r, char *lds, uint32_t voff) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(void __attribute__((address_space(3))) *)lds;
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen nt lds"
+      :
+      : "v"(voff), "s"(r), "s"(__builtin_amdgcn_readfirstlane(m0))
+      : "memory", "m0");
+}
+
 // 4 bytes per lane from buffer `r` at byte offset `voff` into LDS at
 // lds + 4 * lane (same rules as dma16).
 static __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, char *lds, uint32_t voff) {
