@@ -893,21 +893,32 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
     return hipGetLastError();
   }
   if (x) {  // router GEMM as a kernel of its own, then the routing kernels
-    // 32-token tiles spread a moderate batch over more compute units; 128-token
-    // tiles read the gate weight a quarter as often
-    const bool small = N <= 4096;
-    const unsigned g = (unsigned)((N + (small ? 31 : 127)) / (small ? 32 : 128));
+    // The largest tile (32, 64 or 128 tokens) that still gives every compute
+    // unit a workgroup: larger tiles read the gate weight less often, but a
+    // launch with fewer workgroups than CUs leaves the x stream short of
+    // loads in flight (128-token tiles at 8192 tokens: 63 us; 32-token: ~51)
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    const int nt = N >= 128 * (int64_t)cus ? 128 : N >= 64 * (int64_t)cus ? 64 : 32;
+    const unsigned g = (unsigned)((N + nt - 1) / nt);
     auto gemm = [&](auto kern) {
       hipLaunchKernelGGL(kern, dim3(g), dim3(kGateThreads), 0, s, x, wg, N, H, E, lw);
     };
-    switch (gate_bucket(E) * (small ? 1 : -1)) {
-      case 32: gemm(gate_gemm<T, 32, 32>); break;
-      case 64: gemm(gate_gemm<T, 32, 64>); break;
-      case 128: gemm(gate_gemm<T, 32, 128>); break;
-      case 256: gemm(gate_gemm<T, 32, 256>); break;
-      case -32: gemm(gate_gemm<T, 128, 32>); break;
-      case -64: gemm(gate_gemm<T, 128, 64>); break;
-      case -128: gemm(gate_gemm<T, 128, 128>); break;
+    switch (gate_bucket(E) * 1000 + nt) {
+      case 32032: gemm(gate_gemm<T, 32, 32>); break;
+      case 64032: gemm(gate_gemm<T, 32, 64>); break;
+      case 128032: gemm(gate_gemm<T, 32, 128>); break;
+      case 256032: gemm(gate_gemm<T, 32, 256>); break;
+      case 32064: gemm(gate_gemm<T, 64, 32>); break;
+      case 64064: gemm(gate_gemm<T, 64, 64>); break;
+      case 128064: gemm(gate_gemm<T, 64, 128>); break;
+      case 256064: gemm(gate_gemm<T, 64, 256>); break;
+      case 32128: gemm(gate_gemm<T, 128, 32>); break;
+      case 64128: gemm(gate_gemm<T, 128, 64>); break;
+      case 128128: gemm(gate_gemm<T, 128, 128>); break;
       default: gemm(gate_gemm<T, 128, 256>); break;
     }
     const hipError_t err = hipGetLastError();

@@ -89,6 +89,14 @@ def test_gate_route_largest_batch():
     _gate_case(65536, 128, 2880, 4, "bf16", sample=512)
 
 
+# batches that take the 64-token tile (at least 64 tokens per compute unit, fewer
+# than 128) and the 32-token tile just below it
+@pytest.mark.parametrize("n,e,h,k,dt", [(20000, 64, 512, 8, "bf16"), (17000, 33, 264, 3, "f32"),
+                                        (16000, 128, 1024, 4, "bf16")])
+def test_gate_route_mid_batches(n, e, h, k, dt):
+    _gate_case(n, e, h, k, dt, sample=512)
+
+
 def test_gate_route_equals_route_on_its_logits():
     x, w = router_inputs(3000, 64, 256, "bf16", seed=3)
     lg, r1 = moe_gate_route(x.to(DEV), w.to(DEV), 4)
