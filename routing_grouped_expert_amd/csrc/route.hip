@@ -672,24 +672,24 @@ __global__ __launch_bounds__(THREADS) void route_fused(
   }
 }
 
-// Multi-block path, kernel 1: one chunk of kRouteTokens tokens per workgroup;
+// Multi-block path, kernel 1: one chunk of NTB tokens per workgroup (64 or 256);
 // per-block expert counts and per-entry in-block ranks to the workspace.
 constexpr int kTopkThreads = 1024;
 
-template <typename T, int C>
+template <typename T, int C, int NTB>
 __global__ __launch_bounds__(kTopkThreads) void route_topk_rank(
     const T *__restrict__ logits, int64_t N, int E, int K, int lo, int nl, int logG, int vec,
     int32_t *__restrict__ topk_idx, T *__restrict__ topk_w, uint32_t *__restrict__ bitmatrix,
     int32_t *__restrict__ blk_cnt, int nbp, uint8_t *__restrict__ blk_rank) {
-  __shared__ ChunkLds<T, kRouteTokens> L;
+  __shared__ ChunkLds<T, NTB> L;
   const int tid = threadIdx.x;
-  const int64_t tok0 = (int64_t)blockIdx.x * kRouteTokens;
+  const int64_t tok0 = (int64_t)blockIdx.x * NTB;
   topk_chunk<T, kTopkThreads, C>(logits, N, E, K, lo, nl, logG, vec, tok0, topk_idx, topk_w,
                                  bitmatrix, L);
   __syncthreads();
-  rank_chunk<kTopkThreads>(nl, (int)min<int64_t>(kRouteTokens, N - tok0), L);
+  rank_chunk<kTopkThreads>(nl, (int)min<int64_t>(NTB, N - tok0), L);
   const int64_t t = tok0 + tid;
-  if (tid < kRouteTokens && t < N) {
+  if (tid < NTB && t < N) {
 #pragma unroll
     for (int j = 0; j < kMaxTopk; ++j) {
       if (j < K) {
@@ -711,7 +711,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_rank(
 // in earlier blocks) + rank in the block.
 constexpr int kScatterThreads = 1024;
 
-template <typename T>
+template <typename T, int NTB>
 __global__ __launch_bounds__(kScatterThreads) void route_scatter(
     int64_t N, int K, int lo, int nl, int nblocks, int nbp, const int32_t *__restrict__ blk_cnt,
     const uint8_t *__restrict__ blk_rank, const int32_t *__restrict__ topk_idx,
@@ -726,10 +726,10 @@ __global__ __launch_bounds__(kScatterThreads) void route_scatter(
   __shared__ int s_all[kParts][kMaxExperts];
   const int tid = threadIdx.x;
   const int b = blockIdx.x;
-  // the block's entries: token t = b * 256 + tid, slots 0..K-1.  They do not
+  // the block's entries: token t = b * NTB + tid, slots 0..K-1.  They do not
   // depend on the counts, so their loads go out first and overlap the sums.
-  const int64_t t = (int64_t)b * kRouteTokens + tid;
-  const bool own = tid < kRouteTokens && t < N;
+  const int64_t t = (int64_t)b * NTB + tid;
+  const bool own = tid < NTB && t < N;
   int ex[kMaxTopk], rk[kMaxTopk];
   T w[kMaxTopk];
   if (own) {
@@ -806,10 +806,10 @@ __global__ __launch_bounds__(kScatterThreads) void route_scatter(
     }
   }
   // sorted positions past the local entries: this block clears its share of
-  // [m_local, N*K), the positions [b*256*K, (b+1)*256*K)
+  // [m_local, N*K), the positions [b*NTB*K, (b+1)*NTB*K)
   const int64_t M = N * K, m_local = s_off[E];
-  const int64_t p_end = min(M, ((int64_t)b + 1) * kRouteTokens * K);
-  for (int64_t p = max(m_local, (int64_t)b * kRouteTokens * K) + tid; p < p_end;
+  const int64_t p_end = min(M, ((int64_t)b + 1) * NTB * K);
+  for (int64_t p = max(m_local, (int64_t)b * NTB * K) + tid; p < p_end;
        p += kScatterThreads) {
     col_sorted[p] = -1;
     gate_scal[p] = from_f32<T>(0.f);
@@ -833,6 +833,11 @@ inline RoutePath route_path(int64_t N, int E, int K) {
   (void)K;
   return N <= kFusedTokens ? kPathFused : kPathBlocks;
 }
+// Tokens per block of the multi-block path.  A block's top-k runs on one CU,
+// so batches too small to fill the CUs with 256-token blocks take 64-token
+// blocks (one pass of 16 lanes a token at E = 128): 4x the workgroups.
+constexpr int64_t kSmallBlocksUpTo = 16384;
+inline int route_block_tokens(int64_t N) { return N <= kSmallBlocksUpTo ? 64 : kRouteTokens; }
 
 // With x != nullptr (router GEMM), `logits` is written from x and the gate
 // weight wg [E, H] before the top-k reads it.
@@ -843,7 +848,9 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
   constexpr int V = Logit<T>::kVec;
   // two chunks a lane when one would need more than 8 lanes a token, unless the
   // batch is so small that spreading it over more lanes matters more
-  const bool wide = (E + V - 1) / V > 8 && N > 64;
+  const RoutePath path = route_path(N, E, K);
+  const int ntb = route_block_tokens(N);
+  const bool wide = (E + V - 1) / V > 8 && N > 64 && !(path == kPathBlocks && ntb == 64);
   const int C = wide ? 2 : 1;
   const int need = (E + C * V - 1) / (C * V);
   int logG = 0;
@@ -851,7 +858,6 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
   const int vec = (E % V) == 0;
   T *tw = reinterpret_cast<T *>(r->topk_w);
   T *gs = reinterpret_cast<T *>(r->gate_scal);
-  const RoutePath path = route_path(N, E, K);
   T *lw = const_cast<T *>(logits);
   const int gate_np = x ? gate_parts(E, H * (int)sizeof(T)) : 0;
   if (x && N <= kGateFusedTokens && kGateSplitK && gate_np <= kGateMaxParts) {
@@ -939,21 +945,23 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
                          r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs);
     return hipGetLastError();
   }
-  const int64_t nb = (N + kRouteTokens - 1) / kRouteTokens;
+  const int64_t nb = (N + ntb - 1) / ntb;
   const int nbp = (int)((nb + 3) / 4 * 4);
   int32_t *blk_cnt = reinterpret_cast<int32_t *>(scratch);
   uint8_t *blk_rank = reinterpret_cast<uint8_t *>(scratch) + align256((size_t)nbp * E * 4);
-  if (wide)
-    hipLaunchKernelGGL((route_topk_rank<T, 2>), dim3((unsigned)nb), dim3(kTopkThreads), 0, s,
-                       logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw, r->bitmatrix, blk_cnt, nbp,
-                       blk_rank);
+  auto blocks = [&](auto topk_kern, auto scatter_kern) {
+    hipLaunchKernelGGL(topk_kern, dim3((unsigned)nb), dim3(kTopkThreads), 0, s, logits, N, E, K,
+                       lo, nl, logG, vec, r->topk_idx, tw, r->bitmatrix, blk_cnt, nbp, blk_rank);
+    hipLaunchKernelGGL(scatter_kern, dim3((unsigned)nb), dim3(kScatterThreads), 0, s, N, K, lo, nl,
+                       (int)nb, nbp, blk_cnt, blk_rank, r->topk_idx, tw, r->col_sum, r->offsets,
+                       r->col_sorted, r->row_sorted, gs);
+  };
+  if (ntb == 64)
+    blocks(route_topk_rank<T, 1, 64>, route_scatter<T, 64>);
+  else if (wide)
+    blocks(route_topk_rank<T, 2, kRouteTokens>, route_scatter<T, kRouteTokens>);
   else
-    hipLaunchKernelGGL((route_topk_rank<T, 1>), dim3((unsigned)nb), dim3(kTopkThreads), 0, s,
-                       logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw, r->bitmatrix, blk_cnt, nbp,
-                       blk_rank);
-  hipLaunchKernelGGL(route_scatter<T>, dim3((unsigned)nb), dim3(kScatterThreads), 0, s, N, K, lo,
-                     nl, (int)nb, nbp, blk_cnt, blk_rank, r->topk_idx, tw, r->col_sum, r->offsets,
-                     r->col_sorted, r->row_sorted, gs);
+    blocks(route_topk_rank<T, 1, kRouteTokens>, route_scatter<T, kRouteTokens>);
   return hipGetLastError();
 }
 
@@ -968,7 +976,8 @@ size_t gate_scratch_bytes(int64_t n_tokens, int n_experts, int hidden, moe_dtype
 
 size_t route_scratch_bytes(int64_t n_tokens, int n_experts, int topk) {
   if (route_path(n_tokens, n_experts, topk) != kPathBlocks) return 0;
-  const int64_t nb = (n_tokens + kRouteTokens - 1) / kRouteTokens;
+  const int ntb = route_block_tokens(n_tokens);
+  const int64_t nb = (n_tokens + ntb - 1) / ntb;
   const int64_t nbp = (nb + 3) / 4 * 4;
   return align256((size_t)nbp * n_experts * 4) + align256((size_t)n_tokens * topk);
 }

@@ -43,6 +43,8 @@ EDGE = [
     (4097, 8, 1, "bf16"),    # one token past it: multi-block
     (4096, 16, 1, "f32"),    # compact path, fp32 logits
     (2049, 3, 2, "bf16"),    # compact path, scalar loads, ragged 64-token groups
+    (12345, 256, 16, "bf16"),  # 64-token blocks: widest layer, ragged last block
+    (16385, 32, 4, "bf16"),  # first batch back on 256-token blocks, one-token tail
 ]
 
 
