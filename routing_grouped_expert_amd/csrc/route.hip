@@ -548,11 +548,47 @@ __device__ __forceinline__ void gate_logits(const T *__restrict__ x, const T *__
 // part[(t * E + e) * npad + z] (a logit's slices contiguous, npad a multiple of
 // 4); the routing kernel adds them up.  The gate weight is read by as many
 // compute units as it has slices instead of by one.
-constexpr int kGateMaxParts = 64;  // more K-slices than this: the one-workgroup GEMM
+constexpr int kGateMaxParts = 256;  // more K-slices than this: the one-workgroup GEMM
+// Split-K sums up to this many bytes are added up in the routing kernel's
+// prologue; more take a reduction kernel of their own first.
+constexpr int64_t kGateSumInlineBytes = 32 * 1024;
 template <typename T, int EPB>
 __global__ __launch_bounds__(256) void gate_partial(const T *__restrict__ x,
                                                     const T *__restrict__ wg, int64_t N, int H,
                                                     int E, float *__restrict__ part, int npad);
+
+// Logit i of the split-K router GEMM: its nparts K-slice sums added in slice
+// order from zero in fp32 (rounded by the caller).  The slices are contiguous;
+// the 16-byte loads of 32 of them are all issued before their additions (a
+// wider round costs more in cold instruction-cache misses than it saves).
+__device__ __forceinline__ float gate_slice_sum(const float *__restrict__ part, int64_t i,
+                                                int nparts) {
+  constexpr int Z = 32, Q = Z / 4;
+  const f32x4_t *q = reinterpret_cast<const f32x4_t *>(part + i * ((nparts + 3) & ~3));
+  float acc = 0.f;
+  for (int z0 = 0; z0 < nparts; z0 += Z) {
+    f32x4_t v[Q];
+#pragma unroll
+    for (int u = 0; u < Q; ++u)
+      v[u] = z0 + 4 * u < nparts ? q[z0 / 4 + u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int z = 0; z < Z; ++z)
+      if (z0 + z < nparts) acc += v[z / 4][z % 4];
+  }
+  return acc;
+}
+
+// The split-K sums of ne logits added up over many workgroups, one logit a
+// thread, when there are too many for the routing kernel's prologue (a single
+// workgroup) to read quickly.
+constexpr int kGateReduceThreads = 256;
+template <typename T>
+__global__ __launch_bounds__(kGateReduceThreads) void gate_reduce(const float *__restrict__ part,
+                                                                  int64_t ne, int nparts,
+                                                                  T *__restrict__ logits) {
+  const int64_t i = (int64_t)blockIdx.x * kGateReduceThreads + threadIdx.x;
+  if (i < ne) logits[i] = from_f32<T>(gate_slice_sum(part, i, nparts));
+}
 
 // Router GEMM alone: one workgroup of 256 threads per NT tokens, all experts.
 constexpr int kGateThreads = 256;
@@ -619,23 +655,9 @@ __global__ __launch_bounds__(THREADS) void route_fused(
   if constexpr (GATE == 1)  // N <= kGateFusedTokens
     gate_logits<T, kGateFusedTokens, THREADS, EPB, GS, GRB>(x, wg, N, H, E, 0, logits_out, s_raw);
   if constexpr (GATE == 2) {  // slices summed in order, rounded once
-    // a logit's nparts sums are contiguous (stride npad, a multiple of 4): up to
-    // 16 travel in four independent 16-byte loads
-    const int ne = (int)N * E, npad = (nparts + 3) & ~3;
-    for (int i = tid; i < ne; i += THREADS) {
-      const f32x4_t *q = reinterpret_cast<const f32x4_t *>(part + (size_t)i * npad);
-      float acc = 0.f;
-      for (int z0 = 0; z0 < nparts; z0 += 16) {
-        f32x4_t v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          v[u] = z0 + 4 * u < nparts ? q[z0 / 4 + u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-          if (z0 + u < nparts) acc += v[u / 4][u % 4];
-      }
-      logits_out[i] = from_f32<T>(acc);
-    }
+    const int ne = (int)N * E;
+    for (int i = tid; i < ne; i += THREADS)
+      logits_out[i] = from_f32<T>(gate_slice_sum(part, i, nparts));
     __syncthreads();
   }
   topk_chunk<T, THREADS, C>(logits, N, E, K, lo, nl, logG, vec, 0, topk_idx, topk_w, bitmatrix,
@@ -874,8 +896,20 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
       case 128: partial(gate_partial<T, 128>); break;
       default: partial(gate_partial<T, 256>); break;
     }
-    const hipError_t err = hipGetLastError();
+    hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    const int64_t ne = N * E;
+    if (ne * npad * 4 > kGateSumInlineBytes) {
+      hipLaunchKernelGGL(gate_reduce<T>,
+                         dim3((unsigned)((ne + kGateReduceThreads - 1) / kGateReduceThreads)),
+                         dim3(kGateReduceThreads), 0, s, part, ne, np, lw);
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      hipLaunchKernelGGL((route_fused<T, 1024, 1, ChunkLds<T, kSmallTokens>>), dim3(1), dim3(1024),
+                         0, s, logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw, r->bitmatrix,
+                         r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs);
+      return hipGetLastError();
+    }
     hipLaunchKernelGGL((route_fused<T, 1024, 1, ChunkLds<T, kSmallTokens>, 2>), dim3(1),
                        dim3(1024), 0, s, logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw,
                        r->bitmatrix, r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs, x,

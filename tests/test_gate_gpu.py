@@ -73,8 +73,14 @@ GATE_CASES = [
     (1000, 33, 1000, 3, "f32"),     # fp32, multi-block
     (4096, 8, 512, 1, "bf16"),      # small-model router
     (4096, 128, 2880, 4, "bf16"),   # gpt-oss-sized router
-    (2, 16, 8200, 2, "bf16"),       # more K-slices than the split-K path takes: full prologue
+    (2, 16, 8200, 2, "bf16"),       # split-K over 65 slices: three rounds of the slice sum
+    (2, 16, 32776, 2, "bf16"),      # more K-slices (257) than the split-K path takes: full prologue
+    (8, 128, 2880, 4, "bf16"),      # split-K sums past the prologue's share: reduction kernel
+    (4, 32, 2880, 4, "bf16"),       # split-K sums added up in the routing kernel's prologue
     (40, 256, 4096, 8, "bf16"),     # split-K with the widest expert bucket
+    (1, 256, 7168, 8, "bf16"),      # DeepSeek-sized router, decode: 112 K-slices
+    (64, 256, 7168, 8, "bf16"),     # the same at the largest split-K batch
+    (17, 64, 1000, 6, "f32"),       # fp32 split-K through the reduction kernel
 ]
 
 
