@@ -423,13 +423,12 @@ template <int RB> __device__ __forceinline__ int gate_swz(int r, int c) {
 // lane ends up holding one token and runs of 4 experts).  Uses S * (NT + EPB) *
 // RB bytes of `lds` and ends with every thread past a barrier, the logits
 // stored.  PART: only the K-slices [zb, ze) are summed and the fp32 sums are
-// stored to part[((t - tok0) * E + e) * pstride] instead.
+// stored to part[(t - tok0) * E + e] instead.
 template <typename T, int NT, int THREADS, int EPB, int S, int RB, bool PART = false>
 __device__ __forceinline__ void gate_logits(const T *__restrict__ x, const T *__restrict__ wg,
                                             int64_t N, int H, int E, int64_t tok0,
                                             T *__restrict__ logits, char *lds, int zb = 0,
-                                            int ze = -1, float *__restrict__ part = nullptr,
-                                            int pstride = 1) {
+                                            int ze = -1, float *__restrict__ part = nullptr) {
   using Mm = GateMma<T>;
   constexpr int NW = THREADS / 64;
   constexpr int RS = NT + EPB;                 // LDS rows of one stage
@@ -532,7 +531,7 @@ __device__ __forceinline__ void gate_logits(const T *__restrict__ x, const T *__
           const int e = eb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           if (e < E) {
             if constexpr (PART)
-              part[((t - tok0) * E + e) * pstride] = acc[j][r];
+              part[(t - tok0) * E + e] = acc[j][r];
             else
               logits[t * E + e] = from_f32<T>(acc[j][r]);
           }
@@ -543,37 +542,44 @@ __device__ __forceinline__ void gate_logits(const T *__restrict__ x, const T *__
   __syncthreads();  // logits visible to the workgroup; the ring's LDS may be reused
 }
 
-// Router GEMM of a small batch (N <= kGateFusedTokens) split over K: workgroup
-// z sums K-slice z of every token and expert and stores the fp32 sums to
-// part[(t * E + e) * npad + z] (a logit's slices contiguous, npad a multiple of
-// 4); the routing kernel adds them up.  The gate weight is read by as many
-// compute units as it has slices instead of by one.
-constexpr int kGateMaxParts = 256;  // more K-slices than this: the one-workgroup GEMM
+// Router GEMM split over K for batches of up to kGateSplitTokens: workgroup
+// (z, y) sums K-group z (g consecutive K-slices) of token tile y
+// (kGateFusedTokens tokens) over all experts and stores the fp32 sums to
+// part[(z * N + t) * E + e] (group-major: a workgroup writes whole rows, and a
+// group's sums of consecutive logits are adjacent); gate_reduce or the routing
+// kernel adds them up.  The gate weight is then
+// read by about kGateSplitWGs compute units at once, each with a ring of slices
+// in flight, instead of by one workgroup per token tile.
+constexpr int kGateMaxParts = 256;  // more K-slices than this: no split over K
+constexpr int64_t kGateSplitTokens = 4096;
+constexpr int kGateSplitWGs = 256;
+// Past one token tile, a row of fewer K-slices than this does not gain from
+// the split (the extra reduction launch costs more: E = 8, H = 512, 4096
+// tokens 14.1 -> 15.4 us).
+constexpr int kGateSplitMinSlices = 8;
 // Split-K sums up to this many bytes are added up in the routing kernel's
 // prologue; more take a reduction kernel of their own first.
 constexpr int64_t kGateSumInlineBytes = 32 * 1024;
 template <typename T, int EPB>
 __global__ __launch_bounds__(256) void gate_partial(const T *__restrict__ x,
                                                     const T *__restrict__ wg, int64_t N, int H,
-                                                    int E, float *__restrict__ part, int npad);
+                                                    int E, float *__restrict__ part, int g);
 
-// Logit i of the split-K router GEMM: its nparts K-slice sums added in slice
-// order from zero in fp32 (rounded by the caller).  The slices are contiguous;
-// the 16-byte loads of 32 of them are all issued before their additions (a
+// Logit i of the split-K router GEMM: its nparts K-group sums (group z at
+// part[z * ne + i]) added in group order from zero in fp32 (rounded by the
+// caller).  The loads of 32 groups are all issued before their additions (a
 // wider round costs more in cold instruction-cache misses than it saves).
 __device__ __forceinline__ float gate_slice_sum(const float *__restrict__ part, int64_t i,
-                                                int nparts) {
-  constexpr int Z = 32, Q = Z / 4;
-  const f32x4_t *q = reinterpret_cast<const f32x4_t *>(part + i * ((nparts + 3) & ~3));
+                                                int64_t ne, int nparts) {
+  constexpr int Z = 32;
   float acc = 0.f;
   for (int z0 = 0; z0 < nparts; z0 += Z) {
-    f32x4_t v[Q];
+    float v[Z];
 #pragma unroll
-    for (int u = 0; u < Q; ++u)
-      v[u] = z0 + 4 * u < nparts ? q[z0 / 4 + u] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < Z; ++u) v[u] = z0 + u < nparts ? part[(z0 + u) * ne + i] : 0.f;
 #pragma unroll
-    for (int z = 0; z < Z; ++z)
-      if (z0 + z < nparts) acc += v[z / 4][z % 4];
+    for (int u = 0; u < Z; ++u)
+      if (z0 + u < nparts) acc += v[u];
   }
   return acc;
 }
@@ -587,7 +593,7 @@ __global__ __launch_bounds__(kGateReduceThreads) void gate_reduce(const float *_
                                                                   int64_t ne, int nparts,
                                                                   T *__restrict__ logits) {
   const int64_t i = (int64_t)blockIdx.x * kGateReduceThreads + threadIdx.x;
-  if (i < ne) logits[i] = from_f32<T>(gate_slice_sum(part, i, nparts));
+  if (i < ne) logits[i] = from_f32<T>(gate_slice_sum(part, i, ne, nparts));
 }
 
 // Router GEMM alone: one workgroup of 256 threads per NT tokens, all experts.
@@ -604,22 +610,38 @@ __global__ __launch_bounds__(kGateThreads) void gate_gemm(const T *__restrict__ 
                                                lds);
 }
 
-// Row bytes of the split-K router GEMM's slices (one slice a workgroup), and
-// the number of slices of a row of rowb bytes.
+// Row bytes of the split-K router GEMM's slices, and the number of slices of a
+// row of rowb bytes.
 constexpr int gate_part_rb(int epb) { return gate_row_bytes(kGateFusedTokens, epb, kGateLdsBudget); }
 inline int gate_parts(int e, int rowb) {
   const int rb = gate_part_rb(gate_bucket(e));
   return (rowb + rb - 1) / rb;
 }
+// Whether the router GEMM of n tokens with rows of nsl K-slices splits over K.
+inline bool gate_split(int64_t n, int nsl) {
+  return kGateSplitK && nsl <= kGateMaxParts &&
+         (n <= kGateFusedTokens || (n <= kGateSplitTokens && nsl >= kGateSplitMinSlices));
+}
+// K-groups for N tokens and nsl slices: about kGateSplitWGs workgroups over the
+// token tiles, each group the same whole number of slices (the last one fewer);
+// a batch of one tile gets one slice a group.
+inline int gate_groups(int64_t n, int nsl) {
+  const int64_t tiles = (n + kGateFusedTokens - 1) / kGateFusedTokens;
+  const int ng = (int)std::min<int64_t>(nsl, (kGateSplitWGs + tiles - 1) / tiles);
+  const int g = (nsl + ng - 1) / ng;
+  return (nsl + g - 1) / g;
+}
 template <typename T, int EPB>
 __global__ __launch_bounds__(256) void gate_partial(const T *__restrict__ x,
                                                     const T *__restrict__ wg, int64_t N, int H,
-                                                    int E, float *__restrict__ part, int npad) {
+                                                    int E, float *__restrict__ part, int g) {
   constexpr int RB = gate_part_rb(EPB);
-  __shared__ __align__(16) char lds[2 * (kGateFusedTokens + EPB) * RB];
-  const int z = blockIdx.x;
-  gate_logits<T, kGateFusedTokens, kGateThreads, EPB, 2, RB, true>(
-      x, wg, N, H, E, 0, nullptr, lds, z, z + 1, part + z, npad);
+  constexpr int S = gate_stages(kGateFusedTokens, EPB, kGateLdsBudget, RB);
+  __shared__ __align__(16) char lds[S * (kGateFusedTokens + EPB) * RB];
+  const int z = blockIdx.x, nsl = (H * (int)sizeof(T) + RB - 1) / RB;
+  const int64_t tok0 = (int64_t)blockIdx.y * kGateFusedTokens;
+  gate_logits<T, kGateFusedTokens, kGateThreads, EPB, S, RB, true>(
+      x, wg, N, H, E, tok0, nullptr, lds, z * g, min(z * g + g, nsl), part + (z * N + tok0) * E);
 }
 
 // Batches of at most NT tokens: one workgroup, one launch.  Every per-entry
@@ -657,7 +679,7 @@ __global__ __launch_bounds__(THREADS) void route_fused(
   if constexpr (GATE == 2) {  // slices summed in order, rounded once
     const int ne = (int)N * E;
     for (int i = tid; i < ne; i += THREADS)
-      logits_out[i] = from_f32<T>(gate_slice_sum(part, i, nparts));
+      logits_out[i] = from_f32<T>(gate_slice_sum(part, i, ne, nparts));
     __syncthreads();
   }
   topk_chunk<T, THREADS, C>(logits, N, E, K, lo, nl, logG, vec, 0, topk_idx, topk_w, bitmatrix,
@@ -881,14 +903,17 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
   T *tw = reinterpret_cast<T *>(r->topk_w);
   T *gs = reinterpret_cast<T *>(r->gate_scal);
   T *lw = const_cast<T *>(logits);
-  const int gate_np = x ? gate_parts(E, H * (int)sizeof(T)) : 0;
-  if (x && N <= kGateFusedTokens && kGateSplitK && gate_np <= kGateMaxParts) {
-    // split-K router GEMM into the scratch, then the routing kernel adds the
-    // slices up in its prologue (batches this small take one logit chunk a lane)
+  const int gate_nsl = x ? gate_parts(E, H * (int)sizeof(T)) : 0;
+  if (x && gate_split(N, gate_nsl)) {
+    // split-K router GEMM into the scratch; the sums are added up by gate_reduce
+    // or, for a small batch, in the routing kernel's prologue
     float *part = reinterpret_cast<float *>(scratch);
-    const int ep = gate_bucket(E), np = gate_np, npad = (np + 3) & ~3;
+    const int ep = gate_bucket(E), np = gate_groups(N, gate_nsl);
+    const int g = (gate_nsl + np - 1) / np;
+    const unsigned tiles = (unsigned)((N + kGateFusedTokens - 1) / kGateFusedTokens);
     auto partial = [&](auto kern) {
-      hipLaunchKernelGGL(kern, dim3((unsigned)np), dim3(256), 0, s, x, wg, N, H, E, part, npad);
+      hipLaunchKernelGGL(kern, dim3((unsigned)np, tiles), dim3(256), 0, s, x, wg, N, H, E, part,
+                         g);
     };
     switch (ep) {
       case 32: partial(gate_partial<T, 32>); break;
@@ -899,24 +924,20 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t ne = N * E;
-    if (ne * npad * 4 > kGateSumInlineBytes) {
-      hipLaunchKernelGGL(gate_reduce<T>,
-                         dim3((unsigned)((ne + kGateReduceThreads - 1) / kGateReduceThreads)),
-                         dim3(kGateReduceThreads), 0, s, part, ne, np, lw);
-      err = hipGetLastError();
-      if (err != hipSuccess) return err;
-      hipLaunchKernelGGL((route_fused<T, 1024, 1, ChunkLds<T, kSmallTokens>>), dim3(1), dim3(1024),
-                         0, s, logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw, r->bitmatrix,
-                         r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs);
+    if (N <= kSmallTokens && ne * np * 4 <= kGateSumInlineBytes) {
+      hipLaunchKernelGGL((route_fused<T, 1024, 1, ChunkLds<T, kSmallTokens>, 2>), dim3(1),
+                         dim3(1024), 0, s, logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw,
+                         r->bitmatrix, r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs,
+                         x, wg, H, lw, part, np);
       return hipGetLastError();
     }
-    hipLaunchKernelGGL((route_fused<T, 1024, 1, ChunkLds<T, kSmallTokens>, 2>), dim3(1),
-                       dim3(1024), 0, s, logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw,
-                       r->bitmatrix, r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs, x,
-                       wg, H, lw, part, np);
-    return hipGetLastError();
-  }
-  if (x && N <= kGateFusedTokens) {  // router GEMM in the routing kernel's prologue
+    hipLaunchKernelGGL(gate_reduce<T>,
+                       dim3((unsigned)((ne + kGateReduceThreads - 1) / kGateReduceThreads)),
+                       dim3(kGateReduceThreads), 0, s, part, ne, np, lw);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    // the logits are in place: the routing kernels below
+  } else if (x && N <= kGateFusedTokens) {  // router GEMM in the routing kernel's prologue
     // (batches this small take one logit chunk a lane: `wide` is false)
     auto fused = [&](auto kern) {
       hipLaunchKernelGGL(kern, dim3(1), dim3(1024), 0, s, logits, N, E, K, lo, nl, logG, vec,
@@ -931,8 +952,7 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
       default: fused(route_fused<T, 1024, 1, L, 1, 256>); break;
     }
     return hipGetLastError();
-  }
-  if (x) {  // router GEMM as a kernel of its own, then the routing kernels
+  } else if (x) {  // router GEMM as a kernel of its own, then the routing kernels
     // The largest tile (32, 64 or 128 tokens) that still gives every compute
     // unit a workgroup: larger tiles read the gate weight less often, but a
     // launch with fewer workgroups than CUs leaves the x stream short of
@@ -1002,10 +1022,10 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
 }  // namespace
 
 size_t gate_scratch_bytes(int64_t n_tokens, int n_experts, int hidden, moe_dtype_t dt) {
-  if (!kGateSplitK || n_tokens > kGateFusedTokens) return 0;
-  const int np = gate_parts(n_experts, hidden * (dt == MOE_BF16 ? 2 : 4));
-  if (np > kGateMaxParts) return 0;
-  return align256((size_t)((np + 3) & ~3) * n_tokens * n_experts * 4);
+  const int nsl = gate_parts(n_experts, hidden * (dt == MOE_BF16 ? 2 : 4));
+  if (!gate_split(n_tokens, nsl)) return 0;
+  const int np = gate_groups(n_tokens, nsl);
+  return align256((size_t)np * n_tokens * n_experts * 4);
 }
 
 size_t route_scratch_bytes(int64_t n_tokens, int n_experts, int topk) {

@@ -67,12 +67,15 @@ GATE_CASES = [
     (1, 128, 2880, 4, "bf16"),      # decode: router GEMM in the routing kernel's prologue
     (33, 8, 128, 2, "f32"),         # the tiny fp32 layer's router
     (64, 32, 512, 4, "bf16"),       # largest batch of the prologue path
-    (65, 32, 512, 4, "bf16"),       # first batch of the separate GEMM kernel
+    (65, 32, 512, 4, "bf16"),       # first batch of the separate GEMM kernel (4 K-slices)
+    (65, 128, 2880, 4, "bf16"),     # first batch of the split over token tiles and K-groups
     (300, 6, 136, 2, "bf16"),       # E off the 32/8 grids; H leaves a 16-byte K tail
     (777, 256, 264, 8, "bf16"),     # largest expert count, multi-block routing
-    (1000, 33, 1000, 3, "f32"),     # fp32, multi-block
-    (4096, 8, 512, 1, "bf16"),      # small-model router
-    (4096, 128, 2880, 4, "bf16"),   # gpt-oss-sized router
+    (1000, 33, 1000, 3, "f32"),     # fp32, multi-block, split over K (16 groups)
+    (4096, 8, 512, 1, "bf16"),      # small-model router (too few K-slices to split)
+    (4096, 128, 2880, 4, "bf16"),   # gpt-oss-sized router: 4 K-groups of 6, 6, 6 and 5 slices
+    (4097, 128, 2880, 4, "bf16"),   # first batch past the split: the separate GEMM kernel
+    (700, 256, 7168, 8, "bf16"),    # DeepSeek-sized router at a prefill batch (11 tiles)
     (2, 16, 8200, 2, "bf16"),       # split-K over 65 slices: three rounds of the slice sum
     (2, 16, 32776, 2, "bf16"),      # more K-slices (257) than the split-K path takes: full prologue
     (8, 128, 2880, 4, "bf16"),      # split-K sums past the prologue's share: reduction kernel
