@@ -60,7 +60,8 @@ constexpr int kRouteTokens = 256;  // tokens per routing block (one per thread i
 
 size_t route_scratch_bytes(int64_t n_tokens, int n_experts, int topk);
 // Scratch the router GEMM of moe_gate_route needs besides route_scratch_bytes
-// (the split-K partial sums of small batches; the two are never live together).
+// (the split-K partial sums of batches up to 4096 tokens; the two are never
+// live together).
 size_t gate_scratch_bytes(int64_t n_tokens, int n_experts, int hidden, moe_dtype_t dt);
 // Routing for the expert share [local_offset, local_offset + n_local) of the
 // n_experts (0 and n_experts for the whole layer).  With x != nullptr the

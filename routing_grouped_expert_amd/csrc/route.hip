@@ -716,6 +716,105 @@ __global__ __launch_bounds__(THREADS) void route_fused(
   }
 }
 
+// One token: a single wave runs the whole routing step in registers, with no
+// workgroup barrier.  Lane l holds the 16-byte logit chunk of experts
+// [l V, l V + V); k rounds of a wave-wide key maximum select the experts (the
+// keys and tie rule of topk_chunk, so the same choices), and the softmax adds
+// up the same terms in the same slot order.  With at most one entry per expert,
+// an entry's sorted position and every offset are prefix popcounts of the
+// selected-expert mask, whose bitmatrix word w lane w holds.  SUM: the logits
+// are first added up from the router GEMM's K-group sums (in group order, as
+// gate_reduce), stored, and read back from LDS.
+template <typename T, bool SUM>
+__global__ __launch_bounds__(64) void route_one(
+    const T *logits, int E, int K, int lo, int nl, int vec, int32_t *__restrict__ topk_idx,
+    T *__restrict__ topk_w, uint32_t *__restrict__ bitmatrix, int32_t *__restrict__ col_sum,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ col_sorted,
+    int32_t *__restrict__ row_sorted, T *__restrict__ gate_scal,
+    const float *__restrict__ part = nullptr, int nparts = 0, T *logits_out = nullptr) {
+  using Lg = Logit<T>;
+  using Key = typename Lg::Key;
+  constexpr int V = Lg::kVec;
+  const int lane = threadIdx.x, e0 = lane * V;
+  u32x4_t raw = {0u, 0u, 0u, 0u};
+  if constexpr (SUM) {
+    __shared__ __align__(16) T s_lg[kMaxExperts];
+    for (int e = lane; e < E; e += 64) {
+      const T v = from_f32<T>(gate_slice_sum(part, e, E, nparts));
+      logits_out[e] = v;
+      s_lg[e] = v;
+    }
+    __syncthreads();
+    // chunks end within the kMaxExperts entries; values past E are masked below
+    if (e0 < E) raw = *reinterpret_cast<const u32x4_t *>(s_lg + e0);
+  } else {
+    if (e0 < E) raw = fetch16(logits, e0, E, vec != 0);
+  }
+  Key key[V];
+  Lg::decode(raw, e0, E, key);
+  int my_e = -1;  // lane j: slot j's expert and logit
+  float my_v = 0.f, vmax = 0.f, ssum = 0.f;
+  uint32_t word = 0;  // lane w: bitmatrix word w (local expert ids)
+  for (int j = 0; j < K; ++j) {
+    Key m = key[0];
+#pragma unroll
+    for (int i = 1; i < V; ++i) m = kmax(m, key[i]);
+    m = group_max(m, 64);
+    const int e = Lg::expert(m);
+    const float v = Lg::value(m);
+#pragma unroll
+    for (int i = 0; i < V; ++i)
+      if (e0 + i == e) key[i] = 0;  // only the owning lane matches
+    if (j == 0) vmax = v;           // slot 0 holds the maximum
+    ssum += expf(v - vmax);
+    if (lane == j) {
+      my_e = e;
+      my_v = v;
+    }
+    const int l = e - lo;
+    if ((unsigned)l < (unsigned)nl && (l >> 5) == lane) word |= 1u << (l & 31);
+  }
+  // selected local experts below local id x (x <= nl <= kMaxExperts): the
+  // popcount prefix of the words before x / 32 plus the bits of that word below
+  // x.  Shuffles: every lane calls this with the same trip count.
+  const int pc = __popc(word), excl = wave_inclusive_sum(pc) - pc;
+  auto below = [&](int x, uint32_t &w) {
+    w = (uint32_t)__shfl((int)word, x >> 5);
+    return __shfl(excl, x >> 5) + __popc(w & ((1u << (x & 31)) - 1u));
+  };
+  for (int x0 = 0; x0 <= kMaxExperts; x0 += 64) {
+    const int x = x0 + lane;
+    uint32_t w;
+    const int r = below(min(x, nl), w);
+    if (x <= nl) offsets[x] = r;
+    if (x < nl) col_sum[x] = (w >> (x & 31)) & 1u;
+  }
+  const int words = (nl + 31) >> 5;
+  if (lane < words) bitmatrix[lane] = word;
+  const int l = my_e - lo;
+  const bool local = lane < K && (unsigned)l < (unsigned)nl;
+  uint32_t w;
+  const int p = below(local ? l : 0, w);
+  uint32_t wn;
+  const int m_local = below(nl, wn);
+  if (lane < K) {
+    const T wt = from_f32<T>(expf(my_v - vmax) / ssum);
+    topk_idx[lane] = my_e;
+    topk_w[lane] = wt;
+    if (local) {
+      col_sorted[p] = lane;
+      row_sorted[lane] = p;
+      gate_scal[p] = wt;
+    } else {
+      row_sorted[lane] = -1;
+    }
+    if (lane >= m_local) {  // positions no local entry fills
+      col_sorted[lane] = -1;
+      gate_scal[lane] = from_f32<T>(0.f);
+    }
+  }
+}
+
 // Multi-block path, kernel 1: one chunk of NTB tokens per workgroup (64 or 256);
 // per-block expert counts and per-entry in-block ranks to the workspace.
 constexpr int kTopkThreads = 1024;
@@ -924,6 +1023,12 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t ne = N * E;
+    if (N == 1 && ne * np * 4 <= kGateSumInlineBytes) {
+      hipLaunchKernelGGL((route_one<T, true>), dim3(1), dim3(64), 0, s, logits, E, K, lo, nl, vec,
+                         r->topk_idx, tw, r->bitmatrix, r->col_sum, r->offsets, r->col_sorted,
+                         r->row_sorted, gs, part, np, lw);
+      return hipGetLastError();
+    }
     if (N <= kSmallTokens && ne * np * 4 <= kGateSumInlineBytes) {
       hipLaunchKernelGGL((route_fused<T, 1024, 1, ChunkLds<T, kSmallTokens>, 2>), dim3(1),
                          dim3(1024), 0, s, logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw,
@@ -985,7 +1090,11 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
     if (err != hipSuccess) return err;
   }
   if (path == kPathFused) {
-    if (N <= kSmallTokens)  // (`wide` needs N > 64)
+    if (N == 1)
+      hipLaunchKernelGGL((route_one<T, false>), dim3(1), dim3(64), 0, s, logits, E, K, lo, nl, vec,
+                         r->topk_idx, tw, r->bitmatrix, r->col_sum, r->offsets, r->col_sorted,
+                         r->row_sorted, gs);
+    else if (N <= kSmallTokens)  // (`wide` needs N > 64)
       hipLaunchKernelGGL((route_fused<T, 1024, 1, ChunkLds<T, kSmallTokens>>), dim3(1), dim3(1024),
                          0, s, logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw, r->bitmatrix,
                          r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs);

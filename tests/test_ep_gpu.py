@@ -42,6 +42,9 @@ ROUTE_CASES = [
     (40, 64, 8, "bf16", 60, 4),
     (5000, 16, 1, "bf16", 12, 4),      # top-1
     (65536, 128, 4, "bf16", 16, 16),   # EP8 share at the largest routing batch
+    (1, 128, 4, "bf16", 17, 45),       # one token (single-wave kernel), share across words
+    (1, 256, 16, "bf16", 224, 32),     # one token, last share of the widest layer
+    (1, 32, 4, "f32", 8, 8),           # one token, fp32
 ]
 
 
@@ -51,7 +54,7 @@ def test_route_ep_bit_exact(n, e, k, dt, lo, nl):
     _route(routing_logits(n, e, dt, seed=3 * n + e + lo), k, lo, nl, "share")
 
 
-@pytest.mark.parametrize("n", [100, 3000])
+@pytest.mark.parametrize("n", [1, 100, 3000])
 def test_route_ep_whole_layer_equals_route(n):
     lg = routing_logits(n, 64, "bf16", seed=n).to(DEV)
     a = moe_route(lg, 4)
@@ -61,7 +64,7 @@ def test_route_ep_whole_layer_equals_route(n):
         assert torch.equal(getattr(a, f), getattr(b, f)), f
 
 
-@pytest.mark.parametrize("n", [150, 2000])
+@pytest.mark.parametrize("n", [1, 150, 2000])
 def test_route_ep_share_nobody_chose(n):
     lg = routing_logits(n, 32, "f32", seed=5)
     lg[:, 8:16] = -40.0                        # never in any token's top-4

@@ -45,6 +45,12 @@ EDGE = [
     (2049, 3, 2, "bf16"),    # compact path, scalar loads, ragged 64-token groups
     (12345, 256, 16, "bf16"),  # 64-token blocks: widest layer, ragged last block
     (16385, 32, 4, "bf16"),  # first batch back on 256-token blocks, one-token tail
+    # one token: the single-wave kernel
+    (1, 256, 16, "bf16"),    # widest layer, largest top-k
+    (1, 33, 3, "bf16"),      # scalar loads (E not a multiple of the 16-byte vector)
+    (1, 200, 8, "f32"),      # fp32 logits over all 64 lanes
+    (1, 5, 5, "f32"),        # k == E
+    (1, 1, 1, "bf16"),       # single expert
 ]
 
 
@@ -60,6 +66,12 @@ def test_routing_forced_ties_and_signed_zero():
     for dt in (torch.bfloat16, torch.float32):
         _run(lg.to(dt), 4, f"ties-{dt}")
     _run(torch.full((500, 16), 0.75).to(torch.bfloat16), 3, "all-equal")
+    # one token: ties and signed zeros through the single-wave kernel
+    for dt in (torch.bfloat16, torch.float32):
+        _run(lg[:1].to(dt), 4, f"ties-one-{dt}")
+        _run(torch.tensor([[0.0, -0.0, 1.0, 1.0, -0.0, 0.0, 1.0, -2.0, 0.0]]).to(dt), 6,
+             f"signed-zero-one-{dt}")
+    _run(torch.full((1, 40), -1.5).to(torch.bfloat16), 7, "all-equal-one")
 
 
 def test_routing_skewed_zipf():
