@@ -627,6 +627,7 @@ inline bool gate_split(int64_t n, int nsl) {
 // a batch of one tile gets one slice a group.
 inline int gate_groups(int64_t n, int nsl) {
   const int64_t tiles = (n + kGateFusedTokens - 1) / kGateFusedTokens;
+  if (tiles <= 1) return nsl;  // (an empty batch included)
   const int ng = (int)std::min<int64_t>(nsl, (kGateSplitWGs + tiles - 1) / tiles);
   const int g = (nsl + ng - 1) / ng;
   return (nsl + g - 1) / g;

@@ -58,6 +58,18 @@ def test_workspace_sizes(lib):
     assert lib.moe_workspace_bytes(16, 8, 2, 512, 512, 7) == 0
 
 
+def test_workspace_sizes_router_gemm(lib):
+    # hidden given: room for the router GEMM's split-K partial sums as well; every
+    # batch size is defined, the empty batch included
+    for n in (0, 1, 64, 65, 4096, 4097, 65536):
+        assert lib.moe_workspace_bytes(n, 128, 4, 2880, 0, N.MOE_BF16) > 0, n
+        assert lib.moe_workspace_bytes(n, 128, 4, 2880, 2880, N.MOE_BF16) > 0, n
+    assert lib.moe_workspace_bytes(0, 8, 2, 128, 256, N.MOE_F32) > 0
+    # one token: fp32 sums of 23 K-slices (2880 bf16 values in 256-byte slices)
+    # for each of the 128 experts
+    assert lib.moe_workspace_bytes(1, 128, 4, 2880, 0, N.MOE_BF16) >= 23 * 128 * 4
+
+
 def routing(fields=None, w_dtype=N.MOE_BF16, ptr=FAKE):
     r = N.MoeRouting(*([ptr] * 8), w_dtype)
     for k, v in (fields or {}).items():

@@ -84,6 +84,8 @@ GATE_CASES = [
     (1, 256, 7168, 8, "bf16"),      # DeepSeek-sized router, decode: 112 K-slices
     (64, 256, 7168, 8, "bf16"),     # the same at the largest split-K batch
     (17, 64, 1000, 6, "f32"),       # fp32 split-K through the reduction kernel
+    (2000, 64, 3000, 4, "f32"),     # fp32, K-groups of 6 slices (the last 5), K tail
+    (300, 6, 2000, 2, "bf16"),      # E off the 32/8 grids through the split
 ]
 
 
