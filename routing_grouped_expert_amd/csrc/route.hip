@@ -25,17 +25,21 @@
 //  * route_fused: batches of up to 256 tokens run both phases in one
 //    workgroup of 1024 threads with every per-entry value kept in LDS (one
 //    launch for the whole routing step).
+//  * route_one: a single token, in one wave's registers (no workgroup
+//    barrier; offsets and positions are prefix popcounts of its experts).
 //
 // Router GEMM (moe_gate_route): the logits are computed from the token rows and
 // the router's gate weight (logits = x . W_gate^T, fp32 accumulation on MFMA,
 // rounded once to the layer dtype) and written out; top-k then runs on them.
 // The router's own matmul is the step ahead of the routing that the vLLM PR
-// #45457 report leaves as a separate kernel ("motivation").  Batches of at
-// most kGateFusedTokens tokens compute their logits in the prologue of the
-// one-workgroup routing kernel (one launch for the whole step); larger batches
-// run the same device function as a kernel of its own, one workgroup per 64
-// tokens, because the prologue of a 256-token routing block would put all of
-// that block's router matmul on one compute unit.
+// #45457 report leaves as a separate kernel ("motivation").  Batches of up to
+// kGateSplitTokens tokens split the product over 64-token tiles and K-groups
+// (gate_partial, about one workgroup a compute unit) and add the fp32 group
+// sums up in the routing kernel's prologue (one token, or a few with little to
+// add) or in gate_reduce; rows too short to split and larger batches run the
+// whole product per token tile, in the prologue of the one-workgroup routing
+// kernel (at most kGateFusedTokens tokens) or as gate_gemm ahead of the
+// routing kernels.
 //
 // Expert-parallel share: every kernel takes the share [lo, lo + nl) of the E
 // experts that this GPU holds (lo = 0, nl = E for the whole layer).  Top-k and
@@ -387,10 +391,10 @@ template <> struct GateMma<float> {
 };
 
 constexpr int kGateRowBytes = 256;  // one K-slice of a row in LDS (preferred)
-// Batches up to this size finish the router GEMM in the one-workgroup routing
-// kernel's prologue; larger ones launch gate_gemm first.  kGateSplitK: the
-// prologue adds up K-slice sums that gate_partial spread over many compute
-// units, instead of computing the whole product on one.
+// Token tile of the split router GEMM, and the largest batch whose whole
+// product may run in the one-workgroup routing kernel's prologue.  kGateSplitK:
+// split over K-groups where it pays (gate_split), instead of computing a
+// tile's whole product on one compute unit.
 constexpr int kGateFusedTokens = 64;
 constexpr bool kGateSplitK = true;
 
@@ -569,7 +573,7 @@ __global__ __launch_bounds__(256) void gate_partial(const T *__restrict__ x,
 // part[z * ne + i]) added in group order from zero in fp32 (rounded by the
 // caller).  The loads of 32 groups are all issued before their additions (a
 // wider round costs more in cold instruction-cache misses than it saves).
-__device__ __forceinline__ float gate_slice_sum(const float *__restrict__ part, int64_t i,
+__device__ __forceinline__ float gate_group_sum(const float *__restrict__ part, int64_t i,
                                                 int64_t ne, int nparts) {
   constexpr int Z = 32;
   float acc = 0.f;
@@ -593,7 +597,7 @@ __global__ __launch_bounds__(kGateReduceThreads) void gate_reduce(const float *_
                                                                   int64_t ne, int nparts,
                                                                   T *__restrict__ logits) {
   const int64_t i = (int64_t)blockIdx.x * kGateReduceThreads + threadIdx.x;
-  if (i < ne) logits[i] = from_f32<T>(gate_slice_sum(part, i, ne, nparts));
+  if (i < ne) logits[i] = from_f32<T>(gate_group_sum(part, i, ne, nparts));
 }
 
 // Router GEMM alone: one workgroup of 256 threads per NT tokens, all experts.
@@ -655,7 +659,7 @@ __global__ __launch_bounds__(256) void gate_partial(const T *__restrict__ x,
 // stored.
 constexpr int kFusedGateRing = 140 * 1024;
 // GATE: 0 logits given; 1 router GEMM in the prologue; 2 the prologue adds up
-// the K-slice partial sums of gate_partial (nparts slices) into the logits.
+// the K-group sums of gate_partial (nparts groups) into the logits.
 template <typename T, int THREADS, int C, typename Lds, int GATE = 0, int EPB = 32>
 __global__ __launch_bounds__(THREADS) void route_fused(
     const T *logits, int64_t N, int E, int K, int lo, int nl, int logG, int vec,
@@ -677,10 +681,10 @@ __global__ __launch_bounds__(THREADS) void route_fused(
   const int tid = threadIdx.x;
   if constexpr (GATE == 1)  // N <= kGateFusedTokens
     gate_logits<T, kGateFusedTokens, THREADS, EPB, GS, GRB>(x, wg, N, H, E, 0, logits_out, s_raw);
-  if constexpr (GATE == 2) {  // slices summed in order, rounded once
+  if constexpr (GATE == 2) {  // groups summed in order, rounded once
     const int ne = (int)N * E;
     for (int i = tid; i < ne; i += THREADS)
-      logits_out[i] = from_f32<T>(gate_slice_sum(part, i, ne, nparts));
+      logits_out[i] = from_f32<T>(gate_group_sum(part, i, ne, nparts));
     __syncthreads();
   }
   topk_chunk<T, THREADS, C>(logits, N, E, K, lo, nl, logG, vec, 0, topk_idx, topk_w, bitmatrix,
@@ -741,7 +745,7 @@ __global__ __launch_bounds__(64) void route_one(
   if constexpr (SUM) {
     __shared__ __align__(16) T s_lg[kMaxExperts];
     for (int e = lane; e < E; e += 64) {
-      const T v = from_f32<T>(gate_slice_sum(part, e, E, nparts));
+      const T v = from_f32<T>(gate_group_sum(part, e, E, nparts));
       logits_out[e] = v;
       s_lg[e] = v;
     }
