@@ -495,8 +495,8 @@ def main():
                          "of known size that hardware byte counters can be scaled by")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md on how the layer would shard)", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library drives a single GPU and has no "
+              "multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
     if args.calibrate_copy > 0:

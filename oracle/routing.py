@@ -23,7 +23,7 @@ What is computed, and where the pages define it:
   (local_expert_offset, num_local_experts) pair of the kernel call in the vLLM
   PR #47106 report ("key source snippets").
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 ties in top-k go to the lowest expert index; slots are ordered by descending
 logit, ties by ascending index; -0.0 equals +0.0; logits must be finite;
 softmax is evaluated in float64 and rounded once (nearest-even) to the weight
