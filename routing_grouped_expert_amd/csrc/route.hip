@@ -207,10 +207,13 @@ __device__ __forceinline__ void topk_chunk(const T *logits, int64_t N, int E, in
   const int tpp = 64 >> logG;  // tokens per wave pass
   const int grp = lane >> logG, lg = lane & (G - 1);
   const int words = (nl + 31) >> 5;  // bitmatrix words over the local experts
-  // Tokens are dealt round-robin over the NW = THREADS / 64 waves: pass p of
-  // wave w, group grp holds chunk token (p * tpp + grp) * NW + w, so a small
-  // batch still spreads over every wave, and many waves per SIMD overlap the
-  // serial reduction chains of their passes.
+  // Whole passes are dealt round-robin over the NW = THREADS / 64 waves: pass
+  // p of wave w is pass q = p * NW + w of the chunk, whose group grp holds
+  // chunk token q * tpp + grp.  A partial chunk then fills the passes of the
+  // first waves and the rest stop at once: a wave's pass costs the same
+  // instructions however many of its groups hold a token, so spreading a few
+  // tokens over every wave multiplied the selection's VALU work (32 tokens of
+  // 4 lanes each: 16 wave passes instead of 2).
   constexpr int NW = THREADS / 64;
   const int npass = (NT / NW + tpp - 1) / tpp;
   // A lane's 16-byte logit chunks for kBatch passes are fetched before any is
@@ -221,12 +224,12 @@ __device__ __forceinline__ void topk_chunk(const T *logits, int64_t N, int E, in
   // A pass whose first token (group 0) is past N has no live token, nor has
   // any later pass of the wave: the wave stops there (the rank phase treats
   // chunk tokens past N as empty).
-  auto first_tok = [&](int p) { return tok0 + (int64_t)p * tpp * NW + wave; };
+  auto first_tok = [&](int p) { return tok0 + ((int64_t)p * NW + wave) * tpp; };
   for (int pass0 = 0; pass0 < npass && first_tok(pass0) < N; pass0 += kBatch) {
     u32x4_t raw[kBatch][C];
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
-      const int tl = ((pass0 + q) * tpp + grp) * NW + wave;  // token within the chunk
+      const int tl = ((pass0 + q) * NW + wave) * tpp + grp;  // token within the chunk
       const int64_t t = tok0 + tl;
 #pragma unroll
       for (int c = 0; c < C; ++c) {
@@ -238,7 +241,7 @@ __device__ __forceinline__ void topk_chunk(const T *logits, int64_t N, int E, in
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       if (pass0 + q < npass && first_tok(pass0 + q) < N) {
-        const int tl = ((pass0 + q) * tpp + grp) * NW + wave;
+        const int tl = ((pass0 + q) * NW + wave) * tpp + grp;
         const int64_t t = tok0 + tl;
         const bool inwave = tl < NT;
         const bool live = inwave && t < N;
@@ -691,11 +694,13 @@ __global__ __launch_bounds__(THREADS) void route_fused(
                             L);
   __syncthreads();
   rank_chunk<THREADS>(nl, (int)N, L);
-  for (int t = tid; t < N; t += THREADS) {
-#pragma unroll
-    for (int j = 0; j < Lds::kSlots; ++j) {
-      const int l = (int)L.sel[t * K + j] - lo;
-      if (j < K && (unsigned)l < (unsigned)nl) s_rank[t * K + j] = (uint16_t)chunk_rank(L, t, l);
+  const int M = (int)N * K;
+  // in-chunk ranks, one entry a thread on waves 1.., while wave 0 scans the
+  // chunk totals into offsets
+  if (tid >= 64) {
+    for (int f = tid - 64; f < M; f += THREADS - 64) {
+      const int l = (int)L.sel[f] - lo;
+      if ((unsigned)l < (unsigned)nl) s_rank[f] = (uint16_t)chunk_rank(L, f / K, l);
     }
   }
   block_exclusive_scan(L.tot, s_off, nl);  // synchronises
@@ -703,7 +708,7 @@ __global__ __launch_bounds__(THREADS) void route_fused(
     offsets[e] = s_off[e];
     if (e < nl) col_sum[e] = L.tot[e];
   }
-  const int M = (int)N * K, m_local = s_off[nl];
+  const int m_local = s_off[nl];
   for (int f = tid; f < M; f += THREADS) {
     const int l = (int)L.sel[f] - lo;
     if ((unsigned)l < (unsigned)nl) {
