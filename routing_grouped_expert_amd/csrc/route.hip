@@ -981,11 +981,18 @@ constexpr int kFusedTokens = 256;
 // then spreads the experts over all 16 waves of the workgroup.
 constexpr int kSmallTokens = 64;
 static_assert(kGateFusedTokens <= kSmallTokens, "the router-GEMM prologue paths use the small chunk");
+// Past kFusedWideTokens tokens, layers of more than kFusedWideExperts experts
+// (two or more 16-byte logit chunks per lane-group row) take the multi-block
+// path: the one-workgroup top-k is then VALU-bound on one CU (E = 128 at 256
+// tokens: 15.3 us fused, 11.4 us in 64-token blocks; E = 256, k = 8: 35.5 vs
+// 20.6), while few experts stay cheaper in one launch (E = 32 at 256 tokens:
+// 7.4 vs 10.4 us; E = 64, k = 16 at 150 tokens: 15.7 vs 17.4).
+constexpr int kFusedWideTokens = 128, kFusedWideExperts = 64;
 enum RoutePath { kPathFused, kPathBlocks };
 inline RoutePath route_path(int64_t N, int E, int K) {
-  (void)E;
   (void)K;
-  return N <= kFusedTokens ? kPathFused : kPathBlocks;
+  if (N <= kFusedWideTokens) return kPathFused;
+  return N <= kFusedTokens && E <= kFusedWideExperts ? kPathFused : kPathBlocks;
 }
 // Tokens per block of the multi-block path.  A block's top-k runs on one CU,
 // so batches too small to fill the CUs with 256-token blocks take 64-token

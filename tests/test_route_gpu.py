@@ -45,6 +45,10 @@ EDGE = [
     (2049, 3, 2, "bf16"),    # compact path, scalar loads, ragged 64-token groups
     (12345, 256, 16, "bf16"),  # 64-token blocks: widest layer, ragged last block
     (16385, 32, 4, "bf16"),  # first batch back on 256-token blocks, one-token tail
+    (129, 128, 4, "bf16"),   # past 128 tokens, more than 64 experts: 64-token blocks
+    (256, 256, 8, "bf16"),   # the same at the one-workgroup path's former limit
+    (200, 128, 4, "f32"),    # fp32 logits on that path
+    (256, 64, 16, "bf16"),   # 64 experts stay on the one-workgroup path up to 256 tokens
     # one token: the single-wave kernel
     (1, 256, 16, "bf16"),    # widest layer, largest top-k
     (1, 33, 3, "bf16"),      # scalar loads (E not a multiple of the 16-byte vector)
