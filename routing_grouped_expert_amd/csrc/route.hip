@@ -972,10 +972,11 @@ __global__ __launch_bounds__(kScatterThreads) void route_scatter(
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Which routing path a batch takes: one workgroup for up to 256 tokens,
-// otherwise one workgroup per 256 tokens plus the scatter kernel.  (One
-// workgroup for up to 4096 tokens of a few experts was measured slower than
-// the two kernels: 16.8 against 11.1 us at N = 4096, E = 8.)
+// Which routing path a batch takes: one workgroup for small batches (see
+// route_path), otherwise one workgroup per block of 64 or 256 tokens plus the
+// scatter kernel.  (One workgroup for up to 4096 tokens of a few experts was
+// measured slower than the two kernels: 16.8 against 11.1 us at N = 4096,
+// E = 8.)
 constexpr int kFusedTokens = 256;
 // Batches of at most 64 tokens (decode) use a one-group chunk: the rank phase
 // then spreads the experts over all 16 waves of the workgroup.
