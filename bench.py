@@ -166,8 +166,9 @@ def cpu_baseline(spec, layer, budget_s: float):
 def expert_kernel(spec, mxfp4: bool) -> str:
     """Which kernel family runs the expert GEMMs of this layer: the library takes
     the matrix-vector kernel for decode-sized bf16 batches (at most 128 tokens,
-    N * topk <= 3 E, or <= 1.5 E with MXFP4 weights; K <= 4096) and the MFMA
-    tiles otherwise.  Used for labels only."""
+    N * topk <= 3 E for w13 (5 E for w2), or <= 1.5 E with MXFP4 weights;
+    K <= 4096) and the MFMA tiles otherwise.  The label names the w13 kernel.
+    Used for labels only."""
     n, m, e = spec.n_tokens, spec.n_tokens * spec.topk, spec.n_local or spec.n_experts
     fits = spec.dtype == "bf16" and n <= 128 and max(spec.hidden, spec.inter) <= 4096 and \
         (2 * m <= 3 * e if mxfp4 else m <= 3 * e)

@@ -539,11 +539,11 @@ hipError_t launch_epi(const GemmArgs &a, int64_t M, int cb, hipStream_t s) {
 }  // namespace
 
 bool gemv_fits(moe_dtype_t dt, int64_t n_tokens, int topk, int n_experts, int K, int Nout,
-               bool mxfp4) {
+               bool mxfp4, bool plain) {
   if (dt != MOE_BF16 || n_tokens > kGemvMaxTokens || K % 8 != 0 || K > 4096 || Nout % 8 != 0)
     return false;
   const int64_t m = n_tokens * topk;
-  return mxfp4 ? 2 * m <= 3 * (int64_t)n_experts : m <= 3 * (int64_t)n_experts;
+  return mxfp4 ? 2 * m <= 3 * (int64_t)n_experts : m <= (plain ? 5 : 3) * (int64_t)n_experts;
 }
 
 bool gemm2_combine_fits(moe_dtype_t dt, int64_t n_tokens, int topk, int n_experts, int hidden,

@@ -744,7 +744,7 @@ hipError_t launch_gemm2(const void *act_in, const void *w2, void *y, const int32
   GemmArgs a{act_in, w2, y, offsets, col_sorted, gate_scal, (uint32_t)(M * inter * es),
              (uint32_t)(c_rows * hidden * es), gate_dt == MOE_BF16, n_experts, inter, hidden,
              topk, 0, 0, 0, ActParams{1.f, 0.f, 0.f}, w2_scale};
-  if (gemv_fits(dt, n_tokens, topk, n_experts, inter, hidden, w2_scale != nullptr))
+  if (gemv_fits(dt, n_tokens, topk, n_experts, inter, hidden, w2_scale != nullptr, true))
     return launch_gemv(a, 1, direct_out ? EPI_OUT : EPI_Y, n_tokens, M, s);
   if (dt == MOE_BF16)
     return direct_out ? launch_t<bf16_t, 1, EPI_OUT>(a, M, n_experts, s)
