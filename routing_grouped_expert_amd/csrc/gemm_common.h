@@ -65,12 +65,13 @@ __device__ __forceinline__ float act_val(float g, float u, float nal, const ActP
 // Decode-sized batches run the expert GEMMs as grouped matrix-vector
 // products (gemv.hip): bf16 activations, at most kGemvMaxTokens tokens, and
 // few rows per expert on average -- N * topk <= 3 E for w13 with bf16 weights
-// (5 E for the plain w2), <= 1.5 E with MXFP4 weights, whose FP4 decode is
-// repeated for every row.  Above that the MFMA tiles are faster (measured on
-// gpt-oss-sized layers, E = 32 and 128, up to 128 tokens: at 4-5 rows an
-// expert the gated w13 is 3-6 % slower as matrix-vector products, the plain
-// w2 6-19 % faster).  True when that kernel takes a launch of this shape;
-// plain: the w2 launch.
+// (5 E for the plain w2), <= 1.5 E for w13 with MXFP4 weights, whose FP4
+// decode is repeated for every row (3 E for their w2).  Above that the MFMA
+// tiles are faster (measured on gpt-oss-sized layers, E = 32 and 128, up to
+// 128 tokens: at 4-5 rows an expert the gated bf16 w13 is 3-6 % slower as
+// matrix-vector products, the plain bf16 w2 6-19 % faster; the MXFP4 w2 gains
+// up to 2-3 rows an expert and loses past 4).  True when that kernel takes a
+// launch of this shape; plain: the w2 launch.
 constexpr int kGemvMaxTokens = 128;
 bool gemv_fits(moe_dtype_t dt, int64_t n_tokens, int topk, int n_experts, int K, int Nout,
                bool mxfp4, bool plain = false);

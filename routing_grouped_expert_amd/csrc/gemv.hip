@@ -543,7 +543,9 @@ bool gemv_fits(moe_dtype_t dt, int64_t n_tokens, int topk, int n_experts, int K,
   if (dt != MOE_BF16 || n_tokens > kGemvMaxTokens || K % 8 != 0 || K > 4096 || Nout % 8 != 0)
     return false;
   const int64_t m = n_tokens * topk;
-  return mxfp4 ? 2 * m <= 3 * (int64_t)n_experts : m <= (plain ? 5 : 3) * (int64_t)n_experts;
+  const int64_t e = n_experts;
+  if (mxfp4) return plain ? m <= 3 * e : 2 * m <= 3 * e;
+  return m <= (plain ? 5 : 3) * e;
 }
 
 bool gemm2_combine_fits(moe_dtype_t dt, int64_t n_tokens, int topk, int n_experts, int hidden,

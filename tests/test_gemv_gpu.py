@@ -35,6 +35,10 @@ CASES = [
     ("n4-ragged-cols", 4, 1032, 520, 9, 2, "silu", "packed", {}),
     ("n24-k2", 24, 256, 384, 16, 2, "silu", "packed", {}),
     ("n32-top1", 32, 136, 200, 16, 1, "relu2", "packed", {}),
+    # 4-5 rows an expert: w13 on the MFMA tiles, w2 as matrix-vector products
+    ("n20-w2-only", 20, 256, 384, 8, 2, "silu", "packed", {}),
+    ("n9-oai-w2-only", 9, 264, 200, 9, 4, "swiglu_oai", "interleaved",
+     {"alpha": 1.702, "beta": 1.0, "limit": 7.0}),
 ]
 
 # Skewed logits send nearly every token to one expert: that expert holds more

@@ -78,6 +78,10 @@ MX = [
      {"alpha": 1.702, "beta": 1.0, "limit": 7.0}),
     ("n3-silu-interleaved", 3, 160, 96, 8, 3, "silu", "interleaved", {}),
     ("n8-relu2-top1", 8, 96, 160, 8, 1, "relu2", "packed", {}),
+    # 2-3 rows an expert: w13 on the MFMA tiles, w2 as matrix-vector products
+    ("n6-w2-only", 6, 128, 160, 8, 4, "silu", "packed", {}),
+    ("n10-oai-w2-only", 10, 256, 192, 16, 4, "swiglu_oai", "interleaved",
+     {"alpha": 1.702, "beta": 1.0, "limit": 7.0}),
     ("n24-skew-k4096", 24, 4096, 128, 32, 1, "silu", "packed", {"zipf_s": 6.0}),
     # prefill-sized: the 128-row ping-pong tiles for both GEMMs
     ("mq-oai-interleaved", 2500, 1024, 512, 4, 2, "swiglu_oai", "interleaved",
@@ -88,16 +92,22 @@ MX = [
 
 
 def _same_kernels(n, k, e):
-    """True when the MXFP4 and the bf16 layer take the same GEMM kernels (then
-    the results are the same bits): both the matrix-vector kernel (at most 128
-    tokens, n * k <= 1.5 E for MXFP4 and <= 3 E for bf16), or both the one-wave /
+    """True when the MXFP4 and the bf16 layer take the same kernel for each of
+    the two GEMMs (then the results are the same bits): both the matrix-vector
+    kernel (at most 128 tokens and few rows an expert: w13 n * k <= 1.5 E for
+    MXFP4 and <= 3 E for bf16, w2 <= 3 E and <= 5 E), or both the one-wave /
     32-row MFMA tiles (n * k < 48 E, outside the matrix-vector range)."""
     m = n * k
-    gv_mx, gv_16 = n <= 128 and 2 * m <= 3 * e, n <= 128 and m <= 3 * e
+
+    def same(gv_mx, gv_16):
+        return (gv_mx and gv_16) or (not gv_mx and not gv_16 and m < 48 * e)
+
+    small = n <= 128
     # (at k > 1 and m <= E the bf16 layer folds the combine into its w2 kernel
     # and the MXFP4 layer does not: the fused kernel is built to give the same
     # bits, which this comparison then checks)
-    return (gv_mx and gv_16) or (not gv_mx and not gv_16 and m < 48 * e)
+    return (same(small and 2 * m <= 3 * e, small and m <= 3 * e)
+            and same(small and m <= 3 * e, small and m <= 5 * e))
 
 
 @pytest.mark.parametrize("case", MX, ids=[c[0] for c in MX])
