@@ -300,11 +300,12 @@ moe_status_t moe_quantize_mxfp4(const void *w, moe_dtype_t dtype, int32_t n_expe
  *   (dtype MOE_BF16, else MOE_ERR_UNSUPPORTED); hidden and inter multiples of
  *   32.  Each weight is its code's value times its block's scale, exactly
  *   representable in bf16, so the result is that of moe_experts on the
- *   dequantised bf16 weights (bit-identical when both take the same GEMM
- *   kernels: decode-sized batches with N * topk <= 1.5 E take the matrix-vector
- *   kernels in both, and the 32-row / one-wave tiles are shared below 48 rows
- *   an expert; the 128-row MXFP4 tiles differ from the bf16 ones).  Workspace
- *   and other arguments as moe_experts / moe_forward. */
+ *   dequantised bf16 weights (bit-identical when both take the same kernel for
+ *   each GEMM: at most 128 tokens with N * topk <= 1.5 E take the
+ *   matrix-vector kernels in both, and past the bf16 layer's matrix-vector
+ *   range (3 E for w13, 5 E for w2) the 32-row / one-wave tiles are shared
+ *   below 48 rows an expert; the 128-row MXFP4 tiles differ from the bf16
+ *   ones).  Workspace and other arguments as moe_experts / moe_forward. */
 moe_status_t moe_experts_mxfp4(const void *x, moe_dtype_t dtype, int64_t n_tokens,
                                int32_t hidden, const void *w13_q, const void *w13_s,
                                const void *w2_q, const void *w2_s, int32_t n_experts,
