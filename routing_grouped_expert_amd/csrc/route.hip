@@ -726,40 +726,65 @@ __global__ __launch_bounds__(THREADS) void route_fused(
   }
 }
 
+// Router GEMM of one token: a wave per expert row computes logits[e] =
+// sum_h x[h] w[e][h] in fp32 -- each lane its 16-byte pieces h in
+// [V (lane + 64 t), V (lane + 64 t + 1)), multiply-adds in element order, then
+// a butterfly sum over the wave -- rounded once.  The logits go straight to the
+// routing kernel, with no partial sums in between.
+constexpr int kGateGemvWaves = 4;
+template <typename T>
+__global__ __launch_bounds__(64 * kGateGemvWaves) void gate_gemv(const T *__restrict__ x,
+                                                                 const T *__restrict__ wg, int H,
+                                                                 int E, T *__restrict__ logits) {
+  constexpr int V = 16 / (int)sizeof(T);  // values a 16-byte piece
+  constexpr int PW = 4 / (int)sizeof(T);  // values a dword
+  const int lane = threadIdx.x & 63;
+  const int e = (int)blockIdx.x * kGateGemvWaves + (int)(threadIdx.x >> 6);
+  if (e >= E) return;  // whole waves
+  const int npc = H / V;  // pieces of a row (H a multiple of 8)
+  const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(x);
+  const u32x4_t *wr = reinterpret_cast<const u32x4_t *>(wg + (size_t)e * H);
+  float acc = 0.f;
+  for (int c = lane; c < npc; c += 64) {
+    const u32x4_t a = xr[c], b = wr[c];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const uint32_t sh = 32 / PW * (i % PW);
+      float xa, wb;
+      if constexpr (sizeof(T) == 2) {
+        xa = __uint_as_float(((a[i / PW] >> sh) & 0xffffu) << 16);
+        wb = __uint_as_float(((b[i / PW] >> sh) & 0xffffu) << 16);
+      } else {
+        xa = __uint_as_float(a[i]);
+        wb = __uint_as_float(b[i]);
+      }
+      acc = fmaf(xa, wb, acc);
+    }
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+  if (lane == 0) logits[e] = from_f32<T>(acc);
+}
+
 // One token: a single wave runs the whole routing step in registers, with no
 // workgroup barrier.  Lane l holds the 16-byte logit chunk of experts
 // [l V, l V + V); k rounds of a wave-wide key maximum select the experts (the
 // keys and tie rule of topk_chunk, so the same choices), and the softmax adds
 // up the same terms in the same slot order.  With at most one entry per expert,
 // an entry's sorted position and every offset are prefix popcounts of the
-// selected-expert mask, whose bitmatrix word w lane w holds.  SUM: the logits
-// are first added up from the router GEMM's K-group sums (in group order, as
-// gate_reduce), stored, and read back from LDS.
-template <typename T, bool SUM>
+// selected-expert mask, whose bitmatrix word w lane w holds.
+template <typename T>
 __global__ __launch_bounds__(64) void route_one(
     const T *logits, int E, int K, int lo, int nl, int vec, int32_t *__restrict__ topk_idx,
     T *__restrict__ topk_w, uint32_t *__restrict__ bitmatrix, int32_t *__restrict__ col_sum,
     int32_t *__restrict__ offsets, int32_t *__restrict__ col_sorted,
-    int32_t *__restrict__ row_sorted, T *__restrict__ gate_scal,
-    const float *__restrict__ part = nullptr, int nparts = 0, T *logits_out = nullptr) {
+    int32_t *__restrict__ row_sorted, T *__restrict__ gate_scal) {
   using Lg = Logit<T>;
   using Key = typename Lg::Key;
   constexpr int V = Lg::kVec;
   const int lane = threadIdx.x, e0 = lane * V;
   u32x4_t raw = {0u, 0u, 0u, 0u};
-  if constexpr (SUM) {
-    __shared__ __align__(16) T s_lg[kMaxExperts];
-    for (int e = lane; e < E; e += 64) {
-      const T v = from_f32<T>(gate_group_sum(part, e, E, nparts));
-      logits_out[e] = v;
-      s_lg[e] = v;
-    }
-    __syncthreads();
-    // chunks end within the kMaxExperts entries; values past E are masked below
-    if (e0 < E) raw = *reinterpret_cast<const u32x4_t *>(s_lg + e0);
-  } else {
-    if (e0 < E) raw = fetch16(logits, e0, E, vec != 0);
-  }
+  if (e0 < E) raw = fetch16(logits, e0, E, vec != 0);
   Key key[V];
   Lg::decode(raw, e0, E, key);
   int my_e = -1;  // lane j: slot j's expert and logit
@@ -1022,6 +1047,18 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
   T *gs = reinterpret_cast<T *>(r->gate_scal);
   T *lw = const_cast<T *>(logits);
   const int gate_nsl = x ? gate_parts(E, H * (int)sizeof(T)) : 0;
+  if (x && N == 1) {
+    // one token: the router GEMM as a wave per expert row, then the one-wave
+    // routing kernel on its logits
+    hipLaunchKernelGGL(gate_gemv<T>, dim3((unsigned)((E + kGateGemvWaves - 1) / kGateGemvWaves)),
+                       dim3(64 * kGateGemvWaves), 0, s, x, wg, H, E, lw);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((route_one<T>), dim3(1), dim3(64), 0, s, logits, E, K, lo, nl, vec,
+                       r->topk_idx, tw, r->bitmatrix, r->col_sum, r->offsets, r->col_sorted,
+                       r->row_sorted, gs);
+    return hipGetLastError();
+  }
   if (x && gate_split(N, gate_nsl)) {
     // split-K router GEMM into the scratch; the sums are added up by gate_reduce
     // or, for a small batch, in the routing kernel's prologue
@@ -1042,12 +1079,6 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t ne = N * E;
-    if (N == 1 && ne * np * 4 <= kGateSumInlineBytes) {
-      hipLaunchKernelGGL((route_one<T, true>), dim3(1), dim3(64), 0, s, logits, E, K, lo, nl, vec,
-                         r->topk_idx, tw, r->bitmatrix, r->col_sum, r->offsets, r->col_sorted,
-                         r->row_sorted, gs, part, np, lw);
-      return hipGetLastError();
-    }
     if (N <= kSmallTokens && ne * np * 4 <= kGateSumInlineBytes) {
       hipLaunchKernelGGL((route_fused<T, 1024, 1, ChunkLds<T, kSmallTokens>, 2>), dim3(1),
                          dim3(1024), 0, s, logits, N, E, K, lo, nl, logG, vec, r->topk_idx, tw,
@@ -1110,7 +1141,7 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
   }
   if (path == kPathFused) {
     if (N == 1)
-      hipLaunchKernelGGL((route_one<T, false>), dim3(1), dim3(64), 0, s, logits, E, K, lo, nl, vec,
+      hipLaunchKernelGGL((route_one<T>), dim3(1), dim3(64), 0, s, logits, E, K, lo, nl, vec,
                          r->topk_idx, tw, r->bitmatrix, r->col_sum, r->offsets, r->col_sorted,
                          r->row_sorted, gs);
     else if (N <= kSmallTokens)  // (`wide` needs N > 64)
@@ -1158,7 +1189,7 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
 
 size_t gate_scratch_bytes(int64_t n_tokens, int n_experts, int hidden, moe_dtype_t dt) {
   const int nsl = gate_parts(n_experts, hidden * (dt == MOE_BF16 ? 2 : 4));
-  if (!gate_split(n_tokens, nsl)) return 0;
+  if (n_tokens == 1 || !gate_split(n_tokens, nsl)) return 0;  // one token: gate_gemv
   const int np = gate_groups(n_tokens, nsl);
   return align256((size_t)np * n_tokens * n_experts * 4);
 }

@@ -64,7 +64,10 @@ def _gate_case(n, e, h, k, dt, sample=None):
 
 
 GATE_CASES = [
-    (1, 128, 2880, 4, "bf16"),      # decode: router GEMM in the routing kernel's prologue
+    (1, 128, 2880, 4, "bf16"),      # decode: a wave per expert row, then the one-wave routing
+    (1, 33, 1000, 3, "f32"),        # one token, fp32, E odd, a ragged last piece per lane
+    (1, 6, 136, 2, "bf16"),         # one token, fewer experts than a workgroup's waves
+    (2, 128, 2880, 4, "bf16"),      # two tokens: split over K, sums in the routing prologue
     (33, 8, 128, 2, "f32"),         # the tiny fp32 layer's router
     (64, 32, 512, 4, "bf16"),       # largest batch of the prologue path
     (65, 32, 512, 4, "bf16"),       # first batch of the separate GEMM kernel (4 K-slices)
@@ -81,7 +84,7 @@ GATE_CASES = [
     (8, 128, 2880, 4, "bf16"),      # split-K sums past the prologue's share: reduction kernel
     (4, 32, 2880, 4, "bf16"),       # split-K sums added up in the routing kernel's prologue
     (40, 256, 4096, 8, "bf16"),     # split-K with the widest expert bucket
-    (1, 256, 7168, 8, "bf16"),      # DeepSeek-sized router, decode: 112 K-slices
+    (1, 256, 7168, 8, "bf16"),      # DeepSeek-sized router, decode (a wave per expert row)
     (64, 256, 7168, 8, "bf16"),     # the same at the largest split-K batch
     (17, 64, 1000, 6, "f32"),       # fp32 split-K through the reduction kernel
     (2000, 64, 3000, 4, "f32"),     # fp32, K-groups of 6 slices (the last 5), K tail
