@@ -744,21 +744,33 @@ __global__ __launch_bounds__(64 * kGateGemvWaves) void gate_gemv(const T *__rest
   const int npc = H / V;  // pieces of a row (H a multiple of 8)
   const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(x);
   const u32x4_t *wr = reinterpret_cast<const u32x4_t *>(wg + (size_t)e * H);
+  // the loads of kBatch pieces a lane go out before their multiply-adds
+  constexpr int kBatch = 8;
   float acc = 0.f;
-  for (int c = lane; c < npc; c += 64) {
-    const u32x4_t a = xr[c], b = wr[c];
+  for (int c0 = lane; c0 < npc; c0 += 64 * kBatch) {
+    u32x4_t a[kBatch], b[kBatch];
 #pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const uint32_t sh = 32 / PW * (i % PW);
-      float xa, wb;
-      if constexpr (sizeof(T) == 2) {
-        xa = __uint_as_float(((a[i / PW] >> sh) & 0xffffu) << 16);
-        wb = __uint_as_float(((b[i / PW] >> sh) & 0xffffu) << 16);
-      } else {
-        xa = __uint_as_float(a[i]);
-        wb = __uint_as_float(b[i]);
+    for (int u = 0; u < kBatch; ++u) {
+      const int c = c0 + 64 * u;
+      a[u] = c < npc ? xr[c] : u32x4_t{0u, 0u, 0u, 0u};
+      b[u] = c < npc ? wr[c] : u32x4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (c0 + 64 * u >= npc) break;
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const uint32_t sh = 32 / PW * (i % PW);
+        float xa, wb;
+        if constexpr (sizeof(T) == 2) {
+          xa = __uint_as_float(((a[u][i / PW] >> sh) & 0xffffu) << 16);
+          wb = __uint_as_float(((b[u][i / PW] >> sh) & 0xffffu) << 16);
+        } else {
+          xa = __uint_as_float(a[u][i]);
+          wb = __uint_as_float(b[u][i]);
+        }
+        acc = fmaf(xa, wb, acc);
       }
-      acc = fmaf(xa, wb, acc);
     }
   }
 #pragma unroll
