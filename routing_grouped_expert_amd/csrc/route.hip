@@ -32,8 +32,9 @@
 // the router's gate weight (logits = x . W_gate^T, fp32 accumulation on MFMA,
 // rounded once to the layer dtype) and written out; top-k then runs on them.
 // The router's own matmul is the step ahead of the routing that the vLLM PR
-// #45457 report leaves as a separate kernel ("motivation").  Batches of up to
-// kGateSplitTokens tokens split the product over 64-token tiles and K-groups
+// #45457 report leaves as a separate kernel ("motivation").  One token takes a
+// wave per expert row (gate_gemv).  Batches of up to kGateSplitTokens tokens
+// split the product over 64-token tiles and K-groups
 // (gate_partial, about one workgroup a compute unit) and add the fp32 group
 // sums up in the routing kernel's prologue (one token, or a few with little to
 // add) or in gate_reduce; rows too short to split and larger batches run the
