@@ -67,6 +67,8 @@ GATE_CASES = [
     (1, 128, 2880, 4, "bf16"),      # decode: a wave per expert row, then the one-wave routing
     (1, 33, 1000, 3, "f32"),        # one token, fp32, E odd, a ragged last piece per lane
     (1, 6, 136, 2, "bf16"),         # one token, fewer experts than a workgroup's waves
+    (1, 32, 2880, 4, "bf16"),       # one token, gpt-oss-20b-sized router
+    (1, 16, 1000, 2, "f32"),        # one token, fp32, a ragged last piece per lane
     (2, 128, 2880, 4, "bf16"),      # two tokens: split over K, sums in the routing prologue
     (33, 8, 128, 2, "f32"),         # the tiny fp32 layer's router
     (64, 32, 512, 4, "bf16"),       # largest batch of the prologue path
