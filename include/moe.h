@@ -210,7 +210,7 @@ moe_status_t moe_experts_weighted_input(const void *x, moe_dtype_t dtype, int64_
  *   computes from those logits goes to *out (out->w_dtype == dtype).  The same
  *   result as writing the logits and calling moe_route on them.  Workspace:
  *   moe_workspace_bytes(n_tokens, n_experts, topk, hidden, 0, dtype) (batches
- *   of 2 to 4096 tokens keep fp32 partial sums of the product over K-groups
+ *   of 5 to 4096 tokens keep fp32 partial sums of the product over K-groups
  *   there); limits as
  *   moe_route; hidden a positive multiple of 8; x, w_gate and logits_out below
  *   2^31 bytes.

@@ -32,8 +32,9 @@
 // the router's gate weight (logits = x . W_gate^T, fp32 accumulation on MFMA,
 // rounded once to the layer dtype) and written out; top-k then runs on them.
 // The router's own matmul is the step ahead of the routing that the vLLM PR
-// #45457 report leaves as a separate kernel ("motivation").  One token takes a
-// wave per expert row (gate_gemv).  Batches of up to kGateSplitTokens tokens
+// #45457 report leaves as a separate kernel ("motivation").  Up to
+// kGateGemvTokens tokens take a wave per expert row (gate_gemv).  Batches of up
+// to kGateSplitTokens tokens
 // split the product over 64-token tiles and K-groups
 // (gate_partial, about one workgroup a compute unit) and add the fp32 group
 // sums up in the routing kernel's prologue (one token, or a few with little to
@@ -727,13 +728,14 @@ __global__ __launch_bounds__(THREADS) void route_fused(
   }
 }
 
-// Router GEMM of one token: a wave per expert row computes logits[e] =
-// sum_h x[h] w[e][h] in fp32 -- each lane its 16-byte pieces h in
-// [V (lane + 64 t), V (lane + 64 t + 1)), multiply-adds in element order, then
-// a butterfly sum over the wave -- rounded once.  The logits go straight to the
-// routing kernel, with no partial sums in between.
-constexpr int kGateGemvWaves = 4;
-template <typename T>
+// Router GEMM of NT <= kGateGemvTokens tokens: a wave per expert row computes
+// logits[t][e] = sum_h x[t][h] w[e][h] in fp32 -- each lane its 16-byte pieces
+// h in [V (lane + 64 c), V (lane + 64 c + 1)), the weight piece loaded once
+// for all NT tokens, multiply-adds in element order, then a butterfly sum over
+// the wave -- rounded once.  The logits go straight to the routing kernel, with
+// no partial sums in between.
+constexpr int kGateGemvWaves = 4, kGateGemvTokens = 4;
+template <typename T, int NT>
 __global__ __launch_bounds__(64 * kGateGemvWaves) void gate_gemv(const T *__restrict__ x,
                                                                  const T *__restrict__ wg, int H,
                                                                  int E, T *__restrict__ logits) {
@@ -743,17 +745,21 @@ __global__ __launch_bounds__(64 * kGateGemvWaves) void gate_gemv(const T *__rest
   const int e = (int)blockIdx.x * kGateGemvWaves + (int)(threadIdx.x >> 6);
   if (e >= E) return;  // whole waves
   const int npc = H / V;  // pieces of a row (H a multiple of 8)
-  const u32x4_t *xr = reinterpret_cast<const u32x4_t *>(x);
   const u32x4_t *wr = reinterpret_cast<const u32x4_t *>(wg + (size_t)e * H);
   // the loads of kBatch pieces a lane go out before their multiply-adds
-  constexpr int kBatch = 8;
-  float acc = 0.f;
+  constexpr int kBatch = NT == 1 ? 8 : 4;
+  float acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = 0.f;
   for (int c0 = lane; c0 < npc; c0 += 64 * kBatch) {
-    u32x4_t a[kBatch], b[kBatch];
+    u32x4_t a[NT][kBatch], b[kBatch];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int c = c0 + 64 * u;
-      a[u] = c < npc ? xr[c] : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        a[t][u] = c < npc ? reinterpret_cast<const u32x4_t *>(x + (size_t)t * H)[c]
+                          : u32x4_t{0u, 0u, 0u, 0u};
       b[u] = c < npc ? wr[c] : u32x4_t{0u, 0u, 0u, 0u};
     }
 #pragma unroll
@@ -762,21 +768,29 @@ __global__ __launch_bounds__(64 * kGateGemvWaves) void gate_gemv(const T *__rest
 #pragma unroll
       for (int i = 0; i < V; ++i) {
         const uint32_t sh = 32 / PW * (i % PW);
-        float xa, wb;
-        if constexpr (sizeof(T) == 2) {
-          xa = __uint_as_float(((a[u][i / PW] >> sh) & 0xffffu) << 16);
+        float wb;
+        if constexpr (sizeof(T) == 2)
           wb = __uint_as_float(((b[u][i / PW] >> sh) & 0xffffu) << 16);
-        } else {
-          xa = __uint_as_float(a[u][i]);
+        else
           wb = __uint_as_float(b[u][i]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          float xa;
+          if constexpr (sizeof(T) == 2)
+            xa = __uint_as_float(((a[t][u][i / PW] >> sh) & 0xffffu) << 16);
+          else
+            xa = __uint_as_float(a[t][u][i]);
+          acc[t] = fmaf(xa, wb, acc[t]);
         }
-        acc = fmaf(xa, wb, acc);
       }
     }
   }
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (lane == 0) logits[e] = from_f32<T>(acc);
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc[t] += __shfl_xor(acc[t], m);
+    if (lane == 0) logits[(size_t)t * E + e] = from_f32<T>(acc[t]);
+  }
 }
 
 // One token: a single wave runs the whole routing step in registers, with no
@@ -1060,19 +1074,19 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
   T *gs = reinterpret_cast<T *>(r->gate_scal);
   T *lw = const_cast<T *>(logits);
   const int gate_nsl = x ? gate_parts(E, H * (int)sizeof(T)) : 0;
-  if (x && N == 1) {
-    // one token: the router GEMM as a wave per expert row, then the one-wave
-    // routing kernel on its logits
-    hipLaunchKernelGGL(gate_gemv<T>, dim3((unsigned)((E + kGateGemvWaves - 1) / kGateGemvWaves)),
-                       dim3(64 * kGateGemvWaves), 0, s, x, wg, H, E, lw);
+  if (x && N <= kGateGemvTokens) {
+    // a few tokens: the router GEMM as a wave per expert row, then the routing
+    // kernels below on its logits
+    const dim3 grid((unsigned)((E + kGateGemvWaves - 1) / kGateGemvWaves)), block(64 * kGateGemvWaves);
+    switch (N) {
+      case 1: hipLaunchKernelGGL((gate_gemv<T, 1>), grid, block, 0, s, x, wg, H, E, lw); break;
+      case 2: hipLaunchKernelGGL((gate_gemv<T, 2>), grid, block, 0, s, x, wg, H, E, lw); break;
+      case 3: hipLaunchKernelGGL((gate_gemv<T, 3>), grid, block, 0, s, x, wg, H, E, lw); break;
+      default: hipLaunchKernelGGL((gate_gemv<T, 4>), grid, block, 0, s, x, wg, H, E, lw); break;
+    }
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((route_one<T>), dim3(1), dim3(64), 0, s, logits, E, K, lo, nl, vec,
-                       r->topk_idx, tw, r->bitmatrix, r->col_sum, r->offsets, r->col_sorted,
-                       r->row_sorted, gs);
-    return hipGetLastError();
-  }
-  if (x && gate_split(N, gate_nsl)) {
+  } else if (x && gate_split(N, gate_nsl)) {
     // split-K router GEMM into the scratch; the sums are added up by gate_reduce
     // or, for a small batch, in the routing kernel's prologue
     float *part = reinterpret_cast<float *>(scratch);
@@ -1202,7 +1216,7 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
 
 size_t gate_scratch_bytes(int64_t n_tokens, int n_experts, int hidden, moe_dtype_t dt) {
   const int nsl = gate_parts(n_experts, hidden * (dt == MOE_BF16 ? 2 : 4));
-  if (n_tokens == 1 || !gate_split(n_tokens, nsl)) return 0;  // one token: gate_gemv
+  if (n_tokens <= kGateGemvTokens || !gate_split(n_tokens, nsl)) return 0;  // gate_gemv
   const int np = gate_groups(n_tokens, nsl);
   return align256((size_t)np * n_tokens * n_experts * 4);
 }

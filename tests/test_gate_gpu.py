@@ -69,7 +69,10 @@ GATE_CASES = [
     (1, 6, 136, 2, "bf16"),         # one token, fewer experts than a workgroup's waves
     (1, 32, 2880, 4, "bf16"),       # one token, gpt-oss-20b-sized router
     (1, 16, 1000, 2, "f32"),        # one token, fp32, a ragged last piece per lane
-    (2, 128, 2880, 4, "bf16"),      # two tokens: split over K, sums in the routing prologue
+    (2, 128, 2880, 4, "bf16"),      # two tokens: a wave per expert row, both tokens' logits
+    (3, 33, 1000, 3, "f32"),        # three tokens, fp32
+    (4, 256, 7168, 8, "bf16"),      # four tokens, DeepSeek-sized router
+    (5, 128, 2880, 4, "bf16"),      # five tokens: split over K, sums in the routing prologue
     (33, 8, 128, 2, "f32"),         # the tiny fp32 layer's router
     (64, 32, 512, 4, "bf16"),       # largest batch of the prologue path
     (65, 32, 512, 4, "bf16"),       # first batch of the separate GEMM kernel (4 K-slices)
@@ -81,8 +84,9 @@ GATE_CASES = [
     (4096, 128, 2880, 4, "bf16"),   # gpt-oss-sized router: 4 K-groups of 6, 6, 6 and 5 slices
     (4097, 128, 2880, 4, "bf16"),   # first batch past the split: the separate GEMM kernel
     (700, 256, 7168, 8, "bf16"),    # DeepSeek-sized router at a prefill batch (11 tiles)
-    (2, 16, 8200, 2, "bf16"),       # split-K over 65 slices: three rounds of the slice sum
-    (2, 16, 32776, 2, "bf16"),      # more K-slices (257) than the split-K path takes: full prologue
+    (2, 16, 8200, 2, "bf16"),       # two tokens, a wave per expert row over a long row
+    (5, 16, 8200, 2, "bf16"),       # split-K over 65 slices: three rounds of the group sum
+    (5, 16, 32776, 2, "bf16"),      # more K-slices (257) than the split-K path takes: full prologue
     (8, 128, 2880, 4, "bf16"),      # split-K sums past the prologue's share: reduction kernel
     (4, 32, 2880, 4, "bf16"),       # split-K sums added up in the routing kernel's prologue
     (40, 256, 4096, 8, "bf16"),     # split-K with the widest expert bucket
