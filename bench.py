@@ -5,21 +5,21 @@
 One step is one pass of the whole layer over one batch of seeded synthetic
 inputs already resident in HBM: one moe_forward call through the C ABI, which
 enqueues the routing kernels (top-k, softmax, bitmatrix, histogram, offsets,
-sorted indices), the w13 grouped GEMM with the activation and the w2 grouped
-GEMM with the routing weight and the combine.  W untimed steps, then K steps
+sorted indices), the w13 grouped GEMM with the activation, the w2 grouped GEMM
+with the routing weight, and the combine.  W untimed steps, then K steps
 between two HIP events on the launch stream give the step time.
 
-Per-stage device times come from separate timed regions on the same stream:
-K back-to-back launches of each stage (moe_route, moe_experts_w13,
-moe_experts_w2) between two events, so a stage's average includes the short
-dispatch gap between back-to-back launches of its kernels.  The w13 average
-is the dominant kernel's launch duration used for the roofline line.
-Rank 0 prints one JSON line.
+Per-kernel device times come from separate timed regions on the same stream:
+K back-to-back launches of each stage's C call (moe_route, moe_experts_w13,
+moe_experts_w2_rows -- GEMM2 alone --, moe_combine) between two events, so a
+stage's average includes the short dispatch gap between back-to-back launches.
+The stage with the longest single-kernel time is the dominant kernel of the
+roofline line.  Rank 0 prints one JSON line.
 
-The default workload is the small-model layer (8 x 512 tokens, hidden 512,
-intermediate 1408, top-1, 8 experts, SiLU-gated, bf16).  ``--workload`` picks
-another named layer for study (tiny_f32, minimind_e4/e8/e16, gptoss_n{1,33,512,4096},
-skewed_silu, skewed_relu2).
+The default workload is the largest layer: 16384 tokens, hidden 4096,
+intermediate 1536, 64 experts, top-8, Zipf-skewed router logits, SiLU-gated,
+bf16.  ``--workload`` picks another named layer (tiny_f32, minimind_e4/e8/e16,
+gptoss_n{1,33,512,4096}, skewed_silu, skewed_relu2, ...).
 """
 from __future__ import annotations
 
@@ -35,7 +35,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from routing_grouped_expert_amd import (Routing, moe_workspace_bytes,  # noqa: E402
-                                        prepare_experts_w13, prepare_experts_w2,
+                                        prepare_combine, prepare_experts_w13,
+                                        prepare_experts_w2, prepare_experts_w2_rows,
                                         prepare_forward, prepare_forward_ep,
                                         prepare_gate_forward, prepare_gate_route, prepare_route,
                                         prepare_route_ep, moe_quantize_mxfp4,
@@ -91,8 +92,13 @@ def algorithmic(spec, col_sum):
     w13_f = 2 * m * g * i * h
     w13_b = et * g * i * h * s + n * h * s + m * i * s
     w2_f = 2 * m * h * i
-    w2_b = et * h * i * s + m * i * s + m * h * s + (m * h * s + m * 4 + n * h * s if k > 1 else 0)
-    return {"route": (0, route_b), "w13": (w13_f, w13_b), "w2": (w2_f, w2_b)}, et
+    # GEMM2 writes the weighted sorted rows (k > 1) or, with one slot a token,
+    # the output rows themselves
+    w2_b = et * h * i * s + m * i * s + m * h * s
+    work = {"route": (0, route_b), "w13": (w13_f, w13_b), "w2": (w2_f, w2_b)}
+    if k > 1:  # each token's k rows read (with their positions) and its row written once
+        work["combine"] = (0, m * h * s + n * k * 4 + n * h * s)
+    return work, et
 
 
 MXFP4_BYTES = 17 / 32  # bytes per weight: a 4-bit code plus a 1-byte scale per 32
@@ -121,6 +127,93 @@ def roofline(spec, flops, nbytes, ms):
     ach = nbytes / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(ach / PEAK_HBM_GBS, 4)}
+
+
+def host_info() -> dict:
+    """The host this run is on: CPU model and hardware threads, ROCm and HIP
+    versions, GPU name and compute-unit count (the same GPU model on different
+    hosts can time differently, so the record names the host)."""
+    info = {"cpu_model": None, "cpu_threads": os.cpu_count(), "rocm": None,
+            "hip_runtime": getattr(torch.version, "hip", None), "gpu": None, "gpu_cus": None}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    if torch.cuda.is_available():
+        p = torch.cuda.get_device_properties(0)
+        info["gpu"] = f"{p.name} ({getattr(p, 'gcnArchName', '?')})"
+        info["gpu_cus"] = p.multi_processor_count
+    return info
+
+
+class ClockSampler:
+    """Samples the GPU's current graphics clock (MHz) from the SMI library on a
+    background thread while the timed regions run; reports the median and range
+    of the samples (None when the SMI library is not usable here)."""
+
+    def __init__(self, period_s: float = 0.02):
+        import threading
+        self.period = period_s
+        self.samples = []
+        self.error = None
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self, smi, h):
+        vals = []
+        try:
+            m = smi.amdsmi_get_gpu_metrics_info(h)
+            cur = m.get("current_gfxclks")
+            if isinstance(cur, (list, tuple)):
+                vals = [v for v in cur if isinstance(v, (int, float)) and 0 < v < 10000]
+            elif isinstance(m.get("current_gfxclk"), (int, float)):
+                vals = [m["current_gfxclk"]]
+        except Exception:
+            vals = []
+        if not vals:
+            c = smi.amdsmi_get_clock_info(h, smi.AmdSmiClkType.GFX)
+            vals = [c["clk"]]
+        return sum(vals) / len(vals)
+
+    def _run(self):
+        try:
+            import amdsmi as smi
+            smi.amdsmi_init()
+            try:
+                hs = smi.amdsmi_get_processor_handles()
+                if len(hs) != 1:
+                    raise RuntimeError(f"{len(hs)} GPUs visible to the SMI library")
+                while not self._stop.is_set():
+                    self.samples.append(self._read(smi, hs[0]))
+                    self._stop.wait(self.period)
+            finally:
+                smi.amdsmi_shut_down()
+        except Exception as exc:  # no SMI access: the record says why
+            self.error = f"{type(exc).__name__}: {exc}"[:160]
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=5)
+
+    def summary(self) -> dict:
+        if not self.samples:
+            return {"median_mhz": None, "error": self.error or "no samples"}
+        v = sorted(self.samples)
+        return {"median_mhz": round(v[len(v) // 2]), "min_mhz": round(v[0]),
+                "max_mhz": round(v[-1]), "samples": len(v)}
 
 
 def _oracle_threads() -> int:
@@ -488,7 +581,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="minimind_e8")
+    ap.add_argument("--workload", default="skewed_silu")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
@@ -549,12 +642,18 @@ def main():
         p_route = prepare_route(lg, k, routing=routing, workspace=ws, stream=stream)
         p_fwd = prepare_forward(x, lg, w13, w2, k, spec.act, spec.layout, act_params(spec),
                                 out=out, routing=routing, workspace=ws, stream=stream)
-    # the halves run the same kernels as the full call (k > 1 for every share
-    # workload, so the combine skips the slots routed to other GPUs)
+    # the split calls run the kernels of the full call: GEMM1 + activation,
+    # GEMM2 + routing weight into sorted rows, then the combine (k > 1); with one
+    # slot a token GEMM2 writes the output rows itself
     if not mx:
         p_w13 = prepare_experts_w13(x, w13, routing, spec.act, spec.layout, act_params(spec),
                                     act_out=act, stream=stream)
-        p_w2 = prepare_experts_w2(act, w2, routing, out=out, workspace=ws, stream=stream)
+        if k > 1:
+            y_rows = torch.empty(n * k, spec.hidden, dtype=dt, device=dev)
+            p_w2 = prepare_experts_w2_rows(act, w2, routing, y_sorted=y_rows, stream=stream)
+            p_comb = prepare_combine(y_rows, routing, out=out, stream=stream)
+        else:
+            p_w2 = prepare_experts_w2(act, w2, routing, out=out, workspace=ws, stream=stream)
 
     K, W = args.steps, args.warmup
 
@@ -572,16 +671,21 @@ def main():
     for _ in range(W):
         p_fwd()
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    st = step_stats(p_fwd, K, stream)
-    wall = time.perf_counter() - t0
-    ms_step = st["mean"]
-    # stages (the routing metadata of the last step stays valid for w13 / w2)
-    stages = (("route", p_route), ("experts", p_exp)) if mx else \
-        (("route", p_route), ("w13", p_w13), ("w2", p_w2))
-    stage_ms = {name: timed(fn, K) for name, fn in stages}
-    cold_step, cold_route = cold_stats([p_fwd, p_route], 20, stream, dev)
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        st = step_stats(p_fwd, K, stream)
+        wall = time.perf_counter() - t0
+        ms_step = st["mean"]
+        # stages (the routing metadata of the last step stays valid for the others)
+        stages = [("route", p_route)]
+        stages += [("experts", p_exp)] if mx else [("w13", p_w13), ("w2", p_w2)]
+        if not mx and k > 1:
+            stages.append(("combine", p_comb))
+        stage_ms = {name: timed(fn, K) for name, fn in stages}
+    cold_fns = [p_fwd, p_route] + ([p_comb] if not mx and k > 1 else [])
+    cold = cold_stats(cold_fns, 20, stream, dev)
     col_sum = routing.col_sum.cpu()
+    stage_roof = {}
     if mx:
         # MXFP4 workloads: both grouped GEMMs of one experts call, weight bytes
         # at 17/32 byte a weight
@@ -593,16 +697,29 @@ def main():
                      "avg_launch_us": round(stage_ms["experts"] * 1e3, 2)})
     else:
         work, et = algorithmic(spec, col_sum)
-        # the w13 grouped GEMM is one kernel and the largest of the layer (it
-        # has n_sets x the flops of the w2 GEMM); its back-to-back launches are
-        # timed
-        dom = "w13"
+        for name in stage_ms:
+            sf, sb = work[name]
+            r = roofline(spec, sf, sb, stage_ms[name])
+            stage_roof[name] = {"bound": r["bound"], "frac": r["frac"], "achieved": r["achieved"],
+                                "unit": r["unit"]}
+        # the dominant kernel: the longest of the single-kernel stages
+        dom = max(("w13", "w2", "combine"), key=lambda s_: stage_ms.get(s_, -1.0))
         f, b = work[dom]
+        label = {"w13": f"{expert_kernel(spec, False)} (w13 + activation)",
+                 "w2": f"{expert_kernel(spec, False)} (w2 + routing weight"
+                       f"{' into sorted rows' if k > 1 else ', to the output rows'})",
+                 "combine": "combine_kernel (scatter-combine)"}[dom]
         roof = roofline(spec, f, b, stage_ms[dom])
-        roof.update({"kernel": f"{expert_kernel(spec, False)} (w13 + activation)",
+        roof.update({"kernel": label, "stage": dom,
                      "traffic": stored_traffic(spec.name, dom),
                      "algorithmic_bytes": b, "algorithmic_flops": f,
                      "avg_launch_us": round(stage_ms[dom] * 1e3, 2)})
+    cold_us = {"step": round(cold[0] * 1e3, 2), "route": round(cold[1] * 1e3, 2)}
+    if len(cold) > 2:
+        cold_us["combine"] = round(cold[2] * 1e3, 2)
+        cb = work["combine"][1]
+        cold_us["combine_gbs"] = round(cb / (cold[2] * 1e-3) / 1e9, 1)
+        cold_us["combine_warm_gbs"] = round(cb / (stage_ms["combine"] * 1e-3) / 1e9, 1)
     result = {
         "metric": METRIC,
         "value": round(n / (ms_step * 1e-3), 1),
@@ -620,10 +737,13 @@ def main():
         "config": {"workload": f"{spec.name}: {describe(spec)}", "n_tokens": n,
                    "experts_touched": et, "max_expert_rows": int(col_sum.max())},
         "routing_us_per_layer": round(stage_ms["route"] * 1e3, 2),
-        "stage_us": {s: round(v * 1e3, 2) for s, v in stage_ms.items()},
-        "cold_us": {"step": round(cold_step * 1e3, 2), "route": round(cold_route * 1e3, 2)},
+        "stage_us": {s_: round(v * 1e3, 2) for s_, v in stage_ms.items()},
+        "stage_roofline": stage_roof,
+        "cold_us": cold_us,
         "wall_ms_per_step": round(wall / K * 1e3, 4),
         "roofline": roof,
+        "gpu_clock": clock.summary(),
+        "host": host_info(),
     }
     if not args.no_cpu_baseline and not mx:
         result["cpu_baseline"] = cpu_baseline(spec, layer, args.cpu_seconds)

@@ -15,7 +15,8 @@
  *
  * moe_experts is also exported as its two halves, moe_experts_w13 (grouped
  * GEMM with w13 + activation) and moe_experts_w2 (grouped GEMM with w2 +
- * routing weight + combine).
+ * routing weight + combine), and the latter as moe_experts_w2_rows (GEMM2 +
+ * routing weight into sorted rows) and moe_combine (the scatter-combine).
  *
  * Sources of the operations (the pages are cited by title and section):
  *  - top-k over the router logits with softmax over the selected values, and the
@@ -83,7 +84,11 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
  *   MOE_ACT_SILU:       a = g' * sigmoid(g') * u'            (uses limit only)
  *   MOE_ACT_SWIGLU_OAI: a = g' * sigmoid(alpha*g') * (u' + beta)
  *     with g' = min(g, limit) and u' = clamp(u, -limit, limit);
- *   MOE_ACT_RELU2:      a = max(h, 0)^2, non-gated (w13 has inter rows), no params. */
+ *   MOE_ACT_RELU2:      a = max(h, 0)^2, non-gated (w13 has inter rows), no params.
+ * The SwiGLU-OAI formula is a reading: the PR #47106 report names only its
+ * parameters alpha, beta and limit (with the 1.702 / 1.0 / 7.0 values) and
+ * prints no formula; this is the public gpt-oss definition, which no passage of
+ * the pages pins (only its reduction to SiLU-gated with the parameters unset). */
 typedef enum { MOE_ACT_SILU = 0, MOE_ACT_SWIGLU_OAI = 1, MOE_ACT_RELU2 = 2 } moe_act_t;
 
 /* Row order of a gated w13 [E, 2*inter, hidden]:
@@ -171,6 +176,32 @@ moe_status_t moe_experts_w2(const void *act_in, moe_dtype_t dtype, int64_t n_tok
                             int32_t hidden, const void *w2, int32_t n_experts, int32_t inter,
                             int32_t topk, const moe_routing_t *routing, void *out,
                             void *workspace, size_t ws_bytes, void *stream);
+
+/* moe_experts_w2 split further into its two kernels, GEMM2 and the combine
+ * (the weighted expert outputs and the index_add_-style sum back into token
+ * rows of the minimind issue #835 page, "Summary"), for callers that time or
+ * overlap them separately.  moe_experts_w2 gives the same bits as the two in
+ * sequence for any topk.
+ *
+ * moe_experts_w2_rows: y_sorted [N*topk, hidden] in `dtype`; row p receives
+ *   gate_scal[p] * (W2[e] act_in[p]), accumulated in fp32 and rounded once
+ *   (nearest-even), for the routed rows p < offsets[n_experts]; rows past it
+ *   (an expert share's unrouted positions) are not written.  Reads
+ *   routing->offsets, col_sorted, gate_scal.  n_experts may be smaller than
+ *   topk (an expert share).  Needs no workspace.
+ * moe_combine: out [N, hidden] in `dtype`; out[t] = sum over j < topk of
+ *   y_sorted[row_sorted[t*topk + j]], in slot order with fp32 accumulation and
+ *   one rounding; slots with row_sorted = -1 add nothing (a token with none
+ *   gets a zero row).  Reads routing->row_sorted only; deterministic, no
+ *   atomics.  Limits: 1 <= topk <= 16, n_tokens * topk < 2^31, hidden a
+ *   positive multiple of 8. */
+moe_status_t moe_experts_w2_rows(const void *act_in, moe_dtype_t dtype, int64_t n_tokens,
+                                 int32_t hidden, const void *w2, int32_t n_experts, int32_t inter,
+                                 int32_t topk, const moe_routing_t *routing, void *y_sorted,
+                                 void *stream);
+moe_status_t moe_combine(const void *y_sorted, moe_dtype_t dtype, int64_t n_tokens,
+                         int32_t hidden, int32_t topk, const moe_routing_t *routing, void *out,
+                         void *stream);
 
 /* moe_route on `logits` (dtype `dtype`) into *routing_out, then moe_experts. */
 moe_status_t moe_forward(const void *x, const void *logits, moe_dtype_t dtype,

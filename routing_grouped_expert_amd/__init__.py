@@ -36,7 +36,8 @@ import torch
 from . import _native as N
 
 __all__ = ["Routing", "MoeError", "Prepared", "moe_route", "moe_experts", "moe_experts_w13",
-           "moe_experts_w2", "moe_forward", "prepare_route", "prepare_experts",
+           "moe_experts_w2", "moe_experts_w2_rows", "moe_combine", "prepare_experts_w2_rows",
+           "prepare_combine", "moe_forward", "prepare_route", "prepare_experts",
            "prepare_experts_w13", "prepare_experts_w2", "prepare_forward",
            "moe_route_ep", "moe_experts_ep", "moe_forward_ep", "prepare_route_ep",
            "prepare_experts_ep", "prepare_forward_ep", "moe_gate_route", "moe_gate_forward",
@@ -373,6 +374,60 @@ def moe_experts_w2(act_in: torch.Tensor, w2: torch.Tensor, routing: Routing, *,
     """Grouped GEMM with w2 + routing weight + combine into ``out [N, hidden]``."""
     return prepare_experts_w2(act_in, w2, routing, out=out, workspace=workspace,
                               stream=stream)()
+
+
+def prepare_experts_w2_rows(act_in, w2, routing: Routing, *, y_sorted=None,
+                            stream=None) -> Prepared:
+    dev = _dev(act_in, w2)
+    e, hidden, inter = w2.shape
+    k = routing.topk
+    n = routing.topk_idx.shape[0]
+    if tuple(act_in.shape) != (n * k, inter) or act_in.dtype != w2.dtype:
+        raise ValueError("act_in must be [N*k, inter] in the layer dtype")
+    _check_routing(routing, n, e, k)
+    if y_sorted is None:
+        y_sorted = torch.empty(n * k, hidden, dtype=w2.dtype, device=dev)
+    if tuple(y_sorted.shape) != (n * k, hidden) or y_sorted.dtype != w2.dtype:
+        raise ValueError("y_sorted must be [N*k, hidden] in the layer dtype")
+    _dev(act_in, y_sorted)
+    r = routing.as_c()
+    args = (act_in.data_ptr(), _dt(act_in), n, hidden, w2.data_ptr(), e, inter, k,
+            ctypes.byref(r), y_sorted.data_ptr(), _stream(dev, stream))
+    return Prepared("moe_experts_w2_rows", args, (r, act_in, w2, y_sorted, routing), y_sorted)
+
+
+def moe_experts_w2_rows(act_in: torch.Tensor, w2: torch.Tensor, routing: Routing, *,
+                        y_sorted: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Grouped GEMM with w2 + routing weight into the sorted rows ``[N*k, hidden]``
+    (no combine); rows past the routed ones are left as they were."""
+    return prepare_experts_w2_rows(act_in, w2, routing, y_sorted=y_sorted, stream=stream)()
+
+
+def prepare_combine(y_sorted, routing: Routing, *, out=None, stream=None) -> Prepared:
+    dev = _dev(y_sorted)
+    n, k = routing.topk_idx.shape
+    if y_sorted.dim() != 2 or y_sorted.shape[0] != n * k:
+        raise ValueError("y_sorted must be [N*k, hidden]")
+    hidden = y_sorted.shape[1]
+    rs = routing.row_sorted
+    if tuple(rs.shape) != (n * k,) or rs.dtype != torch.int32 or not rs.is_contiguous():
+        raise ValueError("routing.row_sorted must be contiguous int32 [N*k]")
+    if out is None:
+        out = torch.empty(n, hidden, dtype=y_sorted.dtype, device=dev)
+    if tuple(out.shape) != (n, hidden) or out.dtype != y_sorted.dtype:
+        raise ValueError("out must be [N, hidden] in the dtype of y_sorted")
+    _dev(y_sorted, out, rs)
+    r = routing.as_c()
+    args = (y_sorted.data_ptr(), _dt(y_sorted), n, hidden, k, ctypes.byref(r), out.data_ptr(),
+            _stream(dev, stream))
+    return Prepared("moe_combine", args, (r, y_sorted, out, routing), out)
+
+
+def moe_combine(y_sorted: torch.Tensor, routing: Routing, *, out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """Scatter-combine ``out[t] = sum_j y_sorted[row_sorted[t*k + j]]`` (slot order,
+    fp32 sum, one rounding; slots with row_sorted = -1 skipped)."""
+    return prepare_combine(y_sorted, routing, out=out, stream=stream)()
 
 
 def prepare_forward(x, logits, w13, w2, topk: int, act: str, layout: str = "packed",

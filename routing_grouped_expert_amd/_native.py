@@ -42,6 +42,9 @@ SIGNATURES = {
                                 c_i32, _P_PARAMS, _P_ROUTING, c_vp, c_vp]),
     "moe_experts_w2": (c_i32, [c_vp, c_i32, c_i64, c_i32, c_vp, c_i32, c_i32, c_i32, _P_ROUTING,
                                c_vp, c_vp, c_sz, c_vp]),
+    "moe_experts_w2_rows": (c_i32, [c_vp, c_i32, c_i64, c_i32, c_vp, c_i32, c_i32, c_i32,
+                                    _P_ROUTING, c_vp, c_vp]),
+    "moe_combine": (c_i32, [c_vp, c_i32, c_i64, c_i32, c_i32, _P_ROUTING, c_vp, c_vp]),
     "moe_forward": (c_i32, [c_vp, c_vp, c_i32, c_i64, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32,
                             c_i32, c_i32, _P_PARAMS, _P_ROUTING, c_vp, c_vp, c_sz, c_vp]),
     "moe_route_ep": (c_i32, [c_vp, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, _P_ROUTING, c_vp,

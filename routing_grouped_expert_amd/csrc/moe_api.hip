@@ -15,6 +15,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 inline bool dtype_ok(int d) { return d == MOE_F32 || d == MOE_BF16; }
 inline size_t dsize(int d) { return d == MOE_BF16 ? 2 : 4; }
+// moe_combine sees no expert count: the size check takes the largest one
+constexpr int32_t kCombineAnyExperts = moe::kMaxExperts;
 
 // Sizes shared by all entry points.  An expert-parallel share may hold fewer
 // experts than a token selects (k_le_e = false for its expert count).
@@ -289,6 +291,41 @@ moe_status_t moe_experts_w2(const void *act_in, moe_dtype_t dtype, int64_t n_tok
     return st;
   return run_w2(act_in, dtype, n_tokens, hidden, w2, n_experts, inter, topk, routing, out,
                 workspace, (hipStream_t)stream) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+moe_status_t moe_experts_w2_rows(const void *act_in, moe_dtype_t dtype, int64_t n_tokens,
+                                 int32_t hidden, const void *w2, int32_t n_experts, int32_t inter,
+                                 int32_t topk, const moe_routing_t *routing, void *y_sorted,
+                                 void *stream) {
+  ActParams prm;
+  moe_status_t st = check_expert_args(dtype, n_tokens, hidden, n_experts, inter, topk,
+                                      MOE_ACT_SILU, MOE_W13_PACKED, nullptr, routing, &prm, true);
+  if (st != MOE_OK || n_tokens == 0) return st;
+  if ((st = check_ptrs({act_in, w2, y_sorted})) != MOE_OK) return st;
+  return moe::launch_gemm2(act_in, w2, y_sorted, routing->offsets, routing->col_sorted,
+                           routing->gate_scal, (moe_dtype_t)routing->w_dtype, dtype, n_tokens,
+                           topk, n_experts, hidden, inter, false, (hipStream_t)stream) ==
+                 hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
+moe_status_t moe_combine(const void *y_sorted, moe_dtype_t dtype, int64_t n_tokens,
+                         int32_t hidden, int32_t topk, const moe_routing_t *routing, void *out,
+                         void *stream) {
+  moe_status_t st = check_sizes(n_tokens, kCombineAnyExperts, topk, false);
+  if (st != MOE_OK) return st;
+  if (check_ffn_sizes(hidden, 8) != MOE_OK) return MOE_ERR_SHAPE;
+  if (!dtype_ok(dtype)) return MOE_ERR_DTYPE;
+  // one thread per 16-byte chunk of out: the grid must stay below 2^31 workgroups of 256
+  if (n_tokens * hidden * (int64_t)dsize(dtype) / 16 > 0x7fffffffLL * 256) return MOE_ERR_SHAPE;
+  if (!routing) return MOE_ERR_NULL;
+  if (n_tokens == 0) return MOE_OK;
+  if ((st = check_ptrs({y_sorted, routing->row_sorted, out})) != MOE_OK) return st;
+  return moe::launch_combine(y_sorted, routing->row_sorted, out, dtype, n_tokens, topk, hidden,
+                             (hipStream_t)stream) == hipSuccess
              ? MOE_OK
              : MOE_ERR_HIP;
 }

@@ -172,6 +172,37 @@ def test_half_entry_points_argument_checks(lib):
     assert w2(wsb=64) == N.MOE_ERR_WORKSPACE
 
 
+def test_w2_rows_and_combine_argument_checks(lib):
+    r = routing()
+    rows = lambda **kw: lib.moe_experts_w2_rows(
+        kw.get("a", FAKE), kw.get("dt", N.MOE_BF16), kw.get("n", 33), kw.get("h", 128), FAKE,
+        kw.get("e", 8), 256, kw.get("k", 2), ctypes.byref(kw.get("r", r)), kw.get("y", FAKE),
+        None)
+    assert rows(n=0, a=None, y=None) == N.MOE_OK
+    assert rows(a=None) == N.MOE_ERR_NULL
+    assert rows(y=None) == N.MOE_ERR_NULL
+    assert rows(y=MISALIGNED) == N.MOE_ERR_ALIGN
+    assert rows(r=routing({"gate_scal": None})) == N.MOE_ERR_NULL
+    assert rows(h=100) == N.MOE_ERR_SHAPE
+    assert rows(k=17) == N.MOE_ERR_SHAPE
+    assert rows(dt=3) == N.MOE_ERR_DTYPE
+    comb = lambda **kw: lib.moe_combine(
+        kw.get("y", FAKE), kw.get("dt", N.MOE_BF16), kw.get("n", 33), kw.get("h", 128),
+        kw.get("k", 2), kw.get("rp", ctypes.byref(kw.get("r", r))), kw.get("out", FAKE), None)
+    assert comb(n=0, y=None, out=None) == N.MOE_OK
+    assert comb(y=None) == N.MOE_ERR_NULL
+    assert comb(out=None) == N.MOE_ERR_NULL
+    assert comb(rp=None) == N.MOE_ERR_NULL
+    assert comb(r=routing({"row_sorted": None})) == N.MOE_ERR_NULL
+    assert comb(r=routing({"row_sorted": MISALIGNED})) == N.MOE_ERR_ALIGN
+    assert comb(out=MISALIGNED) == N.MOE_ERR_ALIGN
+    assert comb(h=12) == N.MOE_ERR_SHAPE
+    assert comb(k=0) == N.MOE_ERR_SHAPE
+    assert comb(k=17) == N.MOE_ERR_SHAPE
+    assert comb(n=1 << 30, k=4) == N.MOE_ERR_SHAPE
+    assert comb(dt=4) == N.MOE_ERR_DTYPE
+
+
 def test_share_entry_points_argument_checks(lib):
     r = routing()
 

@@ -1,7 +1,6 @@
 """GPU expert-parallel share (moe_route_ep / moe_experts_ep / moe_forward_ep)
 against the CPU oracle (route_ep, moe_ffn_share): routing metadata bit-exact,
 layer contributions within the layer tolerance, shares summing to the layer."""
-import numpy as np
 import pytest
 import torch
 
@@ -85,7 +84,7 @@ def _share_spec(family, lo, nl, **kw):
     return base.with_(local_offset=lo, n_local=nl, name=f"{base.name}_s{lo}x{nl}")
 
 
-def run_share(spec, sample=None):
+def run_share(spec):
     print(f"[ep-moe] {spec}", flush=True)
     layer = make_layer(spec)
     lo, nl = spec.local_offset, spec.n_local
@@ -95,16 +94,9 @@ def run_share(spec, sample=None):
     torch.cuda.synchronize()
     ref_r = oracle.route_ep(layer.logits, spec.topk, spec.dtype, lo, nl)
     assert_routing_equal(routing, ref_r, f"{spec.name}.routing")
-    toks = None
-    if sample is not None:
-        rng = np.random.default_rng(0)
-        none_local = np.flatnonzero((ref_r.row_sorted.reshape(spec.n_tokens, -1) < 0).all(axis=1))
-        toks = np.unique(np.concatenate([rng.choice(spec.n_tokens, sample, replace=False),
-                                         none_local[:4], [0, spec.n_tokens - 1]]))
     ref = oracle.moe_ffn_share(layer.x, ref_r.topk_idx, ref_r.topk_w, layer.w13, layer.w2,
-                               spec.act, lo, spec.layout, act_params(spec), tokens=toks)
-    got = out if toks is None else out[torch.from_numpy(toks).to(DEV)]
-    stats = assert_output_close(got, ref, spec.name)
+                               spec.act, lo, spec.layout, act_params(spec))
+    stats = assert_output_close(out, ref, spec.name)
     print(f"[ep-moe] {spec.name}: {stats}", flush=True)
     # tokens with no slot in the share get exact zero rows
     none_local = (ref_r.row_sorted.reshape(spec.n_tokens, -1) < 0).all(axis=1)
@@ -137,7 +129,7 @@ def test_share_layer(case):
 @pytest.mark.timeout(600)
 def test_gptoss_ep8_share_full_size():
     # one GPU of an EP8 group over gpt-oss-sized experts: 16 of 128 experts
-    run_share(_share_spec("gptoss", 0, 16, n_tokens=4096), sample=48)
+    run_share(_share_spec("gptoss", 0, 16, n_tokens=4096))
 
 
 @pytest.mark.parametrize("k,dt", [(2, "bf16"), (1, "f32"), (4, "f32")])

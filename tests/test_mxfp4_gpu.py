@@ -150,15 +150,9 @@ def test_mxfp4_gptoss(n):
     torch.cuda.synchronize()
     ref_r = oracle.route(layer.logits, spec.topk, "bf16")
     assert_routing_equal(routing, ref_r, "gptoss mxfp4 routing")
-    toks = None
-    if n > 33:
-        toks = np.unique(np.concatenate([np.random.default_rng(0).choice(n, 24, replace=False),
-                                         [0, n - 1]]))
     ref = oracle.moe_ffn(layer.x, ref_r.topk_idx, ref_r.topk_w, _Dequantised(w[0], w[1]),
-                         _Dequantised(w[2], w[3]), spec.act, spec.layout, act_params(spec),
-                         tokens=toks)
-    got = out if toks is None else out[torch.from_numpy(toks).to(DEV)]
-    print(f"[mxfp4] gptoss n={n}: {assert_output_close(got, ref, spec.name)}", flush=True)
+                         _Dequantised(w[2], w[3]), spec.act, spec.layout, act_params(spec))
+    print(f"[mxfp4] gptoss n={n}: {assert_output_close(out, ref, spec.name)}", flush=True)
 
 
 def test_mxfp4_argument_checks():
