@@ -49,14 +49,12 @@ def assert_logits_close(gpu: torch.Tensor, x: torch.Tensor, w: torch.Tensor, dt:
     return {"differs_from_oracle_rounding": int((g != ref).sum()), "n": int(g.size)}
 
 
-def _gate_case(n, e, h, k, dt, sample=None):
+def _gate_case(n, e, h, k, dt):
     print(f"[gate] N={n} E={e} H={h} k={k} {dt}", flush=True)
     x, w = router_inputs(n, e, h, dt, seed=n + 7 * e + h)
     lg, routing = moe_gate_route(x.to(DEV), w.to(DEV), k)
     torch.cuda.synchronize()
-    rows = None if sample is None else np.unique(np.concatenate(
-        [np.random.default_rng(0).choice(n, sample, replace=False), [0, n - 1]]))
-    stats = assert_logits_close(lg, x, w, dt, rows, f"logits N={n} E={e} H={h}")
+    stats = assert_logits_close(lg, x, w, dt, None, f"logits N={n} E={e} H={h}")
     ref = oracle.route(lg.cpu(), k, dt)
     assert_routing_equal(routing, ref, f"gate-routing N={n} E={e}")
     print(f"[gate] {stats}", flush=True)
@@ -106,7 +104,7 @@ def test_gate_route(n, e, h, k, dt):
 
 @pytest.mark.timeout(600)
 def test_gate_route_largest_batch():
-    _gate_case(65536, 128, 2880, 4, "bf16", sample=512)
+    _gate_case(65536, 128, 2880, 4, "bf16")
 
 
 # batches that take the 64-token tile (at least 64 tokens per compute unit, fewer
@@ -114,7 +112,7 @@ def test_gate_route_largest_batch():
 @pytest.mark.parametrize("n,e,h,k,dt", [(20000, 64, 512, 8, "bf16"), (17000, 33, 264, 3, "f32"),
                                         (16000, 128, 1024, 4, "bf16")])
 def test_gate_route_mid_batches(n, e, h, k, dt):
-    _gate_case(n, e, h, k, dt, sample=512)
+    _gate_case(n, e, h, k, dt)
 
 
 def test_gate_route_equals_route_on_its_logits():
