@@ -75,7 +75,8 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = -4, /* unsupported (activation, layout) combination    */
   MOE_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned                */
   MOE_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required         */
-  MOE_ERR_HIP = -7          /* a HIP launch failed                             */
+  MOE_ERR_HIP = -7,         /* a HIP launch failed                             */
+  MOE_ERR_SCRATCH = -8      /* moe_forward_noalloc: sizes exceed its scratch   */
 } moe_status_t;
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype_t;
@@ -210,6 +211,33 @@ moe_status_t moe_forward(const void *x, const void *logits, moe_dtype_t dtype,
                          moe_w13_layout_t layout, const moe_act_params_t *params,
                          const moe_routing_t *routing_out, void *out, void *workspace,
                          size_t ws_bytes, void *stream);
+
+/* ---- The layer without a workspace argument -----------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * moe_forward_noalloc: moe_forward (same arguments less the workspace, same
+ *   kernels, same bits) with its intermediates -- the routing scratch, the
+ *   activation rows and the weighted expert rows -- in a static device array of
+ *   MOE_NOALLOC_SCRATCH_BYTES inside the library.  Each GPU holds its own copy
+ *   from the first call on it until the process ends; the call never allocates
+ *   or frees memory.  Sizes whose moe_workspace_bytes(n_tokens, n_experts,
+ *   topk, hidden, inter, dtype) exceed MOE_NOALLOC_SCRATCH_BYTES are rejected
+ *   with MOE_ERR_SCRATCH before anything is enqueued (64 MiB: e.g. up to 1456
+ *   tokens of a top-4, 2880-wide gpt-oss-shaped layer).
+ *   Every call on one GPU uses that GPU's one array: calls that overlap on a
+ *   GPU (two streams, two threads) race and give wrong results; serialise them.
+ *   Nothing in the array needs to start at zero, so a call never depends on
+ *   what an earlier call left there.  The first call on a GPU resolves the
+ *   array's address (a runtime symbol lookup, not a stream operation); make it
+ *   before capturing a graph that contains the call. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status_t moe_forward_noalloc(const void *x, const void *logits, moe_dtype_t dtype,
+                                 int64_t n_tokens, int32_t hidden, const void *w13,
+                                 const void *w2, int32_t n_experts, int32_t inter, int32_t topk,
+                                 moe_act_t act, moe_w13_layout_t layout,
+                                 const moe_act_params_t *params, const moe_routing_t *routing_out,
+                                 void *out, void *stream);
 
 /* ---- Routing weight on the input rows ---------------------------------------
  * moe_experts_weighted_input: the experts apply() of the vLLM PR #47106 report

@@ -37,7 +37,8 @@ from . import _native as N
 
 __all__ = ["Routing", "MoeError", "Prepared", "moe_route", "moe_experts", "moe_experts_w13",
            "moe_experts_w2", "moe_experts_w2_rows", "moe_combine", "prepare_experts_w2_rows",
-           "prepare_combine", "moe_forward", "prepare_route", "prepare_experts",
+           "prepare_combine", "moe_forward", "moe_forward_noalloc", "prepare_forward_noalloc",
+           "prepare_route", "prepare_experts",
            "prepare_experts_w13", "prepare_experts_w2", "prepare_forward",
            "moe_route_ep", "moe_experts_ep", "moe_forward_ep", "prepare_route_ep",
            "prepare_experts_ep", "prepare_forward_ep", "moe_gate_route", "moe_gate_forward",
@@ -452,6 +453,41 @@ def prepare_forward(x, logits, w13, w2, topk: int, act: str, layout: str = "pack
             ctypes.byref(r), out.data_ptr(), ws.data_ptr(), _nbytes(ws), _stream(dev, stream))
     return Prepared("moe_forward", args, (r, p, x, logits, w13, w2, out, ws, routing),
                     (out, routing))
+
+
+def prepare_forward_noalloc(x, logits, w13, w2, topk: int, act: str, layout: str = "packed",
+                            params: Optional[dict] = None, *, out=None, routing=None,
+                            stream=None) -> Prepared:
+    dev = _dev(x, logits, w13, w2)
+    _shapes(x, w13, w2, act, out, logits)
+    n, hidden = x.shape
+    e, inter = w2.shape[0], w2.shape[2]
+    if logits.dtype != x.dtype:
+        raise TypeError("moe_forward_noalloc takes logits in the layer dtype")
+    if routing is None:
+        routing = Routing.empty(n, e, topk, logits.dtype, dev)
+    _check_routing(routing, n, e, topk)
+    if out is None:
+        out = torch.empty_like(x)
+    r = routing.as_c()
+    p = _params(params)
+    args = (x.data_ptr(), logits.data_ptr(), _dt(x), n, hidden, w13.data_ptr(), w2.data_ptr(),
+            e, inter, topk, ACTS[act], LAYOUTS[layout], ctypes.byref(p) if p else None,
+            ctypes.byref(r), out.data_ptr(), _stream(dev, stream))
+    return Prepared("moe_forward_noalloc", args, (r, p, x, logits, w13, w2, out, routing),
+                    (out, routing))
+
+
+def moe_forward_noalloc(x: torch.Tensor, logits: torch.Tensor, w13: torch.Tensor,
+                        w2: torch.Tensor, topk: int, act: str, layout: str = "packed",
+                        params: Optional[dict] = None, *, out: Optional[torch.Tensor] = None,
+                        routing: Optional[Routing] = None, stream=None):
+    """moe_forward with no workspace argument: the intermediates live in the
+    library's static per-GPU scratch (MOE_NOALLOC_SCRATCH_BYTES).  With ``out``
+    and ``routing`` given, nothing is allocated; calls that overlap on one GPU
+    race.  Returns (out, routing)."""
+    return prepare_forward_noalloc(x, logits, w13, w2, topk, act, layout, params, out=out,
+                                   routing=routing, stream=stream)()
 
 
 def prepare_forward_ep(x, logits, w13, w2, topk: int, local_offset: int, act: str,

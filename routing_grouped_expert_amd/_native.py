@@ -12,6 +12,8 @@ c_i32, c_i64, c_u32, c_sz, c_vp, c_f = (ctypes.c_int32, ctypes.c_int64, ctypes.c
 # moe_status_t
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE = 0, -1, -2, -3
 MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE, MOE_ERR_HIP = -4, -5, -6, -7
+MOE_ERR_SCRATCH = -8
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 # moe_dtype_t, moe_act_t, moe_w13_layout_t
 MOE_F32, MOE_BF16 = 0, 1
 MOE_ACT_SILU, MOE_ACT_SWIGLU_OAI, MOE_ACT_RELU2 = 0, 1, 2
@@ -47,6 +49,8 @@ SIGNATURES = {
     "moe_combine": (c_i32, [c_vp, c_i32, c_i64, c_i32, c_i32, _P_ROUTING, c_vp, c_vp]),
     "moe_forward": (c_i32, [c_vp, c_vp, c_i32, c_i64, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32,
                             c_i32, c_i32, _P_PARAMS, _P_ROUTING, c_vp, c_vp, c_sz, c_vp]),
+    "moe_forward_noalloc": (c_i32, [c_vp, c_vp, c_i32, c_i64, c_i32, c_vp, c_vp, c_i32, c_i32,
+                                    c_i32, c_i32, c_i32, _P_PARAMS, _P_ROUTING, c_vp, c_vp]),
     "moe_route_ep": (c_i32, [c_vp, c_i32, c_i64, c_i32, c_i32, c_i32, c_i32, _P_ROUTING, c_vp,
                              c_sz, c_vp]),
     "moe_experts_ep": (c_i32, [c_vp, c_i32, c_i64, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32,

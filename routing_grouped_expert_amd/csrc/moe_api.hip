@@ -4,6 +4,7 @@
 #include <math.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "moe_common.h"
 
@@ -218,6 +219,54 @@ moe_status_t run_experts(const void *x, moe_dtype_t dtype, int64_t n, int32_t hi
   return MOE_OK;
 }
 
+// Scratch of moe_forward_noalloc, for callers that cannot allocate device
+// memory: a file-scope device array of MOE_NOALLOC_SCRATCH_BYTES.  Every GPU
+// the library runs on holds its own copy, at its own address, until the
+// process ends.  In host code the array's name is only a stand-in, never a
+// device address: kernels receive the address hipGetSymbolAddress returns for
+// the device, resolved once per device with that device current.
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  std::once_flag once;
+  void *ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the device that runs stream s (the current
+// device for the null stream).  The first call on a device makes that device
+// current for the lookup and restores the caller's device.
+hipError_t noalloc_scratch(hipStream_t s, void **out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (s != nullptr) {
+    hipDevice_t d = 0;
+    if ((e = hipStreamGetDevice(s, &d)) != hipSuccess) return e;
+    dev = (int)d;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  ScratchSlot &slot = g_scratch[dev];
+  std::call_once(slot.once, [&] {
+    if (dev != cur && (slot.err = hipSetDevice(dev)) != hipSuccess) return;
+    slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t back = hipSetDevice(cur);
+      if (slot.err == hipSuccess) slot.err = back;
+    }
+  });
+  if (slot.err != hipSuccess) return slot.err;
+  *out = slot.ptr;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -350,6 +399,39 @@ moe_status_t moe_forward(const void *x, const void *logits, moe_dtype_t dtype, i
     return MOE_ERR_HIP;
   return run_experts(x, dtype, n_tokens, hidden, w13, w2, n_experts, inter, topk, act, layout,
                      prm, routing_out, out, workspace, s);
+}
+
+moe_status_t moe_forward_noalloc(const void *x, const void *logits, moe_dtype_t dtype,
+                                 int64_t n_tokens, int32_t hidden, const void *w13,
+                                 const void *w2, int32_t n_experts, int32_t inter, int32_t topk,
+                                 moe_act_t act, moe_w13_layout_t layout,
+                                 const moe_act_params_t *params, const moe_routing_t *routing_out,
+                                 void *out, void *stream) {
+  // the sizes must fit the static scratch; checked before anything else
+  const size_t need = moe_workspace_bytes(n_tokens, n_experts, topk, hidden, inter, dtype);
+  if (need == 0) return check_sizes(n_tokens, n_experts, topk) != MOE_OK ? MOE_ERR_SHAPE
+                        : !dtype_ok(dtype)                            ? MOE_ERR_DTYPE
+                                                                      : MOE_ERR_SHAPE;
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  // every check of moe_forward, with a stand-in for the workspace (never
+  // dereferenced by the checks) of the scratch's size
+  void *const ws_stand_in = reinterpret_cast<void *>((uintptr_t)256);
+  ActParams prm;
+  moe_status_t st = check_route(logits, dtype, n_tokens, n_experts, topk, routing_out,
+                                ws_stand_in, MOE_NOALLOC_SCRATCH_BYTES);
+  if (st != MOE_OK) return st;
+  st = check_experts(x, dtype, n_tokens, hidden, w13, w2, n_experts, inter, topk, act, layout,
+                     params, routing_out, out, ws_stand_in, MOE_NOALLOC_SCRATCH_BYTES, &prm);
+  if (st != MOE_OK || n_tokens == 0) return st;
+  hipStream_t s = (hipStream_t)stream;
+  void *ws = nullptr;
+  if (noalloc_scratch(s, &ws) != hipSuccess) return MOE_ERR_HIP;
+  // the same launches as moe_forward, into this GPU's copy of the scratch
+  if (moe::launch_route(logits, dtype, n_tokens, n_experts, topk, 0, n_experts, routing_out, ws,
+                        s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return run_experts(x, dtype, n_tokens, hidden, w13, w2, n_experts, inter, topk, act, layout,
+                     prm, routing_out, out, ws, s);
 }
 
 moe_status_t moe_route_ep(const void *logits, moe_dtype_t logits_dtype, int64_t n_tokens,
@@ -554,6 +636,8 @@ const char *moe_status_str(moe_status_t status) {
     case MOE_ERR_ALIGN: return "pointer not 16-byte aligned";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_SCRATCH:
+      return "sizes need more than the library's static scratch (MOE_NOALLOC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, -8, -1):
+    for code in range(0, -9, -1):
         s = lib.moe_status_str(code).decode()
         assert s and s != "unknown status", code
     assert lib.moe_status_str(-99).decode() == "unknown status"
@@ -170,6 +170,25 @@ def test_half_entry_points_argument_checks(lib):
     assert w2(a=None) == N.MOE_ERR_NULL
     assert w2(ws=None) == N.MOE_ERR_WORKSPACE            # topk 2 needs the weighted rows
     assert w2(wsb=64) == N.MOE_ERR_WORKSPACE
+
+
+def test_noalloc_forward_argument_checks(lib):
+    r = routing()
+
+    def fwd(n=33, e=8, k=2, h=128, i=256, x=FAKE, lg=FAKE, out=FAKE, dt=N.MOE_BF16):
+        return lib.moe_forward_noalloc(x, lg, dt, n, h, FAKE, FAKE, e, i, k, N.MOE_ACT_SILU,
+                                       N.MOE_W13_PACKED, None, ctypes.byref(r), out, None)
+    assert fwd(n=0, x=None, lg=None, out=None) == N.MOE_OK   # empty: nothing enqueued
+    assert fwd(x=None) == N.MOE_ERR_NULL
+    assert fwd(lg=MISALIGNED) == N.MOE_ERR_ALIGN
+    assert fwd(k=0) == N.MOE_ERR_SHAPE
+    assert fwd(h=100) == N.MOE_ERR_SHAPE
+    assert fwd(dt=6) == N.MOE_ERR_DTYPE
+    # past the static scratch: rejected before any device call
+    assert lib.moe_workspace_bytes(4096, 128, 4, 2880, 2880, N.MOE_BF16) > \
+        N.MOE_NOALLOC_SCRATCH_BYTES
+    assert fwd(n=4096, e=128, k=4, h=2880, i=2880) == N.MOE_ERR_SCRATCH
+    assert fwd(n=1457, e=128, k=4, h=2880, i=2880) == N.MOE_ERR_SCRATCH
 
 
 def test_w2_rows_and_combine_argument_checks(lib):
