@@ -156,14 +156,17 @@ def host_info() -> dict:
 
 
 class ClockSampler:
-    """Samples the GPU's current graphics clock (MHz) from the SMI library on a
-    background thread while the timed regions run; reports the median and range
-    of the samples (None when the SMI library is not usable here)."""
+    """Samples the GPU's current graphics clock (MHz, the mean over the XCDs)
+    from the SMI library on a background thread.  Started before the warm-up so
+    the library is up when the timed region begins; only samples taken between
+    begin() and end() count.  Reports their median and range (None when the SMI
+    library is not usable here)."""
 
-    def __init__(self, period_s: float = 0.02):
+    def __init__(self, period_s: float = 0.005):
         import threading
         self.period = period_s
-        self.samples = []
+        self.samples = []           # (perf_counter time, MHz)
+        self.window = [None, None]
         self.error = None
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
@@ -171,17 +174,13 @@ class ClockSampler:
     def _read(self, smi, h):
         vals = []
         try:
-            m = smi.amdsmi_get_gpu_metrics_info(h)
-            cur = m.get("current_gfxclks")
+            cur = smi.amdsmi_get_gpu_metrics_info(h).get("current_gfxclks")
             if isinstance(cur, (list, tuple)):
                 vals = [v for v in cur if isinstance(v, (int, float)) and 0 < v < 10000]
-            elif isinstance(m.get("current_gfxclk"), (int, float)):
-                vals = [m["current_gfxclk"]]
         except Exception:
             vals = []
         if not vals:
-            c = smi.amdsmi_get_clock_info(h, smi.AmdSmiClkType.GFX)
-            vals = [c["clk"]]
+            vals = [smi.amdsmi_get_clock_info(h, smi.AmdSmiClkType.GFX)["clk"]]
         return sum(vals) / len(vals)
 
     def _run(self):
@@ -193,25 +192,32 @@ class ClockSampler:
                 if len(hs) != 1:
                     raise RuntimeError(f"{len(hs)} GPUs visible to the SMI library")
                 while not self._stop.is_set():
-                    self.samples.append(self._read(smi, hs[0]))
+                    self.samples.append((time.perf_counter(), self._read(smi, hs[0])))
                     self._stop.wait(self.period)
             finally:
                 smi.amdsmi_shut_down()
         except Exception as exc:  # no SMI access: the record says why
             self.error = f"{type(exc).__name__}: {exc}"[:160]
 
-    def __enter__(self):
+    def start(self):
         self._thread.start()
         return self
 
-    def __exit__(self, *exc):
+    def begin(self):
+        self.window[0] = time.perf_counter()
+
+    def end(self):
+        self.window[1] = time.perf_counter()
+
+    def stop(self):
         self._stop.set()
         self._thread.join(timeout=5)
 
     def summary(self) -> dict:
-        if not self.samples:
-            return {"median_mhz": None, "error": self.error or "no samples"}
-        v = sorted(self.samples)
+        t0, t1 = self.window
+        v = sorted(m for t, m in self.samples if t0 is not None and t1 is not None and t0 <= t <= t1)
+        if not v:
+            return {"median_mhz": None, "error": self.error or "no samples in the timed region"}
         return {"median_mhz": round(v[len(v) // 2]), "min_mhz": round(v[0]),
                 "max_mhz": round(v[-1]), "samples": len(v)}
 
@@ -668,20 +674,23 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
+    clock = ClockSampler().start()
     for _ in range(W):
         p_fwd()
     torch.cuda.synchronize()
-    with ClockSampler() as clock:
-        t0 = time.perf_counter()
-        st = step_stats(p_fwd, K, stream)
-        wall = time.perf_counter() - t0
-        ms_step = st["mean"]
-        # stages (the routing metadata of the last step stays valid for the others)
-        stages = [("route", p_route)]
-        stages += [("experts", p_exp)] if mx else [("w13", p_w13), ("w2", p_w2)]
-        if not mx and k > 1:
-            stages.append(("combine", p_comb))
-        stage_ms = {name: timed(fn, K) for name, fn in stages}
+    clock.begin()
+    t0 = time.perf_counter()
+    st = step_stats(p_fwd, K, stream)
+    wall = time.perf_counter() - t0
+    ms_step = st["mean"]
+    # stages (the routing metadata of the last step stays valid for the others)
+    stages = [("route", p_route)]
+    stages += [("experts", p_exp)] if mx else [("w13", p_w13), ("w2", p_w2)]
+    if not mx and k > 1:
+        stages.append(("combine", p_comb))
+    stage_ms = {name: timed(fn, K) for name, fn in stages}
+    clock.end()
+    clock.stop()
     cold_fns = [p_fwd, p_route] + ([p_comb] if not mx and k > 1 else [])
     cold = cold_stats(cold_fns, 20, stream, dev)
     col_sum = routing.col_sum.cpu()

@@ -82,6 +82,14 @@ template <int RB> __device__ __forceinline__ int swz(int row, int chunk) {
   return row * RB + ((chunk ^ swz_key<RB>(row)) << 4);
 }
 
+// Two fp32 values as two bf16 (round to nearest even, v_cvt_pk_bf16_f32), the
+// first in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+  const bf16x2v_t p = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
 // Four consecutive output elements of one row.
 typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
@@ -196,7 +204,9 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
   constexpr int SCL = WQ ? NW * 256 : 0;   // WQ: scale bytes of a stage (one 4-byte load a lane)
   constexpr int STAGE = BM * RB + BQ + SCL;
   constexpr int PER = WQ ? JA + JBQ + 1 : JA + JB;  // load instructions per wave per slice
-  constexpr int NST = TM * TN * 4;         // stores per wave per epilogue
+  // stores per wave per epilogue (exact: the ring's vmcnt waits count them):
+  // bf16 rows go out as 16-byte pieces, two per 32 x 32 sub-tile; fp32 four
+  constexpr int NST = TM * TN * (std::is_same<T, bf16_t>::value ? 2 : 4);
   constexpr bool META = EPI == EPI_Y || EPI == EPI_OUT;
   constexpr bool PP = NW == 8;             // ping-pong schedule
   static_assert(!WQ || (std::is_same<T, bf16_t>::value && QCPR >= 1 && JBQ >= 1 &&
@@ -464,10 +474,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = ti.n0 + wn * (BN / WN) + j * 32 + 8 * q + 4 * (lane >> 5);
-          float v[4];
+        auto value = [&](int q, float (&v)[4]) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             if constexpr (META)
@@ -476,11 +483,44 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
               v[t] = act_val<EPI>(acc[i][j][0][4 * q + t], acc[i][j][NSETS - 1][4 * q + t], nal,
                                   g.prm);
           }
-          // Nout is a multiple of 8, so col < Nout covers all four columns
-          const uint32_t off = (ok && col < Nout)
-                                   ? (orow * (uint32_t)Nout + (uint32_t)col) * (uint32_t)sizeof(T)
-                                   : kOOB;
-          store4(rc, off, v, T());
+        };
+        if constexpr (std::is_same<T, bf16_t>::value) {
+          // register groups q and q + 1 hold columns 8q + [0, 8) and 8q + [8, 16)
+          // split between lanes l and l + 32; swapping the halves between the
+          // two lanes (v_permlane32_swap) gives lane l the 8 columns 8q + [0, 8)
+          // and lane l + 32 the 8 columns 8q + [8, 16): one 16-byte store each
+#pragma unroll
+          for (int q = 0; q < 4; q += 2) {
+            float v0[4], v1[4];
+            value(q, v0);
+            value(q + 1, v1);
+            u32x4_t o = {pack_bf16x2(v0[0], v0[1]), pack_bf16x2(v0[2], v0[3]),
+                         pack_bf16x2(v1[0], v1[1]), pack_bf16x2(v1[2], v1[3])};
+            const auto s0 = __builtin_amdgcn_permlane32_swap(o[0], o[2], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(o[1], o[3], false, false);
+            o[0] = s0[0];
+            o[2] = s0[1];
+            o[1] = s1[0];
+            o[3] = s1[1];
+            const int col = ti.n0 + wn * (BN / WN) + j * 32 + 8 * q + 8 * (lane >> 5);
+            // Nout is a multiple of 8, so col < Nout covers all eight columns
+            const uint32_t off =
+                (ok && col < Nout) ? (orow * (uint32_t)Nout + (uint32_t)col) * 2u : kOOB;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, o), rc, (int)off,
+                                                   0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int col = ti.n0 + wn * (BN / WN) + j * 32 + 8 * q + 4 * (lane >> 5);
+            float v[4];
+            value(q, v);
+            // Nout is a multiple of 8, so col < Nout covers all four columns
+            const uint32_t off = (ok && col < Nout)
+                                     ? (orow * (uint32_t)Nout + (uint32_t)col) * (uint32_t)sizeof(T)
+                                     : kOOB;
+            store4(rc, off, v, T());
+          }
         }
       }
     }

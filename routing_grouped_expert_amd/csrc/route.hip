@@ -54,6 +54,8 @@
 // #45457 report ("implementation breakdown"), with the share given as the
 // (local_expert_offset, num_local_experts) pair of the kernel call in the PR
 // #47106 report ("key source snippets").
+#include <type_traits>
+
 #include "lds_dma.h"
 #include "moe_common.h"
 
@@ -1022,6 +1024,335 @@ __global__ __launch_bounds__(kScatterThreads) void route_scatter(
   }
 }
 
+// ---- Large batches of bf16 logits: one lane per token ------------------------
+// Each lane runs the whole top-k of its token.  A bf16 logit becomes a signed
+// order key: the two's complement of its sign-magnitude bits (so -0 and +0 are
+// the same value) in the high half, the inverted expert index in the low half,
+// so keys order by value and then by lower expert index (the same order, and
+// so the same choices, as the unsigned keys of topk_chunk).  Keys are unique,
+// and the lane keeps its best L as a sorted list t[0] > t[1] > ... > t[L-1]
+// into which each key x enters as t'[0] = max(t[0], x), t'[j] = med3(t[j-1],
+// t[j], x): one max and L - 1 median-of-three instructions a key, all from the
+// old list.  Three kernels:
+//  * route_lane_topk: 64-token blocks (one wave each, four a workgroup): top-k,
+//    softmax, topk_idx / topk_w / bitmatrix rows; then per block one ballot per
+//    local expert gives each expert's mask of tokens, whose popcount is the
+//    block's count (stored expert-major) and whose popcount below a lane is
+//    that entry's stable rank in the block.
+//  * route_count_scan: one wave per expert turns its row of block counts into
+//    exclusive prefixes over the blocks (linear in the number of blocks) and
+//    stores the expert's total.
+//  * route_lane_scatter: per block, the totals' exclusive scan gives the
+//    offsets; an entry goes to offsets[e] + (entries of e in earlier blocks) +
+//    its rank.  No atomics: every run gives the same result.
+constexpr int kLaneBlock = 64;   // tokens of a routing block (one wave)
+constexpr int kLaneWaves = 4;    // blocks (waves) of a workgroup
+constexpr int kLaneMaxWords = (kMaxExperts + 31) / 32;
+
+__device__ __forceinline__ int key_med3(int a, int b, int c) {
+  return max(min(a, b), min(max(a, b), c));  // v_med3_i32
+}
+
+// Keys of the 8 logits of a 16-byte chunk (experts e0 .. e0 + 7) inserted in
+// the sorted list t; values past E are skipped.
+template <int L, bool FULL>
+__device__ __forceinline__ void lane_insert_chunk(int (&t)[L], u32x4_t v, int e0, int E) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // the element goes through a scalar first: hipcc miscompiles a bit_cast of
+    // an ext_vector element (every i read element 0)
+    const uint32_t wi = v[i];
+    const s16x2 h = __builtin_bit_cast(s16x2, wi);
+    const s16x2 m = h >> (s16x2){15, 15};
+    const s16x2 tt = ((h & (s16x2){0x7fff, 0x7fff}) ^ m) - m;  // signed value order, -0 == +0
+    const uint32_t u = __builtin_bit_cast(uint32_t, tt);
+    const int e = e0 + 2 * i;
+    const int kk[2] = {(int)((u << 16) | (uint32_t)(0xffff - e)),
+                       (int)((u & 0xffff0000u) | (uint32_t)(0xffff - e - 1))};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if (FULL || e + q < E) {
+        const int x = kk[q];
+        int n[L];
+        n[0] = max(t[0], x);
+#pragma unroll
+        for (int j = 1; j < L; ++j) n[j] = key_med3(t[j - 1], t[j], x);
+#pragma unroll
+        for (int j = 0; j < L; ++j) t[j] = n[j];
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ int lane_key_expert(int k) { return 0xffff - (k & 0xffff); }
+__device__ __forceinline__ float lane_key_value(int k) {
+  const int tv = k >> 16;  // signed value order
+  const uint32_t bits = tv < 0 ? ((uint32_t)(-tv) | 0x8000u) : (uint32_t)tv;
+  return __uint_as_float(bits << 16);
+}
+
+// Logits of a block in LDS: token t's 16-byte chunk c sits in slot
+// t * CH + (c + rot(t)) % CH (CH = 2^lch chunks a row), rot(t) = t / (16 / CH)
+// for CH < 16 and t otherwise, so the 16 lanes of a ds_read_b128 (16 tokens,
+// one chunk each) hit 16 distinct bank groups.
+__device__ __forceinline__ int lane_rot(int t, int lch) { return lch >= 4 ? t : t >> (4 - lch); }
+
+// L: list length, a power of two >= topk.  One wave per 64-token block b.
+// E is a power of two from 8 (whole 16-byte chunks, 2^lch a row); the
+// block's rows are copied to LDS with direct-to-LDS loads, fully coalesced,
+// then each lane reads its own row from there.
+template <int L>
+__global__ __launch_bounds__(64 * kLaneWaves) void route_lane_topk(
+    const bf16_t *__restrict__ logits, int64_t N, int E, int lch, int K, int lo, int nl,
+    int32_t *__restrict__ topk_idx, bf16_t *__restrict__ topk_w,
+    uint32_t *__restrict__ bitmatrix, int32_t *__restrict__ blk_cnt, int nbp,
+    uint8_t *__restrict__ blk_rank) {
+  extern __shared__ __attribute__((aligned(16))) char s_rows[];  // kLaneWaves * 64 * E * 2 bytes
+  __shared__ unsigned long long s_mask[kLaneWaves][kMaxExperts];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t b = (int64_t)blockIdx.x * kLaneWaves + wave;
+  const int64_t tok0 = b * kLaneBlock;
+  if (tok0 >= N) return;  // whole wave: no token of this block exists
+  const int64_t t = tok0 + lane;
+  const bool live = t < N;
+  const int ch = 1 << lch;                           // 16-byte chunks a row (E / 8)
+  const int rowb = E * 2;
+  char *rows = s_rows + wave * kLaneBlock * rowb;
+  {
+    // DMA instruction i fills LDS slots [64 i, 64 i + 64); lane l fetches the
+    // chunk that belongs in slot 64 i + l.  Tokens past N read zeros.
+    const int ntok = (int)min<int64_t>(kLaneBlock, N - tok0);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16_t *>(logits + tok0 * E), (short)0, ntok * rowb, kRsrcWord3);
+    for (int i = 0; i < ch; ++i) {
+      const int slot = i * 64 + lane, tt = slot >> lch, pos = slot & (ch - 1);
+      const int c = (pos - lane_rot(tt, lch)) & (ch - 1);
+      const uint32_t off = tt < ntok ? (uint32_t)(tt * rowb + c * 16) : kOOB;
+      dma16(rs, rows + i * 1024, off);
+    }
+    wait_vm<0>();  // this wave's rows are in LDS (each wave reads only its own)
+    __builtin_amdgcn_wave_barrier();
+  }
+  int key[L];
+#pragma unroll
+  for (int j = 0; j < L; ++j) key[j] = (int)0x80000000;  // below every real key: no-ops
+  if (live) {
+    const char *myrow = rows + lane * rowb;
+    const int rot = lane_rot(lane, lch);
+    for (int c0 = 0; c0 < ch; c0 += 8) {
+      u32x4_t raw[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int pos = (c0 + c + rot) & (ch - 1);
+        if (c0 + c < ch) raw[c] = *reinterpret_cast<const u32x4_t *>(myrow + pos * 16);
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (c0 + c < ch) lane_insert_chunk<L, true>(key, raw[c], (c0 + c) * 8, E);
+    }
+  }
+  // softmax over the selected logits in slot order (the arithmetic of
+  // topk_chunk, so the same weights), outputs, bitmatrix words over local ids
+  const int words = (nl + 31) >> 5;
+  uint32_t word[kLaneMaxWords];
+#pragma unroll
+  for (int w = 0; w < kLaneMaxWords; ++w) word[w] = 0u;
+  int sel[L];
+  if (live) {
+    const float vmax = lane_key_value(key[0]);
+    float ssum = 0.f;
+#pragma unroll
+    for (int j = 0; j < L; ++j)
+      if (j < K) ssum += expf(lane_key_value(key[j]) - vmax);
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      sel[j] = lane_key_expert(key[j]);
+      if (j < K) {
+        topk_idx[t * K + j] = sel[j];
+        topk_w[t * K + j] = from_f32<bf16_t>(expf(lane_key_value(key[j]) - vmax) / ssum);
+        const int l = sel[j] - lo;
+        if ((unsigned)l < (unsigned)nl) {
+#pragma unroll
+          for (int w = 0; w < kLaneMaxWords; ++w)
+            if ((l >> 5) == w) word[w] |= 1u << (l & 31);
+        }
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < kLaneMaxWords; ++w)
+      if (w < words) bitmatrix[t * words + w] = word[w];
+  }
+  // per local expert l: the mask of this block's tokens that chose it (ballot);
+  // lane l % 64 keeps it, then the masks go to LDS for the rank look-ups
+  unsigned long long mine[kMaxExperts / 64];
+#pragma unroll
+  for (int q = 0; q < kMaxExperts / 64; ++q) mine[q] = 0ull;
+#pragma unroll
+  for (int w = 0; w < kLaneMaxWords; ++w) {
+    if (w < words) {
+      const uint32_t wv = word[w];
+      const int nb_w = min(32, nl - 32 * w);
+      const int own = lane - 32 * (w & 1);  // the bit whose expert this lane keeps
+#pragma unroll
+      for (int bit = 0; bit < 32; ++bit) {
+        if (bit < nb_w) {  // (uniform)
+          const unsigned long long m = __ballot((wv >> bit) & 1u);
+          // lane (32 w + bit) % 64 keeps expert 32 w + bit's mask
+          if (own == bit) mine[w >> 1] = m;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kMaxExperts / 64; ++q) {
+    const int l = q * 64 + lane;
+    if (l < nl) {
+      s_mask[wave][l] = mine[q];
+      blk_cnt[(int64_t)l * nbp + b] = popc64(mine[q]);
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (live) {
+    const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      if (j < K) {
+        // slots outside the share get rank 0; the scatter never places them
+        const int l = sel[j] - lo;
+        blk_rank[t * K + j] =
+            (unsigned)l < (unsigned)nl ? (uint8_t)popc64(s_mask[wave][l] & below) : (uint8_t)0;
+      }
+    }
+  }
+}
+
+// One wave per local expert l: the block counts blk_cnt[l][0 .. nb) become
+// exclusive prefixes over the blocks, in place; tot[l] gets the total.  A
+// round covers 1024 blocks (16 a lane, all loaded before any is used).
+constexpr int kScanWaves = 4;
+__global__ __launch_bounds__(64 * kScanWaves) void route_count_scan(int32_t *__restrict__ blk_cnt,
+                                                                    int nbp, int nb, int nl,
+                                                                    int32_t *__restrict__ tot) {
+  const int lane = threadIdx.x & 63;
+  const int l = blockIdx.x * kScanWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (l >= nl) return;  // whole wave
+  u32x4_t *row = reinterpret_cast<u32x4_t *>(blk_cnt + (int64_t)l * nbp);
+  int carry = 0;
+  for (int c0 = 0; c0 < nb; c0 += 1024) {
+    const int base = c0 + 16 * lane;  // this lane's 16 blocks
+    u32x4_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      v[u] = base + 4 * u < nbp ? row[base / 4 + u] : u32x4_t{0u, 0u, 0u, 0u};
+    int c[16], s = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        c[4 * u + q] = base + 4 * u + q < nb ? (int)v[u][q] : 0;  // padding was never written
+        s += c[4 * u + q];
+      }
+    const int incl = wave_inclusive_sum(s);
+    int run = carry + incl - s;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[u][q] = (uint32_t)run;
+        run += c[4 * u + q];
+      }
+      if (base + 4 * u < nbp) row[base / 4 + u] = v[u];
+    }
+    carry += __shfl(incl, 63);
+  }
+  if (lane == 0) tot[l] = carry;
+}
+
+// Per 64-token block (a wave): offsets from the totals, then every entry of
+// the block to offsets[e] + (entries of e in earlier blocks) + rank.
+__global__ __launch_bounds__(64 * kLaneWaves) void route_lane_scatter(
+    int64_t N, int K, int lo, int nl, int nbp, const int32_t *__restrict__ blk_pre,
+    const int32_t *__restrict__ tot, const uint8_t *__restrict__ blk_rank,
+    const int32_t *__restrict__ topk_idx, const bf16_t *__restrict__ topk_w,
+    int32_t *__restrict__ col_sum, int32_t *__restrict__ offsets, int32_t *__restrict__ col_sorted,
+    int32_t *__restrict__ row_sorted, bf16_t *__restrict__ gate_scal) {
+  __shared__ int s_base[kLaneWaves][kMaxExperts + 1];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t b = (int64_t)blockIdx.x * kLaneWaves + wave;
+  const int64_t tok0 = b * kLaneBlock;
+  if (tok0 >= N) return;  // whole wave
+  const int64_t t = tok0 + lane;
+  const bool own = t < N;
+  // the block's entries first: they do not depend on the counts
+  int ex[kMaxTopk], rk[kMaxTopk];
+  bf16_t w[kMaxTopk];
+  if (own) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j) {
+      if (j < K) {
+        ex[j] = topk_idx[t * K + j] - lo;  // local id; outside the share if not in [0, nl)
+        rk[j] = blk_rank[t * K + j];
+        w[j] = topk_w[t * K + j];
+      }
+    }
+  }
+  // totals of the local experts (four a lane) -> exclusive scan -> offsets
+  int v[4], s = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int l = lane * 4 + q;
+    v[q] = l < nl ? tot[l] : 0;
+    s += v[q];
+  }
+  const int incl = wave_inclusive_sum(s);
+  int run = incl - s;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int l = lane * 4 + q;
+    if (l < nl) {
+      s_base[wave][l] = run + blk_pre[(int64_t)l * nbp + b];
+      if (b == 0) {
+        offsets[l] = run;
+        col_sum[l] = v[q];
+      }
+    }
+    run += v[q];
+  }
+  const int m_local = __shfl(incl, 63);
+  if (b == 0 && lane == 0) offsets[nl] = m_local;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (own) {
+#pragma unroll
+    for (int j = 0; j < kMaxTopk; ++j) {
+      if (j < K) {
+        if ((unsigned)ex[j] < (unsigned)nl) {
+          const int p = s_base[wave][ex[j]] + rk[j];
+          col_sorted[p] = (int32_t)(t * K + j);
+          row_sorted[t * K + j] = p;
+          gate_scal[p] = w[j];
+        } else {
+          row_sorted[t * K + j] = -1;
+        }
+      }
+    }
+  }
+  // sorted positions past the local entries: this block clears its share of
+  // [m_local, N*K), the positions [b*64*K, (b+1)*64*K)
+  const int64_t M = N * K;
+  const int64_t p_end = min(M, (b + 1) * kLaneBlock * K);
+  for (int64_t p = max((int64_t)m_local, b * kLaneBlock * K) + lane; p < p_end; p += 64) {
+    col_sorted[p] = -1;
+    gate_scal[p] = from_f32<bf16_t>(0.f);
+  }
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // Which routing path a batch takes: one workgroup for small batches (see
@@ -1052,6 +1383,18 @@ inline RoutePath route_path(int64_t N, int E, int K) {
 // blocks (one pass of 16 lanes a token at E = 128): 4x the workgroups.
 constexpr int64_t kSmallBlocksUpTo = 16384;
 inline int route_block_tokens(int64_t N) { return N <= kSmallBlocksUpTo ? 64 : kRouteTokens; }
+
+// The lane-per-token path takes bf16 logits of a power-of-two expert count
+// from 8 in batches of at least kLaneTokens tokens: there its count scan is
+// linear in the number of blocks, where route_scatter's re-summing of all
+// earlier blocks grows with their square.  Smaller batches keep the
+// cooperative top-k above, whose lanes share a token and keep every SIMD
+// busier (65536 tokens, 128 experts: 28.4 us on this path, 28.9 on the other;
+// 32 experts: 16.7 against 15.5).
+constexpr int64_t kLaneTokens = 131072;
+inline bool lane_path(int64_t N, int E) {
+  return N >= kLaneTokens && E >= 8 && (E & (E - 1)) == 0 && N * E * 2 < ((int64_t)1 << 31);
+}
 
 // With x != nullptr (router GEMM), `logits` is written from x and the gate
 // weight wg [E, H] before the top-k reads it.
@@ -1185,6 +1528,37 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
                          r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs);
     return hipGetLastError();
   }
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (lane_path(N, E)) {
+    // bf16 logits: one lane per token (route_lane_topk, route_count_scan,
+    // route_lane_scatter).  Scratch: block counts [nl][nbp] (then their
+    // prefixes), the local experts' totals, the entries' in-block ranks.
+    const int64_t nb = (N + kLaneBlock - 1) / kLaneBlock;
+    const int nbp = (int)((nb + 3) / 4 * 4);
+    int32_t *blk_cnt = reinterpret_cast<int32_t *>(scratch);
+    int32_t *tot = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(scratch) +
+                                               align256((size_t)nbp * E * 4));
+    uint8_t *blk_rank = reinterpret_cast<uint8_t *>(tot) + align256((size_t)E * 4);
+    const unsigned wgs = (unsigned)((nb + kLaneWaves - 1) / kLaneWaves);
+    const size_t lds = (size_t)kLaneWaves * kLaneBlock * E * 2;
+    auto topk = [&](auto kern) {
+      int lch = 0;
+      while ((8 << lch) < E) ++lch;
+      hipLaunchKernelGGL(kern, dim3(wgs), dim3(64 * kLaneWaves), lds, s, logits, N, E, lch, K, lo,
+                         nl, r->topk_idx, tw, r->bitmatrix, blk_cnt, nbp, blk_rank);
+    };
+    if (K <= 2) topk(route_lane_topk<2>);
+    else if (K <= 4) topk(route_lane_topk<4>);
+    else if (K <= 8) topk(route_lane_topk<8>);
+    else topk(route_lane_topk<16>);
+    hipLaunchKernelGGL(route_count_scan, dim3((unsigned)((nl + kScanWaves - 1) / kScanWaves)),
+                       dim3(64 * kScanWaves), 0, s, blk_cnt, nbp, (int)nb, nl, tot);
+    hipLaunchKernelGGL(route_lane_scatter, dim3(wgs), dim3(64 * kLaneWaves), 0, s, N, K, lo, nl,
+                       nbp, blk_cnt, tot, blk_rank, r->topk_idx, tw, r->col_sum, r->offsets,
+                       r->col_sorted, r->row_sorted, gs);
+    return hipGetLastError();
+    }
+  }
   const int64_t nb = (N + ntb - 1) / ntb;
   const int nbp = (int)((nb + 3) / 4 * 4);
   int32_t *blk_cnt = reinterpret_cast<int32_t *>(scratch);
@@ -1223,10 +1597,13 @@ size_t gate_scratch_bytes(int64_t n_tokens, int n_experts, int hidden, moe_dtype
 
 size_t route_scratch_bytes(int64_t n_tokens, int n_experts, int topk) {
   if (route_path(n_tokens, n_experts, topk) != kPathBlocks) return 0;
-  const int ntb = route_block_tokens(n_tokens);
-  const int64_t nb = (n_tokens + ntb - 1) / ntb;
+  // the most either multi-block path needs: the 64-token blocks of the
+  // lane-per-token path (at least as many blocks as route_block_tokens gives)
+  // plus its expert totals
+  const int64_t nb = (n_tokens + kLaneBlock - 1) / kLaneBlock;
   const int64_t nbp = (nb + 3) / 4 * 4;
-  return align256((size_t)nbp * n_experts * 4) + align256((size_t)n_tokens * topk);
+  return align256((size_t)nbp * n_experts * 4) + align256((size_t)n_experts * 4) +
+         align256((size_t)n_tokens * topk);
 }
 
 hipError_t launch_route(const void *logits, moe_dtype_t dt, int64_t n_tokens, int n_experts,
