@@ -627,7 +627,20 @@ template <int BM_, int BN_, int WM_, int WN_, int S_, int RB_> struct Cfg {
 // Tile configurations, largest first (rows x output columns, waves rows x
 // columns, ring stages, LDS row bytes).  Gated tiles carry 2 * BN weight rows.
 using GatedL = Cfg<256, 128, 4, 2, 4, 64>;  // 8 waves, 64 x (64 + 64) each
+// the same tiles with 128-byte slices in a two-stage ring, for rows of at
+// least kLongRowBytes: four MFMA k-steps a phase instead of two halves the
+// barriers a slice, which pays once a tile's K loop is long (skewed 64-expert
+// layer, 4096-wide rows: gated w13 3270 -> 3106 us, plain ReLU^2 w13 -6 %);
+// with 1536-wide rows the single slice of lookahead loses (w2 +25 %)
+using GatedL2 = Cfg<256, 128, 4, 2, 2, 128>;
+using PlainL2 = Cfg<256, 256, 4, 2, 2, 128>;
+constexpr int kLongRowBytes = 6144;
 using GatedM = Cfg<128, 128, 2, 4, 3, 128>; // 8 waves, 64 x (32 + 32) each
+// 96 - 176 rows an expert (the gpt-oss-sized layer at 2048-4096 tokens): one
+// 192-row plain tile holds all of an expert's rows, where 128-row tiles give
+// about half the experts a second, nearly empty tile (w2 at 4096 tokens 568 ->
+// 545 us; the gated 192-row tile measured no faster than the 128-row one)
+using PlainX = Cfg<192, 256, 2, 4, 2, 128>; // 8 waves, 96 x 64 each
 using GatedS = Cfg<32, 128, 1, 4, 4, 128>;  // 4 waves, 32 x (32 + 32) each
 using PlainL = Cfg<256, 256, 4, 2, 4, 64>;  // 8 waves, 64 x 128 each
 using PlainM = Cfg<128, 128, 2, 4, 3, 128>; // 8 waves, 64 x 32 each
@@ -695,6 +708,8 @@ inline double launch_cost(int64_t tiles, int64_t cus, int BM, int BN, double sur
 // waste), and so do launches too small to give half the CUs a 128-row tile;
 // when even the 32 x 128 tiles number fewer than the CUs, the 32 x 32
 // one-wave tile spreads the weight stream over more CUs.
+// Plain (w2) launches of 96 to 176 rows an expert on average take the 192-row
+// tile (one m-tile an expert).
 // Plain (w2) layers with up to one 256-row tile per expert on average stream
 // each expert's weights about once with 256-row tiles and about 1.5 times with
 // 128-row tiles, so they take the 256-row tile -- when those tiles still cover
@@ -737,11 +752,26 @@ hipError_t launch_t(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
       return launch_cfg<T, NSETS, EPI, Tn>(a, M, E, s);
     return launch_cfg<T, NSETS, EPI, Sm>(a, M, E, s);
   }
-  if (NSETS == 1 && M < (int64_t)L::BM * E && expected_tiles(M, E, a.Nout, L::BM, L::BN) >= cus)
+  if constexpr (NSETS == 1) {
+    if (M >= 96 * (int64_t)E && M <= 176 * (int64_t)E &&
+        expected_tiles(M, E, a.Nout, PlainX::BM, PlainX::BN) >= cus)
+      return launch_cfg<T, NSETS, EPI, PlainX>(a, M, E, s);
+  }
+  // the 256-row tile, with 128-byte slices for long rows
+  // (bf16 only: fp32 layers keep the 64-byte slices)
+  using L2 = typename std::conditional<NSETS == 2, GatedL2, PlainL2>::type;
+  auto launch_l = [&]() {
+    if constexpr (std::is_same<T, bf16_t>::value) {
+      if ((int64_t)a.K * (int64_t)sizeof(T) >= kLongRowBytes)
+        return launch_cfg<T, NSETS, EPI, L2>(a, M, E, s);
+    }
     return launch_cfg<T, NSETS, EPI, L>(a, M, E, s);
+  };
+  if (NSETS == 1 && M < (int64_t)L::BM * E && expected_tiles(M, E, a.Nout, L::BM, L::BN) >= cus)
+    return launch_l();
   const double cl = launch_cost(expected_tiles(M, E, a.Nout, L::BM, L::BN), cus, L::BM, L::BN, 0.0);
   const double cm = launch_cost(tm, cus, Md::BM, Md::BN, 0.15);
-  if (cl <= cm) return launch_cfg<T, NSETS, EPI, L>(a, M, E, s);
+  if (cl <= cm) return launch_l();
   return launch_cfg<T, NSETS, EPI, Md>(a, M, E, s);
 }
 

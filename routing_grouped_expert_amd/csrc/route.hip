@@ -1385,13 +1385,13 @@ constexpr int64_t kSmallBlocksUpTo = 16384;
 inline int route_block_tokens(int64_t N) { return N <= kSmallBlocksUpTo ? 64 : kRouteTokens; }
 
 // The lane-per-token path takes bf16 logits of a power-of-two expert count
-// from 8 in batches of at least kLaneTokens tokens: there its count scan is
-// linear in the number of blocks, where route_scatter's re-summing of all
-// earlier blocks grows with their square.  Smaller batches keep the
-// cooperative top-k above, whose lanes share a token and keep every SIMD
-// busier (65536 tokens, 128 experts: 28.4 us on this path, 28.9 on the other;
-// 32 experts: 16.7 against 15.5).
-constexpr int64_t kLaneTokens = 131072;
+// from 8 in batches of at least kLaneTokens tokens, where it is faster (32768
+// tokens, 128 experts: 22.9 -> 19.8 us; 65536: 27.7 -> 23.2 us; 32 experts
+// even) and its count scan is linear in the number of blocks, where
+// route_scatter's re-summing of all earlier blocks grows with their square
+// (262144 tokens: 146 -> 54 us).  Smaller batches keep the cooperative top-k
+// above: with few tokens a CU the lane path leaves SIMDs idle.
+constexpr int64_t kLaneTokens = 32768;
 inline bool lane_path(int64_t N, int E) {
   return N >= kLaneTokens && E >= 8 && (E & (E - 1)) == 0 && N * E * 2 < ((int64_t)1 << 31);
 }

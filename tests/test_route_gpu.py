@@ -55,11 +55,11 @@ EDGE = [
     (1, 200, 8, "f32"),      # fp32 logits over all 64 lanes
     (1, 5, 5, "f32"),        # k == E
     (1, 1, 1, "bf16"),       # single expert
-    # one lane a token (131072 tokens and more, a power-of-two expert count)
-    (131072 + 29, 256, 16, "bf16"),  # widest layer, largest top-k, ragged last block
-    (131072, 8, 1, "bf16"),  # one chunk a row, top-1
-    (140001, 64, 8, "bf16"),  # more than 2048 blocks: three rounds of the count scan
-    (131100, 40, 3, "bf16"),  # not a power of two: back on the cooperative top-k
+    # one lane a token (32768 tokens and more, a power-of-two expert count)
+    (32768 + 29, 256, 16, "bf16"),  # widest layer, largest top-k, ragged last block
+    (32768, 8, 1, "bf16"),   # one chunk a row, top-1
+    (70001, 64, 8, "bf16"),  # more than 1024 blocks: two rounds of the count scan
+    (32800, 40, 3, "bf16"),  # not a power of two: back on the cooperative top-k
 ]
 
 
@@ -87,13 +87,13 @@ def test_routing_lane_path_ties_and_share():
     """Forced ties and signed zeros, and an expert share, on the one-lane-a-token
     path."""
     g = torch.Generator().manual_seed(5)
-    lg = torch.randint(-2, 3, (131072, 64), generator=g).to(torch.float32)
+    lg = torch.randint(-2, 3, (40000, 64), generator=g).to(torch.float32)
     lg[lg == 0] = torch.where(torch.rand(int((lg == 0).sum()), generator=g) < 0.5, -0.0, 0.0)
     _run(lg.to(torch.bfloat16), 6, "lane-ties")
     from routing_grouped_expert_amd import moe_route_ep
-    lg = routing_logits(131073, 128, "bf16", seed=9)
+    lg = routing_logits(50001, 128, "bf16", seed=9)
     for lo, nl in ((5, 37), (0, 128), (96, 32)):
-        print(f"[route] lane-share N=131073 E=128 k=4 share=[{lo},{lo + nl})", flush=True)
+        print(f"[route] lane-share N=50001 E=128 k=4 share=[{lo},{lo + nl})", flush=True)
         ref = oracle.route_ep(lg, 4, "bf16", lo, nl)
         gpu = moe_route_ep(lg.to(DEV), 4, lo, nl)
         torch.cuda.synchronize()
