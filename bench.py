@@ -9,12 +9,13 @@ sorted indices), the w13 grouped GEMM with the activation, the w2 grouped GEMM
 with the routing weight, and the combine.  W untimed steps, then K steps
 between two HIP events on the launch stream give the step time.
 
-Per-kernel device times come from separate timed regions on the same stream:
-K back-to-back launches of each stage's C call (moe_route, moe_experts_w13,
-moe_experts_w2_rows -- GEMM2 alone --, moe_combine) between two events, so a
-stage's average includes the short dispatch gap between back-to-back launches.
-The stage with the longest single-kernel time is the dominant kernel of the
-roofline line.  Rank 0 prints one JSON line.
+Per-kernel device times: K back-to-back calls of each stage's C call
+(moe_route, moe_experts_w13, moe_experts_w2_rows -- GEMM2 alone --,
+moe_combine) captured in a HIP graph on a stream of their own and replayed
+between two events on that stream, so no host launch cost sits between the
+calls; a stage's average still includes the short gap between consecutive
+kernels.  The stage with the longest single-kernel time is the dominant kernel
+of the roofline line.  Rank 0 prints one JSON line.
 
 The default workload is the largest layer: 16384 tokens, hidden 4096,
 intermediate 1536, 64 experts, top-8, Zipf-skewed router logits, SiLU-gated,
@@ -636,8 +637,6 @@ def main():
         p_route = prepare_route(lg, k, routing=routing, workspace=ws, stream=stream)
         p_fwd = prepare_forward_mxfp4(x, lg, *wq, k, spec.act, spec.layout, act_params(spec),
                                       out=out, routing=routing, workspace=ws, stream=stream)
-        p_exp = prepare_experts_mxfp4(x, *wq, routing, spec.act, spec.layout, act_params(spec),
-                                      out=out, workspace=ws, stream=stream)
     elif share:
         p_route = prepare_route_ep(lg, k, spec.local_offset, spec.n_local, routing=routing,
                                    workspace=ws, stream=stream)
@@ -651,28 +650,54 @@ def main():
     # the split calls run the kernels of the full call: GEMM1 + activation,
     # GEMM2 + routing weight into sorted rows, then the combine (k > 1); with one
     # slot a token GEMM2 writes the output rows itself
-    if not mx:
-        p_w13 = prepare_experts_w13(x, w13, routing, spec.act, spec.layout, act_params(spec),
-                                    act_out=act, stream=stream)
+    y_rows = torch.empty(n * k, spec.hidden, dtype=dt, device=dev) if not mx and k > 1 else None
+
+    def stage_calls(st):
+        """The layer's stages as prepared C calls on stream st, in order."""
+        calls = [("route", prepare_route_ep(lg, k, spec.local_offset, spec.n_local,
+                                            routing=routing, workspace=ws, stream=st)
+                  if share else prepare_route(lg, k, routing=routing, workspace=ws, stream=st))]
+        if mx:
+            return calls + [("experts", prepare_experts_mxfp4(
+                x, *wq, routing, spec.act, spec.layout, act_params(spec), out=out, workspace=ws,
+                stream=st))]
+        calls.append(("w13", prepare_experts_w13(x, w13, routing, spec.act, spec.layout,
+                                                 act_params(spec), act_out=act, stream=st)))
         if k > 1:
-            y_rows = torch.empty(n * k, spec.hidden, dtype=dt, device=dev)
-            p_w2 = prepare_experts_w2_rows(act, w2, routing, y_sorted=y_rows, stream=stream)
-            p_comb = prepare_combine(y_rows, routing, out=out, stream=stream)
+            calls.append(("w2", prepare_experts_w2_rows(act, w2, routing, y_sorted=y_rows,
+                                                        stream=st)))
+            calls.append(("combine", prepare_combine(y_rows, routing, out=out, stream=st)))
         else:
-            p_w2 = prepare_experts_w2(act, w2, routing, out=out, workspace=ws, stream=stream)
+            calls.append(("w2", prepare_experts_w2(act, w2, routing, out=out, workspace=ws,
+                                                   stream=st)))
+        return calls
 
     K, W = args.steps, args.warmup
 
-    def timed(fn, reps):
-        """Average device time of fn() over reps back-to-back calls (ms)."""
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        a.record(stream)
-        for _ in range(reps):
+    def graph_timed(fn, reps, gstream):
+        """Device time of one call (ms): reps back-to-back calls captured in a HIP
+        graph on gstream, replayed between two events on gstream (no host launch
+        cost between the calls); the best of three replays."""
+        with torch.cuda.stream(gstream):
             fn()
-        b.record(stream)
         torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gstream):
+            for _ in range(reps):
+                fn()
+        best = None
+        for _ in range(3):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            with torch.cuda.stream(gstream):
+                a.record(gstream)
+                g.replay()
+                b.record(gstream)
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) / reps
+            best = t if best is None else min(best, t)
+        del g
+        return best
 
     clock = ClockSampler().start()
     for _ in range(W):
@@ -683,14 +708,14 @@ def main():
     st = step_stats(p_fwd, K, stream)
     wall = time.perf_counter() - t0
     ms_step = st["mean"]
-    # stages (the routing metadata of the last step stays valid for the others)
-    stages = [("route", p_route)]
-    stages += [("experts", p_exp)] if mx else [("w13", p_w13), ("w2", p_w2)]
-    if not mx and k > 1:
-        stages.append(("combine", p_comb))
-    stage_ms = {name: timed(fn, K) for name, fn in stages}
+    # stages (the routing metadata of the last step stays valid for the others),
+    # each timed as a captured graph of K calls on a stream of its own
+    gstream = torch.cuda.Stream(device=dev)
+    stage_ms = {name: graph_timed(fn, K, gstream) for name, fn in stage_calls(gstream)}
     clock.end()
     clock.stop()
+    eager = dict(stage_calls(stream))
+    p_comb = eager.get("combine")
     cold_fns = [p_fwd, p_route] + ([p_comb] if not mx and k > 1 else [])
     cold = cold_stats(cold_fns, 20, stream, dev)
     col_sum = routing.col_sum.cpu()
