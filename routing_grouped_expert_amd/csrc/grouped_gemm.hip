@@ -181,8 +181,8 @@ __device__ __forceinline__ TileInfo tile_info(int L, const int *s_ts, const int 
 // 4-byte read of 8 codes and one scale byte, turned into 8 bf16 values with
 // the hardware's scaled FP4 conversion (exact: a code times a power of two).
 template <typename T, int NSETS, int EPI, int BM, int BN, int WM, int WN, int S, int RB,
-          bool WQ = false>
-__global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
+          bool WQ>
+__device__ __forceinline__ void gemm_body(const GemmArgs &g) {
   using Mm = Mma<T>;
   using Frag = typename Mm::Frag;
   constexpr int BK = RB / (int)sizeof(T);  // K elements per slice
@@ -209,6 +209,9 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
   constexpr int NST = TM * TN * (std::is_same<T, bf16_t>::value ? 2 : 4);
   constexpr bool META = EPI == EPI_Y || EPI == EPI_OUT;
   constexpr bool PP = NW == 8;             // ping-pong schedule
+  // four waves over 256-row tiles, one a SIMD: 128-row register blocks
+  constexpr bool BIG = NW == 4 && BM == 256;
+  static_assert(!BIG || !WQ, "four-wave tiles: bf16/fp32 weights");
   static_assert(!WQ || (std::is_same<T, bf16_t>::value && QCPR >= 1 && JBQ >= 1 &&
                         JBQ * QRPI * NW == NB && SBK * NB <= SCL && NB % 4 == 0),
                 "MXFP4 weights: bf16 tiles whose code rows fill whole wave loads");
@@ -474,6 +477,12 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
       }
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
+        if constexpr (BIG) {
+          // the accumulators stay in AGPRs up to here, so their copies to
+          // VGPRs for this sub-tile's arithmetic cannot move earlier
+#pragma unroll
+          for (int s = 0; s < NSETS; ++s) asm volatile("" : "+a"(acc[i][j][s]));
+        }
         auto value = [&](int q, float (&v)[4]) {
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
@@ -522,9 +531,13 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
             store4(rc, off, v, T());
           }
         }
+        // one sub-tile at a time: hoisting every accumulator read would need
+        // 256 more registers in the four-wave tiles
+        if constexpr (BIG) __builtin_amdgcn_sched_barrier(0);
       }
     }
-    st_until = z + S - 1;
+    // the four-wave loop issues slice z + S before this epilogue, the others z + S - 1
+    st_until = z + S - 1 + (BIG ? 1 : 0);
   };
 
 #pragma unroll
@@ -574,6 +587,129 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
       barrier();
     }
     if (!grp) barrier();
+  } else if constexpr (BIG) {
+    // One wave a SIMD: nothing else fills the matrix core while this wave
+    // issues other work, and a wave issues at most one instruction every four
+    // cycles, so the loop keeps its instructions few and each memory
+    // instruction follows an MFMA (about seven free issue slots each).
+    //  * k-step ks < NKS - 1: the fragments of k-step ks + 1 are read, one
+    //    after each MFMA.
+    //  * last k-step: the wave waits for slice z + 1, meets the other waves
+    //    at the barrier (after which none reads slot z % S again), then each
+    //    MFMA is followed by one of the DMA loads of slice z + S into that
+    //    slot or one read of slice z + 1's first fragments.
+    // Every slice takes that path: a slice that starts a tile first sets up
+    // the tile's load offsets, and slices past the end of the stream load
+    // through an empty buffer (zeros into a slot nobody reads), so each wait
+    // is one count.  Rows hold whole slices (no K tail: the host checks).
+    constexpr int NM = TM * TN * NSETS;  // MFMAs a k-step
+    constexpr int NFK = TM + TN * NSETS; // fragment reads a k-step
+    constexpr int NOPS = JA + JB + NFK;  // memory instructions of the last k-step
+    static_assert(!BIG || (NFK <= NM && NOPS <= 2 * NM && NKS % 2 == 0),
+                  "at most two memory instructions a MFMA; k-step pairs");
+    Frag fa[2][TM], fb[2][TN][NSETS];
+    auto frag_read = [&](int buf, const char *la, int ks, int f) {
+      if (f < TM) {
+        fa[buf][f] = Mm::ld(la + frag_addr(ks, wm * (BM / WM) + f * 32 + (lane & 31)));
+      } else {
+        const int j = (f - TM) / NSETS, s = (f - TM) % NSETS;
+        fb[buf][j][s] = bfrag(la + BM * RB, ks, s * BN + wn * (BN / WN) + j * 32 + (lane & 31));
+      }
+    };
+    auto mma_one = [&](int buf, int m) {
+      const int i = m / (TN * NSETS), j = (m / NSETS) % TN, s = m % NSETS;
+      acc[i][j][s] = Mm::mma(fb[buf][j][s], fa[buf][i], acc[i][j][s]);
+    };
+    auto bar = [&]() {  // workgroup barrier; MFMAs may cross it
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    // the loads of a slice past the stream's end: offsets outside every
+    // buffer (zeros, or for rows already marked out of range other bytes of
+    // the same buffers) into a slot no wave reads again
+    static_assert(!BIG || (S & (S - 1)) == 0, "ring slots by mask");
+    const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(smem));  // LDS address of slot 0
+    const uint32_t wb = (uint32_t)(BM * RB + wave * JB * 1024), wa = (uint32_t)(wave * JA * 1024);
+    auto issue_past = [&](int zs) {
+      const uint32_t d = sbase + ((uint32_t)zs & (S - 1)) * STAGE;
+#pragma unroll
+      for (int j = 0; j < JB; ++j) dma16a(rb, d + wb + j * 1024, vb[j], kOOB);
+#pragma unroll
+      for (int j = 0; j < JA; ++j) dma16a(ra, d + wa + j * 1024, va[j], kOOB);
+    };
+    // prologue: slices 0 .. S - 2 went out above (those that exist); the
+    // others go out past the end, so S - 2 slices' loads follow every slice
+    // and each wait below has one count
+#pragma unroll
+    for (int s = 1; s < S - 1; ++s)
+      if (s >= nz) issue_past(s);
+    wait_vm<vm_cap((S - 2) * PER)>();
+    barrier();
+    if (S - 1 < nz) issue(S - 1);  // a slot not read yet
+    else issue_past(S - 1);
+#pragma unroll
+    for (int f = 0; f < NFK; ++f) frag_read(0, smem, 0, f);
+    int z = 0;
+    // where the loads of slice z + S stand: its tile and its place in it
+    int in = (S - 1) / nk, kn = (S - 1) % nk;
+#pragma nounroll
+    for (int it = 0; it < my_tiles; ++it) {
+      zero_acc();
+#pragma nounroll
+      for (int kt = 0; kt < nk; ++kt, ++z) {
+        const char *la = smem + ((uint32_t)z & (S - 1)) * STAGE;
+        uint32_t dst = 0, kb = 0;  // the last k-step's DMA slot and K offset
+        const char *nla = smem;    // and where slice z + 1 sits
+        bool live = false;
+#pragma unroll
+        for (int ks = 0; ks + 1 < NKS; ++ks) {
+          const int cb = ks & 1;
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+            mma_one(cb, m);
+            if (m < NFK) frag_read(cb ^ 1, la, ks + 1, m);
+            if (ks == NKS - 2 && m == NFK) {
+              // the ring's bookkeeping, between MFMAs that carry no read
+              if (++kn == nk) { kn = 0; ++in; }
+              live = z + S < nz;
+              dst = sbase + ((uint32_t)z & (S - 1)) * STAGE;  // slot of slices z and z + S
+              kb = live ? (uint32_t)kn * RB : kOOB;           // past the end: as issue_past
+              nla = smem + ((uint32_t)(z + 1) & (S - 1)) * STAGE;
+            }
+            if (ks == NKS - 2 && m == NM - 3) {
+              // this wave's reads of slot z % S are done (the wait covers
+              // them); slice z + 1 has landed once every wave is here
+              if (z + 1 <= st_until) wait_vm<vm_cap((S - 2) * PER + NST)>();
+              else wait_vm<vm_cap((S - 2) * PER)>();
+              bar();
+              // (uniform) a new tile's load offsets and metadata, after the
+              // barrier: its metadata slot may be the one an epilogue just read
+              if (live && kn == 0) setup_b(in), setup_a(in);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        constexpr int cb = (NKS - 1) & 1;
+        // last k-step: the DMA loads of slice z + S and the reads of slice
+        // z + 1's first fragments, between its MFMAs
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          mma_one(cb, m);
+          // memory instruction q follows MFMA q * NM / NOPS
+#pragma unroll
+          for (int q = 0; q < NOPS; ++q) {
+            if (q * NM / NOPS != m) continue;
+            if (q < JB) dma16a(rb, dst + wb + q * 1024, vb[q], kb);
+            else if (q < JB + JA) dma16a(ra, dst + wa + (q - JB) * 1024, va[q - JB], kb);
+            else frag_read(cb ^ 1, nla, 0, q - JB - JA);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      epilogue(z - 1);
+    }
+    wait_vm<0>();  // the loads past the end of the stream have landed
   } else {
     for (int z = 0; z < nz; ++z) {
       wait_slice(z);
@@ -612,6 +748,20 @@ __global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
   }
 }
 
+template <typename T, int NSETS, int EPI, int BM, int BN, int WM, int WN, int S, int RB,
+          bool WQ = false>
+__global__ __launch_bounds__(64 * WM * WN) void grouped_gemm(GemmArgs g) {
+  gemm_body<T, NSETS, EPI, BM, BN, WM, WN, S, RB, WQ>(g);
+}
+
+// The four-wave 256-row tiles: one wave a SIMD, which may then hold the whole
+// register file (256 accumulator registers for its 128-row block).
+template <typename T, int NSETS, int EPI, int BM, int BN, int WM, int WN, int S, int RB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_w4(
+    GemmArgs g) {
+  gemm_body<T, NSETS, EPI, BM, BN, WM, WN, S, RB, false>(g);
+}
+
 int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -635,6 +785,16 @@ using GatedL = Cfg<256, 128, 4, 2, 4, 64>;  // 8 waves, 64 x (64 + 64) each
 using GatedL2 = Cfg<256, 128, 4, 2, 2, 128>;
 using PlainL2 = Cfg<256, 256, 4, 2, 2, 128>;
 constexpr int kLongRowBytes = 6144;
+// The bf16 256-row tiles: four waves, one a SIMD, with 128 x (64 + 64) and
+// 128 x 128 register blocks.  They read a third fewer LDS bytes a MFMA than
+// the eight-wave tiles (whose LDS is busy 87 % of the time on the skewed
+// 64-expert layer), at the price of a loop in which every other instruction
+// has to issue between MFMAs.  Measured against the eight-wave tiles on that
+// layer (bit-identical): gated w13 3110 -> 3035 us with 64-byte slices in a
+// four-stage ring, plain w2 1840 -> 1690 us with 128-byte slices in a
+// two-stage ring (w2: 1750 us with 64-byte slices).
+using GatedB = Cfg<256, 128, 2, 2, 4, 64>;
+using PlainB = Cfg<256, 256, 2, 2, 2, 128>;
 using GatedM = Cfg<128, 128, 2, 4, 3, 128>; // 8 waves, 64 x (32 + 32) each
 // 96 - 176 rows an expert (the gpt-oss-sized layer at 2048-4096 tokens): one
 // 192-row plain tile holds all of an expert's rows, where 128-row tiles give
@@ -685,8 +845,12 @@ hipError_t launch_cfg(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
   if (grid > tiles) grid = tiles;
   grid = (grid + 7) / 8 * 8;  // whole XCD rounds; surplus workgroups get no tiles
   static_assert(LDS <= 160 * 1024, "LDS budget");
-  hipLaunchKernelGGL((grouped_gemm<T, NSETS, EPI, C::BM, C::BN, C::WM, C::WN, C::S, C::RB, WQ>),
-                     dim3((unsigned)grid), dim3(64 * C::WM * C::WN), 0, s, a);
+  if constexpr (C::WM * C::WN == 4 && C::BM == 256 && !WQ)
+    hipLaunchKernelGGL((grouped_gemm_w4<T, NSETS, EPI, C::BM, C::BN, C::WM, C::WN, C::S, C::RB>),
+                       dim3((unsigned)grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((grouped_gemm<T, NSETS, EPI, C::BM, C::BN, C::WM, C::WN, C::S, C::RB, WQ>),
+                       dim3((unsigned)grid), dim3(64 * C::WM * C::WN), 0, s, a);
   return hipGetLastError();
 }
 
@@ -757,13 +921,16 @@ hipError_t launch_t(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
         expected_tiles(M, E, a.Nout, PlainX::BM, PlainX::BN) >= cus)
       return launch_cfg<T, NSETS, EPI, PlainX>(a, M, E, s);
   }
-  // the 256-row tile, with 128-byte slices for long rows
-  // (bf16 only: fp32 layers keep the 64-byte slices)
+  // the 256-row tile: in bf16 the four-wave one (its loop takes rows of
+  // whole slices), else the eight-wave one with 128-byte slices for long
+  // bf16 rows; fp32 layers keep the 64-byte slices
   using L2 = typename std::conditional<NSETS == 2, GatedL2, PlainL2>::type;
+  using B4 = typename std::conditional<NSETS == 2, GatedB, PlainB>::type;
   auto launch_l = [&]() {
     if constexpr (std::is_same<T, bf16_t>::value) {
-      if ((int64_t)a.K * (int64_t)sizeof(T) >= kLongRowBytes)
-        return launch_cfg<T, NSETS, EPI, L2>(a, M, E, s);
+      const int64_t rowb = (int64_t)a.K * (int64_t)sizeof(T);
+      if (rowb % B4::RB == 0) return launch_cfg<T, NSETS, EPI, B4>(a, M, E, s);
+      if (rowb >= kLongRowBytes) return launch_cfg<T, NSETS, EPI, L2>(a, M, E, s);
     }
     return launch_cfg<T, NSETS, EPI, L>(a, M, E, s);
   };

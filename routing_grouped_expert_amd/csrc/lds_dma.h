@@ -63,6 +63,24 @@ static __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char *lds
       : "memory", "m0");
 }
 
+// dma16 to LDS byte address `lds` (wave-uniform) with a wave-uniform byte
+// offset added to voff in the scalar offset field: no pointer conversion and
+// no per-lane add for a slice's position along K.
+static __device__ __forceinline__ void dma16a(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t voff,
+                                              uint32_t soff) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "buffer_load_dwordx4 %0, %1, %3 offen lds"
+      :
+      : "v"(voff), "s"(r), "s"(lds), "s"(soff)
+      : "memory", "m0");
+}
+
+// LDS byte address of a pointer into LDS.
+static __device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const void __attribute__((address_space(3))) *)p;
+}
+
 // dma16 with the non-temporal cache policy, for operands streamed once.
 static __device__ __forceinline__ void dma16_nt(__amdgpu_buffer_rsrc_t r, char *lds, uint32_t voff) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(void __attribute__((address_space(3))) *)lds;
