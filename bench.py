@@ -219,7 +219,10 @@ class ClockSampler:
         v = sorted(m for t, m in self.samples if t0 is not None and t1 is not None and t0 <= t <= t1)
         if not v:
             return {"median_mhz": None, "error": self.error or "no samples in the timed region"}
-        return {"median_mhz": round(v[len(v) // 2]), "min_mhz": round(v[0]),
+        # p10 / p90 as well: a sample can land in a gap between launches,
+        # where the clock drops at once
+        return {"median_mhz": round(v[len(v) // 2]), "p10_mhz": round(v[len(v) // 10]),
+                "p90_mhz": round(v[(9 * len(v)) // 10]), "min_mhz": round(v[0]),
                 "max_mhz": round(v[-1]), "samples": len(v)}
 
 
