@@ -11,6 +11,8 @@
 // adds nothing; a token with no slot in the share gets a zero row.
 #include "moe_common.h"
 
+#include <type_traits>
+
 namespace moe {
 namespace {
 
@@ -39,7 +41,13 @@ __device__ __forceinline__ u32x4_t pack_chunk(const float (&acc)[4], float) {
   return o;
 }
 
-template <typename T>
+// KK: the number of slots when it is known at compile time (2, 4, 6, 8): all
+// KK index loads and then all KK row loads go out back to back; 0: any k.
+// The sum runs in slot order either way, so both give the same bits.  The
+// expert rows are read once and the output written once, so both go
+// non-temporal: on the skewed 64-expert layer (16384 tokens, k = 8, 1 GB of
+// rows) 242 -> 219 us, fp32 k = 6 94 -> 81 us.
+template <typename T, int KK>
 __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y,
                                                       const int32_t *__restrict__ row_sorted,
                                                       T *__restrict__ out, int64_t N, int K,
@@ -53,11 +61,28 @@ __global__ __launch_bounds__(256) void combine_kernel(const T *__restrict__ y,
   float acc[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) acc[i] = 0.f;
-  for (int j = 0; j < K; ++j) {
-    const int64_t p = row_sorted[t * K + j];
-    if (p >= 0) add_chunk(acc, *reinterpret_cast<const u32x4_t *>(y + p * H + (int64_t)c * CH), T());
+  if constexpr (KK > 0) {
+    int32_t p[KK];
+#pragma unroll
+    for (int j = 0; j < KK; ++j) p[j] = row_sorted[t * KK + j];
+    u32x4_t v[KK];
+#pragma unroll
+    for (int j = 0; j < KK; ++j)
+      v[j] = p[j] >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(
+                             y + (int64_t)p[j] * H + (int64_t)c * CH))
+                       : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < KK; ++j)
+      if (p[j] >= 0) add_chunk(acc, v[j], T());
+  } else {
+    for (int j = 0; j < K; ++j) {
+      const int64_t p = row_sorted[t * K + j];
+      if (p >= 0)
+        add_chunk(acc, *reinterpret_cast<const u32x4_t *>(y + p * H + (int64_t)c * CH), T());
+    }
   }
-  *reinterpret_cast<u32x4_t *>(out + t * H + (int64_t)c * CH) = pack_chunk(acc, T());
+  __builtin_nontemporal_store(pack_chunk(acc, T()),
+                              reinterpret_cast<u32x4_t *>(out + t * H + (int64_t)c * CH));
 }
 
 // Top-1 layer of an expert-parallel share: GEMM2 writes the rows of tokens
@@ -88,14 +113,24 @@ hipError_t launch_combine(const void *y_sorted, const int32_t *row_sorted, void 
   const int ch = dt == MOE_BF16 ? 8 : 4;
   const int64_t total = n_tokens * (hidden / ch);
   const unsigned blocks = (unsigned)((total + 255) / 256);
-  if (dt == MOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s,
-                       reinterpret_cast<const bf16_t *>(y_sorted), row_sorted,
-                       reinterpret_cast<bf16_t *>(out), n_tokens, topk, hidden);
-  else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, s,
-                       reinterpret_cast<const float *>(y_sorted), row_sorted,
-                       reinterpret_cast<float *>(out), n_tokens, topk, hidden);
+  auto go = [&](auto kk) {
+    constexpr int KK = decltype(kk)::value;
+    if (dt == MOE_BF16)
+      hipLaunchKernelGGL((combine_kernel<bf16_t, KK>), dim3(blocks), dim3(256), 0, s,
+                         reinterpret_cast<const bf16_t *>(y_sorted), row_sorted,
+                         reinterpret_cast<bf16_t *>(out), n_tokens, topk, hidden);
+    else
+      hipLaunchKernelGGL((combine_kernel<float, KK>), dim3(blocks), dim3(256), 0, s,
+                         reinterpret_cast<const float *>(y_sorted), row_sorted,
+                         reinterpret_cast<float *>(out), n_tokens, topk, hidden);
+  };
+  switch (topk) {
+    case 2: go(std::integral_constant<int, 2>()); break;
+    case 4: go(std::integral_constant<int, 4>()); break;
+    case 6: go(std::integral_constant<int, 6>()); break;
+    case 8: go(std::integral_constant<int, 8>()); break;
+    default: go(std::integral_constant<int, 0>()); break;
+  }
   return hipGetLastError();
 }
 
