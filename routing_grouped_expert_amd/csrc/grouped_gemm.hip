@@ -594,19 +594,22 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
     // instruction follows an MFMA (about seven free issue slots each).
     //  * k-step ks < NKS - 1: the fragments of k-step ks + 1 are read, one
     //    after each MFMA.
-    //  * last k-step: the wave waits for slice z + 1, meets the other waves
-    //    at the barrier (after which none reads slot z % S again), then each
-    //    MFMA is followed by one of the DMA loads of slice z + S into that
-    //    slot or one read of slice z + 1's first fragments.
+    //  * k-step NKS - 2, once its reads are out: the ring's bookkeeping, the
+    //    wait for slice z + 1 and the barrier (after which no wave reads slot
+    //    z % S again: its last fragments are in registers), then the first
+    //    DMA loads of slice z + S into that slot, one after each MFMA.
+    //  * last k-step: the remaining DMA loads, then the reads of slice
+    //    z + 1's first fragments, spread over its MFMAs (DMA loads bunched in
+    //    one k-step stall their issue: spreading them over two measured 1-2 %
+    //    faster on every 256-row layer).
     // Every slice takes that path: a slice that starts a tile first sets up
     // the tile's load offsets, and slices past the end of the stream load
     // through an empty buffer (zeros into a slot nobody reads), so each wait
     // is one count.  Rows hold whole slices (no K tail: the host checks).
     constexpr int NM = TM * TN * NSETS;  // MFMAs a k-step
     constexpr int NFK = TM + TN * NSETS; // fragment reads a k-step
-    constexpr int NOPS = JA + JB + NFK;  // memory instructions of the last k-step
-    static_assert(!BIG || (NFK <= NM && NOPS <= 2 * NM && NKS % 2 == 0),
-                  "at most two memory instructions a MFMA; k-step pairs");
+    constexpr int NDMA = JA + JB;         // DMA loads a slice
+    static_assert(!BIG || (NFK + 2 <= NM && NKS % 2 == 0), "reads, bookkeeping and barrier in a k-step; k-step pairs");
     Frag fa[2][TM], fb[2][TN][NSETS];
     auto frag_read = [&](int buf, const char *la, int ks, int f) {
       if (f < TM) {
@@ -659,9 +662,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
 #pragma nounroll
       for (int kt = 0; kt < nk; ++kt, ++z) {
         const char *la = smem + ((uint32_t)z & (S - 1)) * STAGE;
-        uint32_t dst = 0, kb = 0;  // the last k-step's DMA slot and K offset
-        const char *nla = smem;    // and where slice z + 1 sits
+        uint32_t dst = 0, kb = 0;  // the DMA slot and K offset of slice z + S
+        const char *nla = smem;    // where slice z + 1 sits
         bool live = false;
+        auto dma = [&](int q) {  // DMA load q of slice z + S (B rows, then A rows)
+          if (q < JB) dma16a(rb, dst + wb + q * 1024, vb[q], kb);
+          else dma16a(ra, dst + wa + (q - JB) * 1024, va[q - JB], kb);
+        };
 #pragma unroll
         for (int ks = 0; ks + 1 < NKS; ++ks) {
           const int cb = ks & 1;
@@ -669,40 +676,45 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
           for (int m = 0; m < NM; ++m) {
             mma_one(cb, m);
             if (m < NFK) frag_read(cb ^ 1, la, ks + 1, m);
-            if (ks == NKS - 2 && m == NFK) {
-              // the ring's bookkeeping, between MFMAs that carry no read
-              if (++kn == nk) { kn = 0; ++in; }
-              live = z + S < nz;
-              dst = sbase + ((uint32_t)z & (S - 1)) * STAGE;  // slot of slices z and z + S
-              kb = live ? (uint32_t)kn * RB : kOOB;           // past the end: as issue_past
-              nla = smem + ((uint32_t)(z + 1) & (S - 1)) * STAGE;
-            }
-            if (ks == NKS - 2 && m == NM - 3) {
-              // this wave's reads of slot z % S are done (the wait covers
-              // them); slice z + 1 has landed once every wave is here
-              if (z + 1 <= st_until) wait_vm<vm_cap((S - 2) * PER + NST)>();
-              else wait_vm<vm_cap((S - 2) * PER)>();
-              bar();
-              // (uniform) a new tile's load offsets and metadata, after the
-              // barrier: its metadata slot may be the one an epilogue just read
-              if (live && kn == 0) setup_b(in), setup_a(in);
+            if (ks == NKS - 2) {
+              if (m == NFK) {
+                // the ring's bookkeeping, between MFMAs that carry no read
+                if (++kn == nk) { kn = 0; ++in; }
+                live = z + S < nz;
+                dst = sbase + ((uint32_t)z & (S - 1)) * STAGE;  // slot of slices z and z + S
+                kb = live ? (uint32_t)kn * RB : kOOB;           // past the end: as issue_past
+                nla = smem + ((uint32_t)(z + 1) & (S - 1)) * STAGE;
+              } else if (m == NFK + 1) {
+                // this wave's reads of slot z % S are done (the wait covers
+                // them); slice z + 1 has landed once every wave is here
+                if (z + 1 <= st_until) wait_vm<vm_cap((S - 2) * PER + NST)>();
+                else wait_vm<vm_cap((S - 2) * PER)>();
+                bar();
+                // (uniform) a new tile's load offsets and metadata, after the
+                // barrier: its metadata slot may be the one an epilogue just read
+                if (live && kn == 0) setup_b(in), setup_a(in);
+              } else if (m > NFK + 1) {
+                dma(m - NFK - 2);  // the first DMA loads go out here already
+              }
             }
             __builtin_amdgcn_sched_barrier(0);
           }
         }
         constexpr int cb = (NKS - 1) & 1;
-        // last k-step: the DMA loads of slice z + S and the reads of slice
-        // z + 1's first fragments, between its MFMAs
+        // last k-step: the remaining DMA loads of slice z + S, then the reads
+        // of slice z + 1's first fragments, spread over its MFMAs
+        constexpr int D0 = NM - NFK - 2;            // DMA loads issued in the k-step before
+        constexpr int NL = NDMA - D0 + NFK;         // memory instructions of this k-step
+        static_assert(!BIG || (D0 >= 0 && D0 <= NDMA && NL <= 2 * NM), "memory instructions a MFMA");
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
           mma_one(cb, m);
-          // memory instruction q follows MFMA q * NM / NOPS
+          // memory instruction q follows MFMA q * NM / NL
 #pragma unroll
-          for (int q = 0; q < NOPS; ++q) {
-            if (q * NM / NOPS != m) continue;
-            if (q < JB) dma16a(rb, dst + wb + q * 1024, vb[q], kb);
-            else if (q < JB + JA) dma16a(ra, dst + wa + (q - JB) * 1024, va[q - JB], kb);
-            else frag_read(cb ^ 1, nla, 0, q - JB - JA);
+          for (int q = 0; q < NL; ++q) {
+            if (q * NM / NL != m) continue;
+            if (q < NDMA - D0) dma(D0 + q);
+            else frag_read(cb ^ 1, nla, 0, q - (NDMA - D0));
           }
           __builtin_amdgcn_sched_barrier(0);
         }
