@@ -710,13 +710,13 @@ def main():
     t0 = time.perf_counter()
     st = step_stats(p_fwd, K, stream)
     wall = time.perf_counter() - t0
+    clock.end()  # the clock over the timed steps only (graph capture below idles the GPU)
+    clock.stop()
     ms_step = st["mean"]
     # stages (the routing metadata of the last step stays valid for the others),
     # each timed as a captured graph of K calls on a stream of its own
     gstream = torch.cuda.Stream(device=dev)
     stage_ms = {name: graph_timed(fn, K, gstream) for name, fn in stage_calls(gstream)}
-    clock.end()
-    clock.stop()
     eager = dict(stage_calls(stream))
     p_comb = eager.get("combine")
     cold_fns = [p_fwd, p_route] + ([p_comb] if not mx and k > 1 else [])
