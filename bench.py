@@ -219,8 +219,8 @@ class ClockSampler:
         v = sorted(m for t, m in self.samples if t0 is not None and t1 is not None and t0 <= t <= t1)
         if not v:
             return {"median_mhz": None, "error": self.error or "no samples in the timed region"}
-        # p10 / p90 as well: a sample can land in a gap between launches,
-        # where the clock drops at once
+        # p10 / p90 as well: the reading moves in steps (the SMI table holds a
+        # value for tens to hundreds of milliseconds)
         return {"median_mhz": round(v[len(v) // 2]), "p10_mhz": round(v[len(v) // 10]),
                 "p90_mhz": round(v[(9 * len(v)) // 10]), "min_mhz": round(v[0]),
                 "max_mhz": round(v[-1]), "samples": len(v)}
@@ -618,6 +618,9 @@ def main():
         return bench_decode_stack(args, args.workload)
     spec = workload(args.workload)
     mx = spec.name.endswith("_mxfp4")
+    # the SMI clock reading is coarse and its library slow to start: sample
+    # from before the layer is built, keep only the timed steps' samples
+    clock = ClockSampler().start()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     layer = make_layer(spec)
@@ -702,7 +705,6 @@ def main():
         del g
         return best
 
-    clock = ClockSampler().start()
     for _ in range(W):
         p_fwd()
     torch.cuda.synchronize()
