@@ -346,17 +346,19 @@ def cold_stats(fns, reps: int, stream, dev) -> list:
 
 
 def bench_route_only(args, name: str):
-    """Routing-metadata workloads: route_n<N>_e<E>_k<k> (bf16 logits)."""
+    """Routing-metadata workloads: route_n<N>_e<E>_k<k> (bf16 logits), with a
+    _f32 suffix fp32 logits and weights."""
     import re
-    m = re.fullmatch(r"route_n(\d+)_e(\d+)_k(\d+)", name)
+    m = re.fullmatch(r"route_n(\d+)_e(\d+)_k(\d+)(_f32)?", name)
     if not m:
         raise SystemExit(f"unknown workload {name!r}")
-    n, e, k = (int(v) for v in m.groups())
+    n, e, k = (int(v) for v in m.groups()[:3])
+    f32 = m.group(4) is not None
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    lg_cpu = routing_logits(n, e, "bf16", seed=0)
+    lg_cpu = routing_logits(n, e, "f32" if f32 else "bf16", seed=0)
     lg = lg_cpu.to(dev)
-    routing = Routing.empty(n, e, k, torch.bfloat16, dev)
+    routing = Routing.empty(n, e, k, torch.float32 if f32 else torch.bfloat16, dev)
     ws = torch.empty(max(1, moe_workspace_bytes(n, e, k)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     p_route = prepare_route(lg, k, routing=routing, workspace=ws, stream=stream)
@@ -367,14 +369,15 @@ def bench_route_only(args, name: str):
     wall = time.perf_counter() - t0
     cold = cold_stats([p_route], 20, stream, dev)[0]
     words = (e + 31) // 32
-    nbytes = n * e * 2 + n * k * (4 + 2 + 4 + 4 + 2) + n * words * 4 + (2 * e + 1) * 4
+    es = 4 if f32 else 2  # logit and weight bytes
+    nbytes = n * e * es + n * k * (4 + es + 4 + 4 + es) + n * words * 4 + (2 * e + 1) * 4
     ach = nbytes / (st["mean"] * 1e-3) / 1e9
     result = {
         "metric": METRIC, "value": round(n / (st["mean"] * 1e-3), 1), "unit": "tokens/s",
         "n_gpus": 1, "steps": st["steps"], "warmup": args.warmup,
         "ms_per_step": round(st["mean"], 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded Gaussian logits)",
-        "config": {"workload": f"{name}: routing metadata only, N={n} E={e} k={k} bf16 logits"},
+        "vs_baseline": None, "dtype": "f32" if f32 else "bf16", "data": "synthetic (seeded Gaussian logits)",
+        "config": {"workload": f"{name}: routing metadata only, N={n} E={e} k={k} {'fp32' if f32 else 'bf16'} logits"},
         "routing_us_per_layer": round(st["mean"] * 1e3, 2),
         "step_us": {q: round(st[q] * 1e3, 2) for q in ("p10", "p50", "p90")},
         "cold_routing_us": round(cold * 1e3, 2),
@@ -390,7 +393,7 @@ def bench_route_only(args, name: str):
         sample = min(n, 4096)
         t0, reps = time.perf_counter(), 0
         while True:
-            oracle.route(lg_cpu[:sample], k, "bf16")
+            oracle.route(lg_cpu[:sample], k, "f32" if f32 else "bf16")
             reps += 1
             if time.perf_counter() - t0 >= args.cpu_seconds:
                 break

@@ -919,10 +919,15 @@ __global__ __launch_bounds__(THREADS) void route_topk_rank(
 // in earlier blocks) + rank in the block.
 constexpr int kScatterThreads = 1024;
 
-template <typename T, int NTB>
+// PRE: route_count_scan has already turned the count rows into exclusive
+// prefixes over the blocks and written the totals to tot, so the workgroup
+// reads its own column and the totals (linear in the number of blocks
+// overall) instead of summing the rows (quadratic).
+template <typename T, int NTB, bool PRE = false>
 __global__ __launch_bounds__(kScatterThreads) void route_scatter(
     int64_t N, int K, int lo, int nl, int nblocks, int nbp, const int32_t *__restrict__ blk_cnt,
-    const uint8_t *__restrict__ blk_rank, const int32_t *__restrict__ topk_idx,
+    const int32_t *__restrict__ tot, const uint8_t *__restrict__ blk_rank,
+    const int32_t *__restrict__ topk_idx,
     const T *__restrict__ topk_w, int32_t *__restrict__ col_sum, int32_t *__restrict__ offsets,
     int32_t *__restrict__ col_sorted, int32_t *__restrict__ row_sorted,
     T *__restrict__ gate_scal) {
@@ -950,8 +955,15 @@ __global__ __launch_bounds__(kScatterThreads) void route_scatter(
       }
     }
   }
-  // thread (e, part): part-th share of row e, in 4-int chunks
   const int E = nl;  // counts, offsets and positions are over the local experts
+  if constexpr (PRE) {
+    for (int x = tid; x < E; x += kScatterThreads) {
+      s_base[x] = blk_cnt[(int64_t)x * nbp + b];
+      s_tot[x] = tot[x];
+    }
+    __syncthreads();
+  } else {
+  // thread (e, part): part-th share of row e, in 4-int chunks
   const int parts = min(kParts, kScatterThreads / E);
   const int e = tid % E, part = tid / E;
   const int nch = nbp / 4;                       // 16-byte chunks per row
@@ -989,6 +1001,7 @@ __global__ __launch_bounds__(kScatterThreads) void route_scatter(
     s_tot[x] = all;
   }
   __syncthreads();
+  }
   block_exclusive_scan(s_tot, s_off, E);
   if (b == 0) {
     for (int x = tid; x <= E; x += kScatterThreads) {
@@ -1234,6 +1247,12 @@ __global__ __launch_bounds__(64 * kLaneWaves) void route_lane_topk(
 // exclusive prefixes over the blocks, in place; tot[l] gets the total.  A
 // round covers 1024 blocks (16 a lane, all loaded before any is used).
 constexpr int kScanWaves = 4;
+// The multi-block scatter sums every earlier block's counts itself up to this
+// many blocks (65536 tokens in 256-token blocks), and reads prefixes that
+// route_count_scan made beyond (fp32 logits, expert counts that are no power
+// of two): 131072 fp32-routed tokens over 128 experts sum 512 x 128 counts in
+// each of 512 workgroups otherwise.
+constexpr int64_t kScanBlocks = 256;
 __global__ __launch_bounds__(64 * kScanWaves) void route_count_scan(int32_t *__restrict__ blk_cnt,
                                                                     int nbp, int nb, int nl,
                                                                     int32_t *__restrict__ tot) {
@@ -1561,14 +1580,23 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
   }
   const int64_t nb = (N + ntb - 1) / ntb;
   const int nbp = (int)((nb + 3) / 4 * 4);
+  // scratch: block counts [nl][nbp], the totals, the entries' in-block ranks
   int32_t *blk_cnt = reinterpret_cast<int32_t *>(scratch);
-  uint8_t *blk_rank = reinterpret_cast<uint8_t *>(scratch) + align256((size_t)nbp * E * 4);
-  auto blocks = [&](auto topk_kern, auto scatter_kern, int tt) {
+  int32_t *tot = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(scratch) +
+                                             align256((size_t)nbp * E * 4));
+  uint8_t *blk_rank = reinterpret_cast<uint8_t *>(tot) + align256((size_t)E * 4);
+  // past kScanBlocks blocks the counts are prefix-summed once (route_count_scan)
+  // instead of by every scatter workgroup
+  const bool pre = nb > kScanBlocks;
+  auto blocks = [&](auto topk_kern, auto scatter_kern, auto scatter_pre, int tt) {
     hipLaunchKernelGGL(topk_kern, dim3((unsigned)nb), dim3(tt), 0, s, logits, N, E, K, lo, nl,
                        logG, vec, r->topk_idx, tw, r->bitmatrix, blk_cnt, nbp, blk_rank);
-    hipLaunchKernelGGL(scatter_kern, dim3((unsigned)nb), dim3(kScatterThreads), 0, s, N, K, lo, nl,
-                       (int)nb, nbp, blk_cnt, blk_rank, r->topk_idx, tw, r->col_sum, r->offsets,
-                       r->col_sorted, r->row_sorted, gs);
+    if (pre)
+      hipLaunchKernelGGL(route_count_scan, dim3((unsigned)((nl + kScanWaves - 1) / kScanWaves)),
+                         dim3(64 * kScanWaves), 0, s, blk_cnt, nbp, (int)nb, nl, tot);
+    hipLaunchKernelGGL(pre ? scatter_pre : scatter_kern, dim3((unsigned)nb), dim3(kScatterThreads),
+                       0, s, N, K, lo, nl, (int)nb, nbp, blk_cnt, tot, blk_rank, r->topk_idx, tw,
+                       r->col_sum, r->offsets, r->col_sorted, r->row_sorted, gs);
   };
   // 64-token blocks of tokens that need at most four lanes each (up to 32 bf16
   // or 16 fp32 experts) fill a quarter of a 1024-thread workgroup in the top-k
@@ -1576,13 +1604,16 @@ hipError_t launch_route_t(const T *logits, int64_t N, int E, int K, int lo, int 
   // E = 32 at 16384 tokens 12.6 -> 10.9 us; the scatter kept at 1024 threads
   // measured best)
   if (ntb == 64 && logG <= 2)
-    blocks(route_topk_rank<T, 1, 64, 256>, route_scatter<T, 64>, 256);
+    blocks(route_topk_rank<T, 1, 64, 256>, route_scatter<T, 64>, route_scatter<T, 64, true>, 256);
   else if (ntb == 64)
-    blocks(route_topk_rank<T, 1, 64>, route_scatter<T, 64>, kTopkThreads);
+    blocks(route_topk_rank<T, 1, 64>, route_scatter<T, 64>, route_scatter<T, 64, true>,
+           kTopkThreads);
   else if (wide)
-    blocks(route_topk_rank<T, 2, kRouteTokens>, route_scatter<T, kRouteTokens>, kTopkThreads);
+    blocks(route_topk_rank<T, 2, kRouteTokens>, route_scatter<T, kRouteTokens>,
+           route_scatter<T, kRouteTokens, true>, kTopkThreads);
   else
-    blocks(route_topk_rank<T, 1, kRouteTokens>, route_scatter<T, kRouteTokens>, kTopkThreads);
+    blocks(route_topk_rank<T, 1, kRouteTokens>, route_scatter<T, kRouteTokens>,
+           route_scatter<T, kRouteTokens, true>, kTopkThreads);
   return hipGetLastError();
 }
 

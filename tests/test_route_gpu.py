@@ -60,6 +60,10 @@ EDGE = [
     (32768, 8, 1, "bf16"),   # one chunk a row, top-1
     (70001, 64, 8, "bf16"),  # more than 1024 blocks: two rounds of the count scan
     (32800, 40, 3, "bf16"),  # not a power of two: back on the cooperative top-k
+    # cooperative top-k past 256 blocks of 256 tokens: count rows prefix-summed once
+    (65536 + 257, 40, 3, "bf16"),   # 258 blocks, ragged last one, odd expert count
+    (70001, 128, 4, "f32"),         # fp32 logits
+    (300000, 32, 8, "f32"),         # 1172 blocks: two rounds of the count scan
 ]
 
 
