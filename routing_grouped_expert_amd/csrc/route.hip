@@ -1199,25 +1199,30 @@ __global__ __launch_bounds__(64 * kLaneWaves) void route_lane_topk(
   }
   // per local expert l: the mask of this block's tokens that chose it (ballot);
   // lane l % 64 keeps it, then the masks go to LDS for the rank look-ups
-  unsigned long long mine[kMaxExperts / 64];
+  // lane (32 w + bit) % 64 keeps expert 32 w + bit's mask, taken by a select
+  // (no branch, no exec juggling); bits past nl were never set, so their
+  // masks are zero and are not stored
+  uint32_t mlo[kMaxExperts / 64], mhi[kMaxExperts / 64];
 #pragma unroll
-  for (int q = 0; q < kMaxExperts / 64; ++q) mine[q] = 0ull;
+  for (int q = 0; q < kMaxExperts / 64; ++q) mlo[q] = mhi[q] = 0u;
 #pragma unroll
   for (int w = 0; w < kLaneMaxWords; ++w) {
-    if (w < words) {
+    if (w < words) {  // (uniform)
       const uint32_t wv = word[w];
-      const int nb_w = min(32, nl - 32 * w);
-      const int own = lane - 32 * (w & 1);  // the bit whose expert this lane keeps
 #pragma unroll
       for (int bit = 0; bit < 32; ++bit) {
-        if (bit < nb_w) {  // (uniform)
-          const unsigned long long m = __ballot((wv >> bit) & 1u);
-          // lane (32 w + bit) % 64 keeps expert 32 w + bit's mask
-          if (own == bit) mine[w >> 1] = m;
-        }
+        const unsigned long long m = __ballot((wv >> bit) & 1u);
+        const int dl = 32 * (w & 1) + bit;
+        const bool keep = lane == dl;
+        mlo[w >> 1] = keep ? (uint32_t)m : mlo[w >> 1];
+        mhi[w >> 1] = keep ? (uint32_t)(m >> 32) : mhi[w >> 1];
       }
     }
   }
+  unsigned long long mine[kMaxExperts / 64];
+#pragma unroll
+  for (int q = 0; q < kMaxExperts / 64; ++q)
+    mine[q] = (unsigned long long)mlo[q] | ((unsigned long long)mhi[q] << 32);
 #pragma unroll
   for (int q = 0; q < kMaxExperts / 64; ++q) {
     const int l = q * 64 + lane;

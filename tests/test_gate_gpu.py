@@ -86,7 +86,8 @@ GATE_CASES = [
     (5, 16, 8200, 2, "bf16"),       # split-K over 65 slices: three rounds of the group sum
     (5, 16, 32776, 2, "bf16"),      # more K-slices (257) than the split-K path takes: full prologue
     (8, 128, 2880, 4, "bf16"),      # split-K sums past the prologue's share: reduction kernel
-    (4, 32, 2880, 4, "bf16"),       # split-K sums added up in the routing kernel's prologue
+    (4, 32, 2880, 4, "bf16"),       # four tokens: still a wave per expert row
+    (6, 32, 2880, 4, "bf16"),       # split-K sums added up in the routing kernel's prologue
     (40, 256, 4096, 8, "bf16"),     # split-K with the widest expert bucket
     (1, 256, 7168, 8, "bf16"),      # DeepSeek-sized router, decode (a wave per expert row)
     (64, 256, 7168, 8, "bf16"),     # the same at the largest split-K batch
