@@ -158,14 +158,15 @@ def host_info() -> dict:
 
 class ClockSampler:
     """Samples the GPU's current graphics clock (MHz, the mean over the XCDs)
-    from the SMI library on a background thread.  Started before the warm-up so
-    the library is up when the timed region begins; only samples taken between
-    begin() and end() count.  Reports their median and range (None when the SMI
-    library is not usable here)."""
+    from the SMI library on a background thread.  Started early, since the
+    library is slow to start; only samples taken in the clock pass (sustained())
+    count.  Reports their median and range (None when the SMI library is not
+    usable here)."""
 
     def __init__(self, period_s: float = 0.005):
         import threading
         self.period = period_s
+        self.seconds, self.settle = 0.0, 0.0
         self.samples = []           # (perf_counter time, MHz)
         self.window = [None, None]
         self.error = None
@@ -204,13 +205,30 @@ class ClockSampler:
         self._thread.start()
         return self
 
-    def begin(self):
-        self.window[0] = time.perf_counter()
-
-    def end(self):
+    def sustained(self, fn, seconds: float, settle: float = 1.2):
+        """Runs fn back to back for `seconds` (after the timed region) and keeps
+        the samples taken after the first `settle` seconds.  The SMI table is
+        refreshed about once a second and holds its value in between, so a timed
+        region of a few hundred milliseconds mostly reads the clock from before
+        the load; this pass gives the clock the same step sustains."""
+        self.seconds, self.settle = seconds, min(settle, seconds / 2)
+        if seconds <= 0:
+            self.error = self.error or "clock pass disabled"
+            self._stop.set()
+            return
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        # launch in chunks of ~20 ms of work, synchronising between them
+        chunk = max(1, min(10000, int(0.02 / max(time.perf_counter() - t, 1e-6))))
+        t0 = time.perf_counter()
+        self.window[0] = t0 + self.settle
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(chunk):
+                fn()
+            torch.cuda.synchronize()
         self.window[1] = time.perf_counter()
-
-    def stop(self):
         self._stop.set()
         self._thread.join(timeout=5)
 
@@ -218,12 +236,14 @@ class ClockSampler:
         t0, t1 = self.window
         v = sorted(m for t, m in self.samples if t0 is not None and t1 is not None and t0 <= t <= t1)
         if not v:
-            return {"median_mhz": None, "error": self.error or "no samples in the timed region"}
-        # p10 / p90 as well: the reading moves in steps (the SMI table holds a
-        # value for tens to hundreds of milliseconds)
-        return {"median_mhz": round(v[len(v) // 2]), "p10_mhz": round(v[len(v) // 10]),
-                "p90_mhz": round(v[(9 * len(v)) // 10]), "min_mhz": round(v[0]),
-                "max_mhz": round(v[-1]), "samples": len(v)}
+            return {"median_mhz": None, "error": self.error or "no samples in the clock pass"}
+        # the reading moves in steps (the SMI table holds a value for up to a
+        # second), so few distinct values: median and range
+        return {"median_mhz": round(v[len(v) // 2]), "min_mhz": round(v[0]),
+                "max_mhz": round(v[-1]), "samples": len(v),
+                "source": f"SMI graphics clock (mean over XCDs) while the step ran back to back "
+                          f"for {self.seconds:g} s after the timed region, samples after the "
+                          f"first {self.settle:g} s"}
 
 
 def _oracle_threads() -> int:
@@ -354,6 +374,7 @@ def bench_route_only(args, name: str):
         raise SystemExit(f"unknown workload {name!r}")
     n, e, k = (int(v) for v in m.groups()[:3])
     f32 = m.group(4) is not None
+    clock = ClockSampler().start()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     lg_cpu = routing_logits(n, e, "f32" if f32 else "bf16", seed=0)
@@ -367,6 +388,7 @@ def bench_route_only(args, name: str):
     t0 = time.perf_counter()
     st = step_stats(p_route, args.steps, stream)
     wall = time.perf_counter() - t0
+    clock.sustained(p_route, args.clock_seconds)
     cold = cold_stats([p_route], 20, stream, dev)[0]
     words = (e + 31) // 32
     es = 4 if f32 else 2  # logit and weight bytes
@@ -387,6 +409,8 @@ def bench_route_only(args, name: str):
                      "kernel": "routing (all routing kernels of one moe_route call)",
                      "traffic": None, "algorithmic_bytes": nbytes,
                      "avg_launch_us": round(st["mean"] * 1e3, 2)},
+        "gpu_clock": clock.summary(),
+        "host": host_info(),
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -415,6 +439,7 @@ def bench_gate_route(args, name: str):
     if not m:
         raise SystemExit(f"unknown workload {name!r}")
     n, e, h, k = (int(v) for v in m.groups())
+    clock = ClockSampler().start()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     x_cpu, w_cpu = router_inputs(n, e, h, "bf16", seed=0)
@@ -431,6 +456,7 @@ def bench_gate_route(args, name: str):
     st = step_stats(p_gate, args.steps, stream)
     wall = time.perf_counter() - t0
     st_route = step_stats(p_route, args.steps, stream)
+    clock.sustained(p_gate, args.clock_seconds)
     cold = cold_stats([p_gate], 20, stream, dev)[0]
     words = (e + 31) // 32
     route_b = n * e * 2 + n * k * (4 + 2 + 4 + 4 + 2) + n * words * 4 + (2 * e + 1) * 4
@@ -454,6 +480,8 @@ def bench_gate_route(args, name: str):
         "cold_routing_us": round(cold * 1e3, 2),
         "wall_ms_per_step": round(wall / st["steps"] * 1e3, 4),
         "roofline": roof,
+        "gpu_clock": clock.summary(),
+        "host": host_info(),
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -485,6 +513,7 @@ def bench_decode_stack(args, name: str):
     L, n, mx = int(m.group(1)), int(m.group(2)), m.group(3) is not None
     e, k, h, i = 32, 4, 2880, 2880
     prm = {"alpha": 1.702, "beta": 1.0, "limit": 7.0}
+    clock = ClockSampler().start()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     gen = torch.Generator(device=dev)
@@ -553,6 +582,7 @@ def bench_decode_stack(args, name: str):
     torch.cuda.synchronize()
     same = bool(torch.equal(bufs[-1], ref))
     st_graph = step_stats(g.replay, args.steps, stream)
+    clock.sustained(g.replay, args.clock_seconds)
     # weights of the experts each layer's tokens touch, read once (counted in an
     # untimed eager pass that reads every layer's histogram)
     touched = []
@@ -585,6 +615,8 @@ def bench_decode_stack(args, name: str):
                      "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
                      "kernel": "whole step (graph replay)", "traffic": None,
                      "algorithmic_bytes": nbytes, "avg_launch_us": round(ms * 1e3, 2)},
+        "gpu_clock": clock.summary(),
+        "host": host_info(),
     }
     print(json.dumps(result), flush=True)
 
@@ -597,6 +629,8 @@ def main():
     ap.add_argument("--workload", default="skewed_silu")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--clock-seconds", type=float, default=3.0,
+                    help="length of the clock pass after the timed region (0: none)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                     help="first copy MB mebibytes device to device three times: a plain copy "
                          "of known size that hardware byte counters can be scaled by")
@@ -621,8 +655,7 @@ def main():
         return bench_decode_stack(args, args.workload)
     spec = workload(args.workload)
     mx = spec.name.endswith("_mxfp4")
-    # the SMI clock reading is coarse and its library slow to start: sample
-    # from before the layer is built, keep only the timed steps' samples
+    # the SMI library is slow to start: start the sampler before the layer is built
     clock = ClockSampler().start()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -711,12 +744,10 @@ def main():
     for _ in range(W):
         p_fwd()
     torch.cuda.synchronize()
-    clock.begin()
     t0 = time.perf_counter()
     st = step_stats(p_fwd, K, stream)
     wall = time.perf_counter() - t0
-    clock.end()  # the clock over the timed steps only (graph capture below idles the GPU)
-    clock.stop()
+    clock.sustained(p_fwd, args.clock_seconds)
     ms_step = st["mean"]
     # stages (the routing metadata of the last step stays valid for the others),
     # each timed as a captured graph of K calls on a stream of its own
