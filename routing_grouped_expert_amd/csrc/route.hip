@@ -1048,10 +1048,10 @@ __global__ __launch_bounds__(kScatterThreads) void route_scatter(
 // t[j], x): one max and L - 1 median-of-three instructions a key, all from the
 // old list.  Three kernels:
 //  * route_lane_topk: 64-token blocks (one wave each, four a workgroup): top-k,
-//    softmax, topk_idx / topk_w / bitmatrix rows; then per block one ballot per
-//    local expert gives each expert's mask of tokens, whose popcount is the
-//    block's count (stored expert-major) and whose popcount below a lane is
-//    that entry's stable rank in the block.
+//    softmax, topk_idx / topk_w / bitmatrix rows; then each token ORs its bit
+//    into an LDS mask per chosen local expert, whose popcount is the block's
+//    count (stored expert-major) and whose popcount below a lane is that
+//    entry's stable rank in the block.
 //  * route_count_scan: one wave per expert turns its row of block counts into
 //    exclusive prefixes over the blocks (linear in the number of blocks) and
 //    stores the expert's total.
@@ -1197,43 +1197,35 @@ __global__ __launch_bounds__(64 * kLaneWaves) void route_lane_topk(
     for (int w = 0; w < kLaneMaxWords; ++w)
       if (w < words) bitmatrix[t * words + w] = word[w];
   }
-  // per local expert l: the mask of this block's tokens that chose it (ballot);
-  // lane l % 64 keeps it, then the masks go to LDS for the rank look-ups
-  // lane (32 w + bit) % 64 keeps expert 32 w + bit's mask, taken by a select
-  // (no branch, no exec juggling); bits past nl were never set, so their
-  // masks are zero and are not stored
-  uint32_t mlo[kMaxExperts / 64], mhi[kMaxExperts / 64];
-#pragma unroll
-  for (int q = 0; q < kMaxExperts / 64; ++q) mlo[q] = mhi[q] = 0u;
-#pragma unroll
-  for (int w = 0; w < kLaneMaxWords; ++w) {
-    if (w < words) {  // (uniform)
-      const uint32_t wv = word[w];
-#pragma unroll
-      for (int bit = 0; bit < 32; ++bit) {
-        const unsigned long long m = __ballot((wv >> bit) & 1u);
-        const int dl = 32 * (w & 1) + bit;
-        const bool keep = lane == dl;
-        mlo[w >> 1] = keep ? (uint32_t)m : mlo[w >> 1];
-        mhi[w >> 1] = keep ? (uint32_t)(m >> 32) : mhi[w >> 1];
-      }
-    }
-  }
-  unsigned long long mine[kMaxExperts / 64];
-#pragma unroll
-  for (int q = 0; q < kMaxExperts / 64; ++q)
-    mine[q] = (unsigned long long)mlo[q] | ((unsigned long long)mhi[q] << 32);
+  // per local expert l: the mask of this block's tokens that chose it, built
+  // in LDS by OR-ing each token's bit into the masks of the experts it chose
+  // (OR does not depend on the order of the updates, so every run builds the
+  // same masks); its popcount is the block's count, its popcount below a lane
+  // that entry's stable rank
+  auto wave_sync = [&]() {  // this wave's LDS operations done and visible to it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
 #pragma unroll
   for (int q = 0; q < kMaxExperts / 64; ++q) {
     const int l = q * 64 + lane;
-    if (l < nl) {
-      s_mask[wave][l] = mine[q];
-      blk_cnt[(int64_t)l * nbp + b] = popc64(mine[q]);
+    if (l < nl) s_mask[wave][l] = 0ull;
+  }
+  wave_sync();
+  if (live) {
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      const int l = sel[j] - lo;
+      if (j < K && (unsigned)l < (unsigned)nl) atomicOr(&s_mask[wave][l], 1ull << lane);
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  wave_sync();
+#pragma unroll
+  for (int q = 0; q < kMaxExperts / 64; ++q) {
+    const int l = q * 64 + lane;
+    if (l < nl) blk_cnt[(int64_t)l * nbp + b] = popc64(s_mask[wave][l]);
+  }
   if (live) {
     const unsigned long long below = lane ? (~0ull >> (64 - lane)) : 0ull;
 #pragma unroll
