@@ -40,6 +40,7 @@
 //  * bf16 uses v_mfma_f32_32x32x16_bf16, fp32 uses v_mfma_f32_32x32x2_f32.
 #include <cmath>
 #include <type_traits>
+#include <utility>
 
 #include "gemm_common.h"
 #include "lds_dma.h"
@@ -147,6 +148,64 @@ __device__ __forceinline__ TileInfo tile_info(int L, const int *s_ts, const int 
   return ti;
 }
 
+// First m-tile of each expert (s_ts[0 .. E], s_ts[E] = all m-tiles) and the
+// routing offsets (s_off[0 .. E]) in LDS, from the device-side offsets: one
+// wave, four experts a lane.
+template <int BM>
+__device__ __forceinline__ void tile_starts(const GemmArgs &g, int *s_ts, int *s_off, int lane) {
+  const int E = g.E;
+  int v[4], s = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane * 4 + q;
+    const int o0 = e < E ? g.offsets[e] : 0;
+    const int o1 = e < E ? g.offsets[e + 1] : 0;
+    if (e < E) s_off[e] = o0;
+    v[q] = (e < E) ? (o1 - o0 + BM - 1) / BM : 0;
+    s += v[q];
+  }
+  const int incl = wave_inclusive_sum(s);
+  int run = incl - s;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane * 4 + q;
+    if (e < E) s_ts[e] = run;
+    run += v[q];
+  }
+  if (lane == 63) {
+    s_ts[E] = incl;
+    s_off[E] = g.offsets[E];
+  }
+}
+
+// f(integral_constant<int, I>) for I = 0 .. N - 1, unrolled at compile time
+// (register arrays indexed by I stay in registers).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F> __device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// This workgroup's share of `total` tiles: first + i * stride, i < count.  The
+// tile order is cut into 8 contiguous chunks, one per XCD (the dispatcher
+// places workgroup b on XCD b % 8); the XCD's workgroups stride through it.
+struct TileShare {
+  int first, stride, count;
+};
+__device__ __forceinline__ TileShare tile_share(int total) {
+  const int gx = (int)gridDim.x / 8;  // workgroups per XCD (grid is a multiple of 8)
+  const int xcd = (int)blockIdx.x % 8, qx = (int)blockIdx.x / 8;
+  const int chunk = (total + 7) / 8;
+  const int cbeg = min(total, xcd * chunk), cend = min(total, cbeg + chunk);
+  TileShare t;
+  t.first = cbeg + qx;
+  t.stride = gx;
+  t.count = t.first < cend ? (cend - t.first + gx - 1) / gx : 0;
+  return t;
+}
+
 // Tile of BM rows x BN output columns; WM x WN waves; S-stage LDS ring of
 // RB-byte K-slices.
 //
@@ -240,41 +299,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs &g) {
   const int E = g.E, K = g.K, Nout = g.Nout;
 
   // ---- tile starts per expert (same in every workgroup) ---------------------
-  if (wave == 0) {
-    int v[4], s = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane * 4 + q;
-      const int o0 = e < E ? g.offsets[e] : 0;
-      const int o1 = e < E ? g.offsets[e + 1] : 0;
-      if (e < E) s_off[e] = o0;
-      v[q] = (e < E) ? (o1 - o0 + BM - 1) / BM : 0;
-      s += v[q];
-    }
-    const int incl = wave_inclusive_sum(s);
-    int run = incl - s;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane * 4 + q;
-      if (e < E) s_ts[e] = run;
-      run += v[q];
-    }
-    if (lane == 63) {
-      s_ts[E] = incl;
-      s_off[E] = g.offsets[E];
-    }
-  }
+  if (wave == 0) tile_starts<BM>(g, s_ts, s_off, lane);
   __syncthreads();
 
   const int n_nt = (Nout + BN - 1) / BN;
-  const int total = s_ts[E] * n_nt;
-  // this workgroup's tiles: L = first + i * stride, i < my_tiles
-  const int gx = (int)gridDim.x / 8;  // workgroups per XCD (grid is a multiple of 8)
-  const int xcd = (int)blockIdx.x % 8, qx = (int)blockIdx.x / 8;
-  const int chunk = (total + 7) / 8;
-  const int cbeg = min(total, xcd * chunk), cend = min(total, cbeg + chunk);
-  const int first = cbeg + qx;
-  const int my_tiles = first < cend ? (cend - first + gx - 1) / gx : 0;
+  // this workgroup's tiles: L = first + i * gx, i < my_tiles
+  const TileShare share = tile_share(s_ts[E] * n_nt);
+  const int first = share.first, gx = share.stride, my_tiles = share.count;
 
   const int kbytes = K * (int)sizeof(T);
   const int nk = (K + BK - 1) / BK;
@@ -774,6 +805,322 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   gemm_body<T, NSETS, EPI, BM, BN, WM, WN, S, RB, false>(g);
 }
 
+// ---- Register-weight tiles ---------------------------------------------------
+// weight slices in the register ring, activation slices loaded ahead
+constexpr int kRwD = 4, kRwDA = 3;
+constexpr int kAuxW = 0;   // weight-load cache policy (non-temporal measured 12 % slower)
+//
+// Layers with about 48 - 192 rows an expert stream their weights: each weight
+// slice is read from HBM once per m-tile and used by few rows, so the rate is
+// set by the weight bytes each CU keeps in flight, and an LDS ring, which holds
+// activation and weight slices together, keeps at most two weight slices in
+// flight.  Here each of the four waves (one a SIMD) loads its own 64 weight
+// rows straight into registers, D slices ahead (a ring of D slices: 4 x D x
+// 8 KB a CU), and only the activation rows go through LDS, by direct-to-LDS
+// loads DA slices ahead into a ring of D slots.  Every wave covers all BM rows
+// of the tile, so an expert with up to BM rows has one m-tile and each weight
+// slice is streamed once for it.
+//
+// v_mfma_f32_16x16x32_bf16 with the weight fragment first: lane l supplies 16
+// bytes (8 K elements) of weight row l % 16 at K chunk l / 16 of a 32-deep
+// k-step, so one load instruction reads 16 rows x 64 contiguous bytes; the
+// activation fragment is the same 16 bytes of row l % 16 of a 16-row block,
+// read from LDS.  Lane l ends with weight positions 4 (l / 16) + [0, 4) of
+// token row l % 16.  A wave's weight rows form 16-row half blocks h = 0, 1:
+// position i of half h is output column 8 (i / 4) + 4 h + i % 4, so a lane
+// holds 8 consecutive output columns of one row (one 16-byte store); gated
+// layers load the gate rows of those columns into blocks 0, 1 and the up rows
+// into blocks 2, 3 (the same lane and register for both halves of a pair).
+//
+// vmcnt retires loads in issue order, so a wait for one load is a wait for all
+// older ones: the activation loads of a slice go out before its weight loads,
+// DA < D slices ahead, and each slice's single barrier waits for the
+// activation rows of the next slice only.  The weight loads are compiler-
+// visible (it places their waits); the direct-to-LDS loads are not, and the
+// barrier's wait counts every load issued after them.
+template <int NSETS, int EPI, int BM, int D, int DA>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void grouped_gemm_rw(
+    GemmArgs g) {
+  constexpr int RB = 128;                   // bytes of a row's K-slice: 64 bf16, two k-steps
+  constexpr int NKS = 2;
+  constexpr int TMB = BM / 16;              // 16-row blocks
+  constexpr int WC = 64 / NSETS;            // output columns of a wave
+  constexpr int BN = 4 * WC;                // output columns of a tile
+  constexpr int JA = BM * RB / 1024 / 4;    // 1 KB activation loads a wave a slice
+  constexpr int NSL = DA + 3;               // metadata slots
+  constexpr int SLOT = BM * RB;             // bytes of an LDS slot
+  constexpr bool META = EPI == EPI_Y || EPI == EPI_OUT;
+  static_assert(JA * 4 * 1024 == BM * RB, "tile rows");
+  static_assert(D >= 2 && (D & (D - 1)) == 0 && DA >= 1 && DA < D, "rings");
+  static_assert((EPI == EPI_RELU2 || EPI == EPI_Y || EPI == EPI_OUT) == (NSETS == 1),
+                "gated epilogues take two weight sets");
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+  __shared__ __attribute__((aligned(16))) char s_a[D * SLOT];
+  __shared__ int s_ts[kMaxExperts + 1];
+  __shared__ int s_off[kMaxExperts + 1];
+  __shared__ i32x2_t s_meta[META ? NSL : 1][META ? BM : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int E = g.E, K = g.K, Nout = g.Nout;
+  if (wave == 0) tile_starts<BM>(g, s_ts, s_off, lane);
+  __syncthreads();
+  const int n_nt = (Nout + BN - 1) / BN;
+  const TileShare share = tile_share(s_ts[E] * n_nt);
+  const int first = share.first, gx = share.stride, my_tiles = share.count;
+  const int kbytes = K * 2;
+  const int nk = K / 64;         // rows hold whole slices (the host checks)
+  const int nz = my_tiles * nk;  // slices of this workgroup's stream
+  if (nz == 0) return;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void *>(g.A), (short)0, (int)g.a_bytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rc =
+      __builtin_amdgcn_make_buffer_rsrc(g.C, (short)0, (int)g.c_bytes, kRsrcWord3);
+  const uint32_t w_bytes = (uint32_t)NSETS * Nout * kbytes;
+  const float nal = -g.prm.alpha * 1.44269504088896341f;
+  const int fi = lane & 15, fq = lane >> 4;  // fragment row and K chunk
+  const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(s_a));
+
+  // ---- weights: 8 loads a lane a slice, register ring of D slices ----------
+  // A slice's weight loads go out together (the two 64-byte halves of each
+  // 128-byte piece of a row back to back), D - 1 slices ahead, into the slot
+  // the previous slice has finished with.  The K offset goes in the scalar
+  // offset field (a slice past the stream's end: out of range, zeros).
+  u32x4_t wr[D][NKS][4];
+  __amdgpu_buffer_rsrc_t rb = ra;
+  uint32_t vb[4];
+  int ib = 0, kb = -1;  // tile and slice of the weight loads in progress
+  bool blive = false;
+  auto setup_b = [&](int i) __attribute__((always_inline)) {
+    const TileInfo t = tile_info<BM, BN>(first + i * gx, s_ts, s_off, E, n_nt);
+    rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char *>(reinterpret_cast<const char *>(g.W)) + (size_t)t.e * w_bytes,
+        (short)0, (int)w_bytes, kRsrcWord3);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int h = cb & 1, set = NSETS == 2 ? cb >> 1 : 0, pair = NSETS == 2 ? 0 : cb >> 1;
+      const int col = t.n0 + wave * WC + 32 * pair + 8 * (fi >> 2) + 4 * h + (fi & 3);
+      const int row = NSETS == 1 ? col
+                      : g.interleaved ? 2 * col + set
+                                      : set * Nout + col;
+      vb[cb] = col < Nout ? (uint32_t)row * (uint32_t)kbytes + (uint32_t)(fq * 16) : kOOB;
+    }
+  };
+  auto advance_b = [&](int zb) __attribute__((always_inline)) {  // slice zb's weight loads begin
+    if (++kb == nk) { kb = 0; ++ib; }
+    blive = zb < nz;
+    if (blive && kb == 0) setup_b(ib);
+  };
+  auto load_b = [&](int ks, int cb) __attribute__((always_inline)) -> u32x4_t {
+    const uint32_t k = blive ? (uint32_t)(kb * RB + ks * 64) : kOOB;
+    return __builtin_amdgcn_raw_buffer_load_b128(rb, vb[cb], __builtin_amdgcn_readfirstlane(k),
+                                                 kAuxW);
+  };
+
+  // ---- activations: JA direct-to-LDS loads a wave a slice --------------------
+  // load j of wave w fills slot bytes [1024 (w JA + j), + 1024): row
+  // 8 (w JA + j) + lane / 8, physical chunk lane % 8, which holds the row's
+  // logical chunk (lane % 8) ^ key(row)
+  uint32_t va[JA];
+  int gidx[JA];   // the next tile's A row (or output row) per load, fetched a tile ahead
+  float gsc[JA];  // and its routing weight (w2)
+  int ia = 0, ka = -1;  // tile and slice of the activation loads in progress
+  bool alive = false;
+  auto arow_of = [&](int j) __attribute__((always_inline)) { return (wave * JA + j) * 8 + (lane >> 3); };
+  auto fetch_idx = [&](int i) __attribute__((always_inline)) {  // gather indices / metadata of tile i
+    if (i >= my_tiles) return;
+    const TileInfo t = tile_info<BM, BN>(first + i * gx, s_ts, s_off, E, n_nt);
+#pragma unroll
+    for (int j = 0; j < JA; ++j) {
+      const int p = t.row0 + min(arow_of(j), t.rows - 1);  // rows past the tile: any valid entry
+      gidx[j] = (g.gather || EPI == EPI_OUT) ? g.col_sorted[p] : p;
+      if constexpr (META)
+        gsc[j] = !g.gate_scal ? 1.f
+                 : g.gate_bf16 ? to_f32(reinterpret_cast<const bf16_t *>(g.gate_scal)[p])
+                               : reinterpret_cast<const float *>(g.gate_scal)[p];
+    }
+  };
+  auto setup_a = [&](int i) __attribute__((always_inline)) {
+    const TileInfo t = tile_info<BM, BN>(first + i * gx, s_ts, s_off, E, n_nt);
+#pragma unroll
+    for (int j = 0; j < JA; ++j) {
+      const int r = arow_of(j), p = t.row0 + r;
+      const uint32_t arow = g.gather ? (uint32_t)(gidx[j] / g.topk) : (uint32_t)p;
+      va[j] = r < t.rows ? arow * (uint32_t)kbytes + (uint32_t)(((lane & 7) ^ swz_key<RB>(r)) << 4)
+                         : kOOB;
+      if (META && (lane & 7) == 0 && r < t.rows) {
+        i32x2_t m;
+        m[0] = EPI == EPI_OUT ? gidx[j] : p;  // topk == 1: entry index == token
+        m[1] = __float_as_int(gsc[j]);
+        s_meta[i % NSL][r] = m;
+      }
+    }
+    fetch_idx(i + 1);
+  };
+  auto advance_a = [&](int za) __attribute__((always_inline)) {  // slice za's activation loads begin
+    if (++ka == nk) { ka = 0; ++ia; }
+    alive = za < nz;
+    if (alive && ka == 0) setup_a(ia);
+  };
+  auto dma_a = [&](int slot, int j) __attribute__((always_inline)) {
+    const uint32_t k = alive ? (uint32_t)(ka * RB) : kOOB;
+    dma16a(ra, sbase + (uint32_t)(slot * SLOT + (wave * JA + j) * 1024), va[j],
+           __builtin_amdgcn_readfirstlane(k));
+  };
+
+  // ---- fragments: group q of a slice is k-step q / TMB, row block q % TMB;
+  // a ring of FR registers read L groups ahead
+  constexpr int NG = NKS * TMB, FR = 4, L = 3;
+  static_assert(NG % FR == 0 && L < FR, "fragment ring");
+  bf16x8_t af[FR];
+  // row 16 i + fi has swizzle key fi / 2 for every block i; k-step 1's chunk
+  // (4 + fq) flips bit 6 of k-step 0's address
+  const int rbase = swz<RB>(fi, fq);
+  auto read_frag = [&](int slot, int q) __attribute__((always_inline)) -> bf16x8_t {
+    const int ks = q / TMB, i = q % TMB;
+    return *reinterpret_cast<const bf16x8_t *>(s_a + slot * SLOT + i * 16 * RB +
+                                              (ks ? (rbase ^ 64) : rbase));
+  };
+
+  f32x4_t acc[TMB][4];
+  // zeros the compiler cannot see through: otherwise it folds them into the
+  // next MFMAs and splits the stream into zeroed and running copies
+  auto zero_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < TMB; ++i)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        acc[i][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        asm volatile("" : "+a"(acc[i][cb]));
+      }
+  };
+  int ic = 0, kc = 0;  // the tile and slice being multiplied
+  int nrb = TMB;       // 16-row blocks of that tile holding rows (the others multiply zeros)
+
+  auto epilogue = [&]() __attribute__((always_inline)) {
+    const TileInfo t = tile_info<BM, BN>(first + ic * gx, s_ts, s_off, E, n_nt);
+#pragma unroll
+    for (int i = 0; i < TMB; ++i) {
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) asm volatile("" : "+a"(acc[i][cb]));
+      const int m = i * 16 + fi;
+      const bool ok = m < t.rows;
+      uint32_t orow = (uint32_t)(t.row0 + m);
+      float gs = 1.f;
+      if constexpr (META) {
+        const i32x2_t md = s_meta[ic % NSL][ok ? m : 0];
+        orow = (uint32_t)md[0];
+        gs = __int_as_float(md[1]);
+      }
+#pragma unroll
+      for (int pr = 0; pr < 2 / NSETS; ++pr) {
+        float v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float a0 = acc[i][2 * pr + (q >> 2)][q & 3];
+          if constexpr (META) v[q] = a0 * gs;
+          else v[q] = act_val<EPI>(a0, acc[i][NSETS == 2 ? 2 + (q >> 2) : 0][q & 3], nal, g.prm);
+        }
+        const u32x4_t o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                           pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+        const int col = t.n0 + wave * WC + 32 * pr + 8 * fq;
+        // Nout is a multiple of 8, so col < Nout covers all eight columns
+        const uint32_t off =
+            (ok && col < Nout) ? (orow * (uint32_t)Nout + (uint32_t)col) * 2u : kOOB;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, o), rc, (int)off, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // ---- the stream: per slice NG groups of four MFMAs, each followed by the
+  // fragment read L groups ahead and at most one memory operation:
+  //   groups [0, JA): slice z + DA's activation loads into slot (z + DA) % D;
+  //   groups [G1, G1 + 8): the weight loads of slice z + D - 1 into the slot
+  //     slice z - 1 used;
+  //   at group NG - L (before the first read of slice z + 1): the wait for
+  //     slice z + 1's activation rows and the barrier.
+  constexpr int G1 = JA;
+  static_assert(G1 + 8 <= NG - L, "memory operations a slice");
+  // loads issued after slice z + 1's activation loads (slice z + 1 - DA) up to
+  // that wait: the weight loads of that slice, then whole slices
+  constexpr int VWAIT = 8 + (DA - 1) * (JA + 8);
+  static_assert(VWAIT < 64, "vmcnt range");
+
+  // prologue: activation rows of slices 0 .. DA - 1, weights of slices
+  // 0 .. D - 2
+  fetch_idx(0);
+#pragma unroll
+  for (int u = 0; u < DA; ++u) {
+    advance_a(u);
+#pragma unroll
+    for (int j = 0; j < JA; ++j) dma_a(u, j);
+  }
+#pragma unroll
+  for (int u = 0; u < D - 1; ++u) {
+    advance_b(u);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) wr[u][ks][cb] = load_b(ks, cb);
+  }
+  zero_acc();
+  wait_vm<0>();
+  barrier();
+#pragma unroll
+  for (int q = 0; q < L; ++q) af[q % FR] = read_frag(0, q);
+
+  const int nzp = (nz + D - 1) / D * D;
+#pragma nounroll
+  for (int z0 = 0; z0 < nzp; z0 += D) {
+    static_for<D>([&](auto uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value;
+      const int z = z0 + u;
+      if (kc == 0 && z < nz) {
+        const TileInfo t = tile_info<BM, BN>(first + ic * gx, s_ts, s_off, E, n_nt);
+        nrb = __builtin_amdgcn_readfirstlane((t.rows + 15) >> 4);
+      }
+      static_for<NG>([&](auto qc) __attribute__((always_inline)) {
+        constexpr int q = decltype(qc)::value;
+        constexpr int ks = q / TMB, i = q % TMB;
+        // row blocks past the tile's rows are skipped (a uniform branch);
+        // slices past the stream's end multiply zeros into accumulators that
+        // no epilogue reads again
+        if (i < nrb) {
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+            acc[i][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, wr[u][ks][cb]), af[q % FR], acc[i][cb], 0, 0, 0);
+        }
+        if constexpr (q == NG - L) {
+          // slice z + 1's activation rows (and this wave's LDS reads) are done
+          wait_vm<VWAIT>();
+          barrier();
+        }
+        if constexpr (q + L < NG) af[(q + L) % FR] = read_frag(u, q + L);
+        else af[(q + L) % FR] = read_frag((u + 1) % D, q + L - NG);
+        if constexpr (q < JA) {
+          if constexpr (q == 0) advance_a(z + DA);
+          dma_a((u + DA) % D, q);
+        }
+        if constexpr (q >= G1 && q < G1 + 8) {
+          constexpr int cb = (q - G1) >> 1, ks = (q - G1) & 1;
+          if constexpr (q == G1) advance_b(z + D - 1);
+          wr[(u + D - 1) % D][ks][cb] = load_b(ks, cb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      if (z < nz && kc == nk - 1) {
+        epilogue();
+        zero_acc();
+      }
+      if (++kc == nk) { kc = 0; ++ic; }
+    });
+  }
+  wait_vm<0>();  // the loads past the end of the stream have landed
+}
+
 int device_cus() {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -866,6 +1213,19 @@ hipError_t launch_cfg(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Register-weight tiles (bf16): one workgroup a CU (four waves, one a SIMD).
+template <int NSETS, int EPI, int BM>
+hipError_t launch_rw(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
+  constexpr int BN = 4 * 64 / NSETS;
+  const int64_t tiles = est_tiles(M, E, a.Nout, BM, BN);
+  int64_t grid = device_cus();
+  if (grid > tiles) grid = tiles;
+  grid = (grid + 7) / 8 * 8;  // whole XCD rounds; surplus workgroups get no tiles
+  hipLaunchKernelGGL((grouped_gemm_rw<NSETS, EPI, BM, kRwD, kRwDA>), dim3((unsigned)grid),
+                     dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 // Expected tiles when the M rows spread evenly over the experts: an expert's
 // last m-tile is half full on average, so about M / BM + E / 2 m-tiles.
 inline int64_t expected_tiles(int64_t M, int E, int Nout, int BM, int BN) {
@@ -927,6 +1287,10 @@ hipError_t launch_t(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
     if (expected_tiles(M, E, a.Nout, Sm::BM, Sm::BN) < cus)
       return launch_cfg<T, NSETS, EPI, Tn>(a, M, E, s);
     return launch_cfg<T, NSETS, EPI, Sm>(a, M, E, s);
+  }
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (a.K % 64 == 0 && M >= 48 * (int64_t)E && M <= 176 * (int64_t)E)
+      return launch_rw<NSETS, EPI, 192>(a, M, E, s);
   }
   if constexpr (NSETS == 1) {
     if (M >= 96 * (int64_t)E && M <= 176 * (int64_t)E &&

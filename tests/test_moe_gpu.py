@@ -97,6 +97,34 @@ def test_variants(case):
     run_layer(spec)
 
 
+# Layers of 48 - 176 rows an expert on average with K a multiple of 64 take the
+# register-weight tiles (192 rows, 128 gated / 256 plain output columns a
+# tile): skewed routing gives some experts more than 192 rows (several
+# m-tiles) and leaves others nearly empty; the output widths leave ragged
+# n-tiles; one K-slice (K = 64) makes each tile a single slice.
+RW = [
+    # (name, N, H, I, E, k, act, layout, zipf_s)
+    ("rw-skew-multitile", 640, 192, 320, 8, 2, "silu", "interleaved", 1.2),
+    ("rw-packed-ragged", 700, 320, 200, 8, 2, "swiglu_oai", "packed", None),
+    ("rw-relu2", 480, 256, 136, 6, 2, "relu2", "packed", 0.8),
+    ("rw-one-slice", 500, 64, 64, 8, 2, "silu", "packed", None),
+    ("rw-topk1", 700, 128, 192, 5, 1, "silu", "interleaved", 1.0),
+]
+
+
+@pytest.mark.parametrize("case", RW, ids=[c[0] for c in RW])
+def test_register_weight_tiles(case):
+    name, n, h, i, e, k, act, layout, zs = case
+    spec = LayerSpec(name, n_tokens=n, hidden=h, inter=i, n_experts=e, topk=k, act=act,
+                     layout=layout, zipf_s=zs, seed=n + i,
+                     alpha=1.702 if act == "swiglu_oai" else None,
+                     beta=1.0 if act == "swiglu_oai" else None,
+                     limit=7.0 if act == "swiglu_oai" else None)
+    _, routing, _ = run_layer(spec)
+    counts = routing.col_sum.cpu()
+    print(f"[moe] {name}: rows per expert {counts.tolist()}", flush=True)
+
+
 def test_layouts_bit_identical_on_gpu():
     """Packed and interleaved w13 built from the same gate/up draws give the same
     output bit for bit (the kernel de-interleaves on the way into LDS)."""
