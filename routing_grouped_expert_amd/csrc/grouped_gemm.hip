@@ -807,8 +807,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
 // ---- Register-weight tiles ---------------------------------------------------
 // weight slices in the register ring, activation slices loaded ahead
-constexpr int kRwD = 4, kRwDA = 3;
-constexpr int kAuxW = 0;   // weight-load cache policy (non-temporal measured 12 % slower)
+constexpr int kRwD = 4, kRwDA = 2;
+// weight-load cache policy: non-temporal for plain layers (gpt-oss-sized w2 at 4096
+// tokens 502 -> 475 us), the default for gated ones (w13 933 -> 965 us non-temporal)
+template <int NSETS> constexpr int kAuxW = NSETS == 1 ? 2 : 0;
 //
 // Layers with about 48 - 192 rows an expert stream their weights: each weight
 // slice is read from HBM once per m-tile and used by few rows, so the rate is
@@ -851,7 +853,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int SLOT = BM * RB;             // bytes of an LDS slot
   constexpr bool META = EPI == EPI_Y || EPI == EPI_OUT;
   static_assert(JA * 4 * 1024 == BM * RB, "tile rows");
-  static_assert(D >= 2 && (D & (D - 1)) == 0 && DA >= 1 && DA < D, "rings");
+  static_assert(D >= 2 && DA >= 1 && DA < D, "rings");
   static_assert((EPI == EPI_RELU2 || EPI == EPI_Y || EPI == EPI_OUT) == (NSETS == 1),
                 "gated epilogues take two weight sets");
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -883,15 +885,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint32_t sbase = __builtin_amdgcn_readfirstlane(lds_addr(s_a));
 
   // ---- weights: 8 loads a lane a slice, register ring of D slices ----------
-  // A slice's weight loads go out together (the two 64-byte halves of each
-  // 128-byte piece of a row back to back), D - 1 slices ahead, into the slot
-  // the previous slice has finished with.  The K offset goes in the scalar
-  // offset field (a slice past the stream's end: out of range, zeros).
-  u32x4_t wr[D][NKS][4];
+  // A 16-row weight block cb of a slice is two 1 KB loads of whole 128-byte
+  // row pieces: X holds rows 0-7, Y rows 8-15 of the block; lane l takes row
+  // l % 8 and, for lanes with bit 3 clear, chunks l / 16 (X) and 4 + l / 16
+  // (Y), the other way round for lanes with bit 3 set.  Then k-step 0's
+  // fragment (row l % 16, chunk l / 16) is X or Y in the lane's own register
+  // (bit 3 picks), and k-step 1's (chunk 4 + l / 16) is the other choice
+  // taken from lane l ^ 8 (a DPP rotate by 8 within each 16-lane row).  A
+  // slice's loads go out together, D - 1 slices ahead, into the slot the
+  // previous slice has finished with, and become fragments at the start of
+  // their slice.  The K offset goes in the scalar offset field (a slice past
+  // the stream's end: out of range, zeros).
+  u32x4_t wr[D][NKS][4];  // [slot][X / Y, then k-step][block]
   __amdgpu_buffer_rsrc_t rb = ra;
-  uint32_t vb[4];
+  uint32_t vb[2][4];
   int ib = 0, kb = -1;  // tile and slice of the weight loads in progress
   bool blive = false;
+  const bool hi8 = (lane & 8) != 0;
   auto setup_b = [&](int i) __attribute__((always_inline)) {
     const TileInfo t = tile_info<BM, BN>(first + i * gx, s_ts, s_off, E, n_nt);
     rb = __builtin_amdgcn_make_buffer_rsrc(
@@ -899,12 +909,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         (short)0, (int)w_bytes, kRsrcWord3);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
-      const int h = cb & 1, set = NSETS == 2 ? cb >> 1 : 0, pair = NSETS == 2 ? 0 : cb >> 1;
-      const int col = t.n0 + wave * WC + 32 * pair + 8 * (fi >> 2) + 4 * h + (fi & 3);
-      const int row = NSETS == 1 ? col
-                      : g.interleaved ? 2 * col + set
-                                      : set * Nout + col;
-      vb[cb] = col < Nout ? (uint32_t)row * (uint32_t)kbytes + (uint32_t)(fq * 16) : kOOB;
+#pragma unroll
+      for (int xy = 0; xy < 2; ++xy) {
+        const int pos = 8 * xy + (lane & 7);  // position in the block: its output column
+        const int chunk = (lane >> 4) + ((((lane >> 3) & 1) ^ xy) ? 4 : 0);
+        const int h = cb & 1, set = NSETS == 2 ? cb >> 1 : 0, pair = NSETS == 2 ? 0 : cb >> 1;
+        const int col = t.n0 + wave * WC + 32 * pair + 8 * (pos >> 2) + 4 * h + (pos & 3);
+        const int row = NSETS == 1 ? col
+                        : g.interleaved ? 2 * col + set
+                                        : set * Nout + col;
+        vb[xy][cb] =
+            col < Nout ? (uint32_t)row * (uint32_t)kbytes + (uint32_t)(chunk * 16) : kOOB;
+      }
     }
   };
   auto advance_b = [&](int zb) __attribute__((always_inline)) {  // slice zb's weight loads begin
@@ -912,10 +928,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     blive = zb < nz;
     if (blive && kb == 0) setup_b(ib);
   };
-  auto load_b = [&](int ks, int cb) __attribute__((always_inline)) -> u32x4_t {
-    const uint32_t k = blive ? (uint32_t)(kb * RB + ks * 64) : kOOB;
-    return __builtin_amdgcn_raw_buffer_load_b128(rb, vb[cb], __builtin_amdgcn_readfirstlane(k),
-                                                 kAuxW);
+  auto load_b = [&](int xy, int cb) __attribute__((always_inline)) -> u32x4_t {
+    const uint32_t k = blive ? (uint32_t)(kb * RB) : kOOB;
+    return __builtin_amdgcn_raw_buffer_load_b128(rb, vb[xy][cb], __builtin_amdgcn_readfirstlane(k),
+                                                 kAuxW<NSETS>);
+  };
+  // X, Y of block cb in slot u -> k-step 0 and (still to rotate) k-step 1
+  auto frag_select = [&](int u, int cb) __attribute__((always_inline)) {
+    const u32x4_t x = wr[u][0][cb], y = wr[u][1][cb];
+    u32x4_t f0, t;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      f0[d] = hi8 ? y[d] : x[d];
+      t[d] = hi8 ? x[d] : y[d];
+    }
+    wr[u][0][cb] = f0;
+    wr[u][1][cb] = t;
+  };
+  auto frag_rotate = [&](int u, int cb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      wr[u][1][cb][d] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)wr[u][1][cb][d],
+                                                              0x128 /* row_ror:8 */, 0xf, 0xf,
+                                                              false);
   };
 
   // ---- activations: JA direct-to-LDS loads a wave a slice --------------------
@@ -1038,7 +1073,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // fragment read L groups ahead and at most one memory operation:
   //   groups [0, JA): slice z + DA's activation loads into slot (z + DA) % D;
   //   groups [G1, G1 + 8): the weight loads of slice z + D - 1 into the slot
-  //     slice z - 1 used;
+  //     slice z - 1 used (X and Y of each block back to back);
+  //   groups [1, 5): k-step 1's fragments rotated into place;
   //   at group NG - L (before the first read of slice z + 1): the wait for
   //     slice z + 1's activation rows and the barrier.
   constexpr int G1 = JA;
@@ -1063,7 +1099,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) wr[u][ks][cb] = load_b(ks, cb);
+      for (int xy = 0; xy < 2; ++xy) wr[u][xy][cb] = load_b(xy, cb);
   }
   zero_acc();
   wait_vm<0>();
@@ -1081,6 +1117,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const TileInfo t = tile_info<BM, BN>(first + ic * gx, s_ts, s_off, E, n_nt);
         nrb = __builtin_amdgcn_readfirstlane((t.rows + 15) >> 4);
       }
+      // this slice's weight fragments: k-step 0 by a select, before its MFMAs
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) frag_select(u, cb);
       static_for<NG>([&](auto qc) __attribute__((always_inline)) {
         constexpr int q = decltype(qc)::value;
         constexpr int ks = q / TMB, i = q % TMB;
@@ -1105,10 +1144,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           dma_a((u + DA) % D, q);
         }
         if constexpr (q >= G1 && q < G1 + 8) {
-          constexpr int cb = (q - G1) >> 1, ks = (q - G1) & 1;
+          constexpr int cb = (q - G1) >> 1, xy = (q - G1) & 1;
           if constexpr (q == G1) advance_b(z + D - 1);
-          wr[(u + D - 1) % D][ks][cb] = load_b(ks, cb);
+          wr[(u + D - 1) % D][xy][cb] = load_b(xy, cb);
         }
+        // k-step 1's fragments rotated into place, one block a group
+        if constexpr (q >= 1 && q < 5) frag_rotate(u, q - 1);
         __builtin_amdgcn_sched_barrier(0);
       });
       if (z < nz && kc == nk - 1) {
@@ -1288,8 +1329,12 @@ hipError_t launch_t(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
       return launch_cfg<T, NSETS, EPI, Tn>(a, M, E, s);
     return launch_cfg<T, NSETS, EPI, Sm>(a, M, E, s);
   }
+  // register-weight tiles (bf16, rows of whole 64-element slices): plain layers
+  // of 48 - 176 rows an expert, gated ones of 96 - 176 (at 64 rows an expert
+  // the gated 128-row ping-pong tile measured faster: gpt-oss-sized w13 at
+  // 2048 tokens 791 vs 829 us; at 4096 tokens 986 vs 905 us)
   if constexpr (std::is_same<T, bf16_t>::value) {
-    if (a.K % 64 == 0 && M >= 48 * (int64_t)E && M <= 176 * (int64_t)E)
+    if (a.K % 64 == 0 && M >= (NSETS == 2 ? 96 : 48) * (int64_t)E && M <= 176 * (int64_t)E)
       return launch_rw<NSETS, EPI, 192>(a, M, E, s);
   }
   if constexpr (NSETS == 1) {

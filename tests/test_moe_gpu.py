@@ -97,7 +97,8 @@ def test_variants(case):
     run_layer(spec)
 
 
-# Layers of 48 - 176 rows an expert on average with K a multiple of 64 take the
+# Layers of 48 - 176 rows an expert on average (gated: 96 - 176) with K a
+# multiple of 64 take the
 # register-weight tiles (192 rows, 128 gated / 256 plain output columns a
 # tile): skewed routing gives some experts more than 192 rows (several
 # m-tiles) and leaves others nearly empty; the output widths leave ragged
