@@ -60,6 +60,10 @@ EDGE = [
     (32768, 8, 1, "bf16"),   # one chunk a row, top-1
     (70001, 64, 8, "bf16"),  # more than 1024 blocks: two rounds of the count scan
     (32800, 40, 3, "bf16"),  # not a power of two: back on the cooperative top-k
+    (32768 + 1, 32, 4, "bf16"),   # rows of four chunks, one-token tail, staged scatter
+    (40000, 128, 2, "bf16"),      # two phases of 64 experts, top-2 vector stores
+    (33000, 16, 8, "bf16"),       # top-8 of 16 experts (vector stores, staged scatter)
+    (65536, 256, 8, "bf16"),      # four phases, two-word-vector bitmatrix rows
     # cooperative top-k past 256 blocks of 256 tokens: count rows prefix-summed once
     (65536 + 257, 40, 3, "bf16"),   # 258 blocks, ragged last one, odd expert count
     (70001, 128, 4, "f32"),         # fp32 logits
