@@ -812,27 +812,26 @@ constexpr int kRwD = 4, kRwDA = 2;
 // tokens 502 -> 475 us), the default for gated ones (w13 933 -> 965 us non-temporal)
 template <int NSETS> constexpr int kAuxW = NSETS == 1 ? 2 : 0;
 //
-// Layers with about 48 - 192 rows an expert stream their weights: each weight
-// slice is read from HBM once per m-tile and used by few rows, so the rate is
-// set by the weight bytes each CU keeps in flight, and an LDS ring, which holds
-// activation and weight slices together, keeps at most two weight slices in
-// flight.  Here each of the four waves (one a SIMD) loads its own 64 weight
-// rows straight into registers, D slices ahead (a ring of D slices: 4 x D x
-// 8 KB a CU), and only the activation rows go through LDS, by direct-to-LDS
-// loads DA slices ahead into a ring of D slots.  Every wave covers all BM rows
-// of the tile, so an expert with up to BM rows has one m-tile and each weight
-// slice is streamed once for it.
+// Layers with about 48 - 176 rows an expert stream their weights: each weight
+// slice is read from HBM once per m-tile and used by few rows, and an LDS ring,
+// which holds activation and weight slices together, keeps at most two weight
+// slices in flight.  Here each of the four waves (one a SIMD) loads its own 64
+// weight rows straight into registers, D - 1 slices ahead (a ring of D slices:
+// 4 x D x 8 KB a CU), and only the activation rows go through LDS, by direct-
+// to-LDS loads DA slices ahead into a ring of D slots.  Every wave covers all
+// BM rows of the tile, so an expert with up to BM rows has one m-tile and each
+// weight slice is streamed once for it.
 //
 // v_mfma_f32_16x16x32_bf16 with the weight fragment first: lane l supplies 16
 // bytes (8 K elements) of weight row l % 16 at K chunk l / 16 of a 32-deep
-// k-step, so one load instruction reads 16 rows x 64 contiguous bytes; the
-// activation fragment is the same 16 bytes of row l % 16 of a 16-row block,
-// read from LDS.  Lane l ends with weight positions 4 (l / 16) + [0, 4) of
-// token row l % 16.  A wave's weight rows form 16-row half blocks h = 0, 1:
-// position i of half h is output column 8 (i / 4) + 4 h + i % 4, so a lane
-// holds 8 consecutive output columns of one row (one 16-byte store); gated
-// layers load the gate rows of those columns into blocks 0, 1 and the up rows
-// into blocks 2, 3 (the same lane and register for both halves of a pair).
+// k-step (built from whole-line loads, below); the activation fragment is the
+// same 16 bytes of row l % 16 of a 16-row block, read from LDS.  Lane l ends
+// with weight positions 4 (l / 16) + [0, 4) of token row l % 16.  A wave's
+// weight rows form 16-row half blocks h = 0, 1: position i of half h is output
+// column 8 (i / 4) + 4 h + i % 4, so a lane holds 8 consecutive output columns
+// of one row (one 16-byte store); gated layers load the gate rows of those
+// columns into blocks 0, 1 and the up rows into blocks 2, 3 (the same lane and
+// register for both halves of a pair).
 //
 // vmcnt retires loads in issue order, so a wait for one load is a wait for all
 // older ones: the activation loads of a slice go out before its weight loads,
