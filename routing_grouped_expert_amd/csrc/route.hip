@@ -1610,15 +1610,24 @@ constexpr int64_t kSmallBlocksUpTo = 16384;
 inline int route_block_tokens(int64_t N) { return N <= kSmallBlocksUpTo ? 64 : kRouteTokens; }
 
 // The lane-per-token path takes bf16 logits of a power-of-two expert count
-// from 8 in batches of at least kLaneTokens tokens, where it is faster (32768
+// from 8 in batches of at least lane_tokens(E) tokens, where it is faster (32768
 // tokens, 128 experts: 22.9 -> 19.8 us; 65536: 27.7 -> 23.2 us; 32 experts
 // even) and its count scan is linear in the number of blocks, where
 // route_scatter's re-summing of all earlier blocks grows with their square
 // (262144 tokens: 146 -> 54 us).  Smaller batches keep the cooperative top-k
-// above: with few tokens a CU the lane path leaves SIMDs idle.
-constexpr int64_t kLaneTokens = 32768;
+// above: with few tokens a CU the lane path leaves SIMDs idle, which costs
+// less the more experts a token ranks.  Where the two cross (same builds,
+// interleaved): 256 experts top-8 from 8192 tokens (25.9 -> 23.5 us; 12288:
+// 29.4 -> 23.7), 128 experts top-4 from 12288 (15.9 -> 15.4; 10240: 15.2
+// against 15.5; 24576: 21.8 -> 15.6), 64 experts past the cooperative path's
+// 64-token blocks (16384 top-4: 12.8 against 13.4; 20480: 16.5 -> 13.5, top-8
+// 22.5 -> 16.3); 32 experts even from 20480 to 28672 tokens, 16 behind up to
+// 28672: 32768 for those.
+inline int64_t lane_tokens(int E) {
+  return E >= 256 ? 8192 : E >= 128 ? 12288 : E >= 64 ? kSmallBlocksUpTo + 1 : 32768;
+}
 inline bool lane_path(int64_t N, int E) {
-  return N >= kLaneTokens && E >= 8 && (E & (E - 1)) == 0 && N * E * 2 < ((int64_t)1 << 31);
+  return E >= 8 && (E & (E - 1)) == 0 && N >= lane_tokens(E) && N * E * 2 < ((int64_t)1 << 31);
 }
 
 // With x != nullptr (router GEMM), `logits` is written from x and the gate

@@ -43,7 +43,8 @@ EDGE = [
     (4097, 8, 1, "bf16"),    # one token past it: multi-block
     (4096, 16, 1, "f32"),    # compact path, fp32 logits
     (2049, 3, 2, "bf16"),    # compact path, scalar loads, ragged 64-token groups
-    (12345, 256, 16, "bf16"),  # 64-token blocks: widest layer, ragged last block
+    (8191, 256, 16, "bf16"),   # 64-token blocks: widest layer, ragged last block
+    (12345, 256, 16, "bf16"),  # one lane a token from 8192 tokens at 256 experts
     (16385, 32, 4, "bf16"),  # first batch back on 256-token blocks, one-token tail
     (129, 128, 4, "bf16"),   # past 128 tokens, more than 64 experts: 64-token blocks
     (256, 256, 8, "bf16"),   # the same at the one-workgroup path's former limit
@@ -61,6 +62,11 @@ EDGE = [
     (70001, 64, 8, "bf16"),  # more than 1024 blocks: two rounds of the count scan
     (32800, 40, 3, "bf16"),  # not a power of two: back on the cooperative top-k
     (32768 + 1, 32, 4, "bf16"),   # rows of four chunks, one-token tail, staged scatter
+    (32767, 32, 4, "bf16"),       # one token short of it: cooperative top-k
+    (8192, 256, 8, "bf16"),       # the lane path's first batch at 256 experts
+    (12287, 128, 4, "bf16"),      # 128 experts: cooperative one token short of 12288
+    (12288, 128, 4, "bf16"),      # and the lane path from there
+    (16385, 64, 8, "bf16"),       # 64 experts: the lane path past 64-token blocks
     (40000, 128, 2, "bf16"),      # two phases of 64 experts, top-2 vector stores
     (33000, 16, 8, "bf16"),       # top-8 of 16 experts (vector stores, staged scatter)
     (65536, 256, 8, "bf16"),      # four phases, two-word-vector bitmatrix rows
