@@ -1286,10 +1286,12 @@ inline double launch_cost(int64_t tiles, int64_t cus, int BM, int BN, double sur
 // one-wave tile spreads the weight stream over more CUs.
 // Plain (w2) launches of 96 to 176 rows an expert on average take the 192-row
 // tile (one m-tile an expert).
-// Plain (w2) layers with up to one 256-row tile per expert on average stream
-// each expert's weights about once with 256-row tiles and about 1.5 times with
-// 128-row tiles, so they take the 256-row tile -- when those tiles still cover
-// the CUs (gpt-oss-sized w2 at 128 rows per expert).  Everything else takes
+// Plain (w2) layers take the 256-row tile whenever those tiles still cover the
+// CUs: with up to one 256-row tile per expert on average it streams each
+// expert's weights about once where 128-row tiles stream them about 1.5 times
+// (gpt-oss-sized w2 at 128 rows per expert), and past that the cost model's
+// near-ties chose the 128-row tile at a large loss (gpt-oss-sized w2 at 256,
+// 384 and 512 rows an expert: 1247 -> 845, 1761 -> 1030, 2255 -> 1258 us).  Everything else takes
 // whichever tile the cost model favours: the gated 256 x 128 tile at 64-128
 // rows per expert is half empty and measured 6-14 % slower than the 128-row
 // tile (gpt-oss-sized layer, 2048 and 4096 tokens), and 64 plain 256-row tiles
@@ -1335,6 +1337,15 @@ hipError_t launch_t(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (a.K % 64 == 0 && M >= (NSETS == 2 ? 96 : 48) * (int64_t)E && M <= 176 * (int64_t)E)
       return launch_rw<NSETS, EPI, 192>(a, M, E, s);
+    // gated layers of 177 - 240 rows an expert: the 256-row register-weight
+    // tile keeps one m-tile an expert (gpt-oss-sized w13 at 6144 tokens 1278 ->
+    // 1159 us, 7168: 1353 -> 1172; the 256-row LDS tile 1167 / 1201; at 256
+    // rows an expert it loses, 1587 -> 1615), where its tiles cover the CUs
+    if constexpr (NSETS == 2) {
+      if (a.K % 64 == 0 && M > 176 * (int64_t)E && M <= 240 * (int64_t)E &&
+          expected_tiles(M, E, a.Nout, 256, 4 * 64 / NSETS) >= cus)
+        return launch_rw<NSETS, EPI, 256>(a, M, E, s);
+    }
   }
   if constexpr (NSETS == 1) {
     if (M >= 96 * (int64_t)E && M <= 176 * (int64_t)E &&
@@ -1354,8 +1365,7 @@ hipError_t launch_t(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
     }
     return launch_cfg<T, NSETS, EPI, L>(a, M, E, s);
   };
-  if (NSETS == 1 && M < (int64_t)L::BM * E && expected_tiles(M, E, a.Nout, L::BM, L::BN) >= cus)
-    return launch_l();
+  if (NSETS == 1 && expected_tiles(M, E, a.Nout, L::BM, L::BN) >= cus) return launch_l();
   const double cl = launch_cost(expected_tiles(M, E, a.Nout, L::BM, L::BN), cus, L::BM, L::BN, 0.0);
   const double cm = launch_cost(tm, cus, Md::BM, Md::BN, 0.15);
   if (cl <= cm) return launch_l();

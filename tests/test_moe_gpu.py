@@ -110,6 +110,13 @@ RW = [
     ("rw-relu2", 480, 256, 136, 6, 2, "relu2", "packed", 0.8),
     ("rw-one-slice", 500, 64, 64, 8, 2, "silu", "packed", None),
     ("rw-topk1", 700, 128, 192, 5, 1, "silu", "interleaved", 1.0),
+    # gated, about 208 rows an expert over 16 n-tiles: the 256-row register-weight
+    # tile (skew puts some experts past 256 rows: a second m-tile)
+    ("rw256-gated", 1664, 128, 2048, 16, 2, "swiglu_oai", "interleaved", 0.5),
+    ("rw256-gated-packed", 1700, 192, 2048, 16, 2, "silu", "packed", None),
+    # plain w2 at about 260 rows an expert with 256-row tiles covering the CUs
+    # (the four-wave 256 x 256 LDS tile past the 256-row mark)
+    ("l256-plain-w2", 4160, 768, 128, 64, 4, "relu2", "packed", 0.3),
 ]
 
 
