@@ -363,7 +363,10 @@ moe_status_t moe_quantize_mxfp4(const void *w, moe_dtype_t dtype, int32_t n_expe
  *   each GEMM: at most 128 tokens with N * topk <= 1.5 E take the
  *   matrix-vector kernels in both, and past the bf16 layer's matrix-vector
  *   range (3 E for w13, 5 E for w2) the 32-row / one-wave tiles are shared
- *   below 48 rows an expert; the 128-row MXFP4 tiles differ from the bf16
+ *   below 48 rows an expert, except where the bf16 layer takes its
+ *   register-weight tiles there (bf16 K a multiple of 64, from 16 rows an
+ *   expert for w2 and ReLU^2 w13, from 32 for gated w13, when those tiles
+ *   cover the compute units); the 128-row MXFP4 tiles differ from the bf16
  *   ones).  Workspace and other arguments as moe_experts / moe_forward. */
 moe_status_t moe_experts_mxfp4(const void *x, moe_dtype_t dtype, int64_t n_tokens,
                                int32_t hidden, const void *w13_q, const void *w13_s,

@@ -117,6 +117,10 @@ RW = [
     # plain w2 at about 260 rows an expert with 256-row tiles covering the CUs
     # (the four-wave 256 x 256 LDS tile past the 256-row mark)
     ("l256-plain-w2", 4160, 768, 128, 64, 4, "relu2", "packed", 0.3),
+    # below 48 rows an expert with the tiles covering the CUs: plain w2 at about
+    # 20 rows an expert, gated w13 at about 36
+    ("rw-low-plain-w2", 640, 1792, 128, 64, 2, "silu", "packed", 0.4),
+    ("rw-low-gated", 1152, 128, 768, 64, 2, "swiglu_oai", "interleaved", None),
 ]
 
 

@@ -91,23 +91,37 @@ MX = [
 ]
 
 
-def _same_kernels(n, k, e):
+def _bf16_register_weight_low(m, e, nout, kdim, plain):
+    """The bf16 layer's choice below 48 rows an expert: the 192-row
+    register-weight tile from 16 (plain) or 32 (gated) rows an expert, for K a
+    multiple of 64, when its expected tiles cover the CUs (the host rule)."""
+    if kdim % 64 or not ((16 if plain else 32) * e <= m < 48 * e):
+        return False
+    bn = 256 if plain else 128
+    tiles = (m // 192 + (min(m, e) + 1) // 2) * ((nout + bn - 1) // bn)
+    return tiles >= torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def _same_kernels(n, k, e, h, i, act):
     """True when the MXFP4 and the bf16 layer take the same kernel for each of
     the two GEMMs (then the results are the same bits): both the matrix-vector
     kernel (at most 128 tokens and few rows an expert: w13 n * k <= 1.5 E for
     MXFP4 and <= 3 E for bf16, w2 <= 3 E and <= 5 E), or both the one-wave /
-    32-row MFMA tiles (n * k < 48 E, outside the matrix-vector range)."""
+    32-row MFMA tiles (n * k < 48 E, outside the matrix-vector range, unless
+    the bf16 layer takes its register-weight tile there)."""
     m = n * k
 
-    def same(gv_mx, gv_16):
-        return (gv_mx and gv_16) or (not gv_mx and not gv_16 and m < 48 * e)
+    def same(gv_mx, gv_16, rw):
+        return (gv_mx and gv_16) or (not gv_mx and not gv_16 and m < 48 * e and not rw)
 
     small = n <= 128
+    rw13 = _bf16_register_weight_low(m, e, i, h, act == "relu2")
+    rw2 = _bf16_register_weight_low(m, e, h, i, True)
     # (at k > 1 and m <= E the bf16 layer folds the combine into its w2 kernel
     # and the MXFP4 layer does not: the fused kernel is built to give the same
     # bits, which this comparison then checks)
-    return (same(small and 2 * m <= 3 * e, small and m <= 3 * e)
-            and same(small and m <= 3 * e, small and m <= 5 * e))
+    return (same(small and 2 * m <= 3 * e, small and m <= 3 * e, rw13)
+            and same(small and m <= 3 * e, small and m <= 5 * e, rw2))
 
 
 @pytest.mark.parametrize("case", MX, ids=[c[0] for c in MX])
@@ -128,7 +142,7 @@ def test_mxfp4_layer(case):
     ref = oracle.moe_ffn(layer.x, ref_r.topk_idx, ref_r.topk_w, d13, d2, act, layout,
                          act_params(spec))
     print(f"[mxfp4] {name}: {assert_output_close(out, ref, name)}", flush=True)
-    if _same_kernels(n, k, e):
+    if _same_kernels(n, k, e, h, i, act):
         deq13 = torch.stack([torch.from_numpy(d13[j]) for j in range(e)]).to(torch.bfloat16)
         deq2 = torch.stack([torch.from_numpy(d2[j]) for j in range(e)]).to(torch.bfloat16)
         ref16 = moe_experts(x, deq13.to(DEV), deq2.to(DEV), routing, act, layout,
