@@ -1326,16 +1326,25 @@ hipError_t launch_t(const GemmArgs &a, int64_t M, int E, hipStream_t s) {
   const int64_t cus = device_cus();
   const int64_t tm = expected_tiles(M, E, a.Nout, Md::BM, Md::BN);
   // below 48 rows an expert the 32-row tiles give every expert with more than
-  // 32 rows a second m-tile (a second pass over its weights); the 192-row
-  // register-weight tile keeps one where its tiles cover the CUs: plain layers
-  // from 16 rows an expert, gated ones from 32 (gpt-oss-sized layer, w13 / w2
+  // 32 rows a second m-tile (a second pass over its weights); a register-weight
+  // tile keeps one where its tiles cover the CUs (gpt-oss-sized layer, w13 / w2
   // in us: 1024 tokens 863 / 602 -> 805 / 411, 1280 tokens 1064 / 773 -> 811 /
-  // 427, 768 tokens w2 464 -> 401, 512 tokens w2 426 -> 386; gated at 16 and 24
-  // rows an expert it loses, 673 -> 796 and 715 -> 799)
+  // 427, 768 tokens w2 464 -> 401, 512 tokens w2 426 -> 386, all on the 192-row
+  // tile; gated at 16 and 24 rows an expert it loses, 673 -> 796 and 715 ->
+  // 799).  Plain layers of 16 - 96 rows an expert take the 128-row one (fewer
+  // activation loads of padding rows: w2 at 768 - 3072 tokens 4 - 8 % faster
+  // than on the 192-row tile, 464 -> 427 us at 2048), gated ones of 32 - 47 the
+  // 192-row one (on the 128-row tile gated layers measured -4 % to +3 %).
   if constexpr (std::is_same<T, bf16_t>::value) {
-    if (a.K % 64 == 0 && M >= (NSETS == 2 ? 32 : 16) * (int64_t)E && M < 48 * (int64_t)E &&
-        expected_tiles(M, E, a.Nout, 192, 4 * 64 / NSETS) >= cus)
-      return launch_rw<NSETS, EPI, 192>(a, M, E, s);
+    if constexpr (NSETS == 1) {
+      if (a.K % 64 == 0 && M >= 16 * (int64_t)E && M <= 96 * (int64_t)E &&
+          expected_tiles(M, E, a.Nout, 128, 4 * 64) >= cus)
+        return launch_rw<NSETS, EPI, 128>(a, M, E, s);
+    } else {
+      if (a.K % 64 == 0 && M >= 32 * (int64_t)E && M < 48 * (int64_t)E &&
+          expected_tiles(M, E, a.Nout, 192, 4 * 64 / NSETS) >= cus)
+        return launch_rw<NSETS, EPI, 192>(a, M, E, s);
+    }
   }
   if (M < 48 * (int64_t)E || tm < cus / 2) {
     if (expected_tiles(M, E, a.Nout, Sm::BM, Sm::BN) < cus)

@@ -121,6 +121,9 @@ RW = [
     # 20 rows an expert, gated w13 at about 36
     ("rw-low-plain-w2", 640, 1792, 128, 64, 2, "silu", "packed", 0.4),
     ("rw-low-gated", 1152, 128, 768, 64, 2, "swiglu_oai", "interleaved", None),
+    # plain w2 at about 80 rows an expert over 4 n-tiles: the 128-row
+    # register-weight tile (skew gives some experts a second m-tile)
+    ("rw128-plain-w2", 2560, 1024, 128, 64, 2, "silu", "packed", 0.6),
 ]
 
 

@@ -92,13 +92,14 @@ MX = [
 
 
 def _bf16_register_weight_low(m, e, nout, kdim, plain):
-    """The bf16 layer's choice below 48 rows an expert: the 192-row
-    register-weight tile from 16 (plain) or 32 (gated) rows an expert, for K a
-    multiple of 64, when its expected tiles cover the CUs (the host rule)."""
+    """The bf16 layer's choice below 48 rows an expert: a register-weight tile
+    (128 rows for plain layers from 16 rows an expert, 192 for gated ones from
+    32), for K a multiple of 64, when its expected tiles cover the CUs (the
+    host rule)."""
     if kdim % 64 or not ((16 if plain else 32) * e <= m < 48 * e):
         return False
-    bn = 256 if plain else 128
-    tiles = (m // 192 + (min(m, e) + 1) // 2) * ((nout + bn - 1) // bn)
+    bm, bn = (128, 256) if plain else (192, 128)
+    tiles = (m // bm + (min(m, e) + 1) // 2) * ((nout + bn - 1) // bn)
     return tiles >= torch.cuda.get_device_properties(0).multi_processor_count
 
 
